@@ -1,0 +1,371 @@
+"""Float64 CPU oracle for causal differential attention (DiffAttn).
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain definition that the
+HIP library is checked against.  Only the tests, the smoke check of the package
+entry file and the CPU-baseline leg of the benchmark may import it; the library
+and its Python binding never do, and this module imports nothing from them.
+
+Every function takes numpy arrays (any float dtype; they are upcast exactly to
+float64) and computes in float64.  Attention maps are materialised block by
+block of query rows; nothing is fused or reordered beyond what the formulas
+state.
+
+Sources (page title, then section / equation):
+  [HADA]   "Differential Transformer: Transformer que cancela ruido de atencao"
+           (pt.news.hada.io), sections "Como a atencao diferencial funciona" and
+           "Estrutura multi-head e arquitetura completa".
+  [PRIOR]  "Differential Transformer: Canceling Context Noise with Differential
+           Attention" (priorstack.com, Attention Mechanism tag page), section
+           "Cancelling Context Noise Through Attention Map Subtraction".
+  [INTOAI] "A Simple Principle From Noise-Cancelling Headphones Supercharges
+           Transformers Like Never Before" (intoai.pub), sections "A Deeper Dive
+           Into Attention Calculations" (causal mask) and "Differential Attention
+           With Multiple Heads" (lambda shared per layer, per-head RMSNorm,
+           scale by 1 - lambda_init).
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+  * 1/sqrt(d) uses d = width of one half (Q1, K1); V and the output are 2d wide.
+  * the lambda vectors have length d.
+  * RMSNorm over one head's 2d channels: x * (mean(x^2) + eps)^(-1/2) * w,
+    eps added inside the root.
+  * Y = (1 - lambda_init) * RMSNorm(O).
+  * the backward pass is not printed on the pages; ``backward`` derives it by
+    the chain rule from the forward definition.
+
+Parity pins (tests/test_oracle.py): lambda_init closed form and limits, zero
+lambda vectors, lambda = 0 against torch's float64 causal scaled-dot-product
+attention, Q2 = Q1 and K2 = K1 giving (1 - lambda) times softmax attention,
+rows of each map summing to one, row 0 attending only to V row 0, mask
+perturbation invariance, RMSNorm against torch's rms_norm, a scalar brute-force
+twin on tiny shapes, decode equal to the last prefill row, and central finite
+differences of the forward for every gradient.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+DEFAULT_EPS = 1e-5
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# lambda
+# --------------------------------------------------------------------------
+def lambda_init(layer: int) -> float:
+    """lambda_init = 0.8 - 0.6 * exp(-0.3 * (l - 1)) for layer index l >= 1.
+
+    [HADA] "Como a atencao diferencial funciona", lambda_init equation.
+    Evaluated left to right in float64: t = -0.3 * (l - 1); e = exp(t);
+    0.8 - (0.6 * e), each step rounded once.
+    """
+    if int(layer) != layer or layer < 1:
+        raise ValueError("layer index must be an integer >= 1")
+    t = -0.3 * float(layer - 1)
+    e = math.exp(t)
+    return 0.8 - 0.6 * e
+
+
+def lambda_scalar(lq1, lk1, lq2, lk2, layer: int) -> Dict[str, float]:
+    """lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init.
+
+    [HADA] "Como a atencao diferencial funciona", lambda equation; [PRIOR],
+    same formula.  One scalar per layer, shared by all heads ([INTOAI]
+    "Differential Attention With Multiple Heads").
+
+    The dot products are summed in index order in float64 (each product of
+    two float32 values is exact in float64).  The result is returned in float64
+    and rounded once to float32 (the value the kernels consume).
+    """
+    lq1, lk1, lq2, lk2 = (_f64(v).reshape(-1) for v in (lq1, lk1, lq2, lk2))
+    if not (lq1.shape == lk1.shape == lq2.shape == lk2.shape):
+        raise ValueError("lambda vectors must have equal length")
+    a = 0.0
+    for x, y in zip(lq1.tolist(), lk1.tolist()):
+        a = a + x * y
+    b = 0.0
+    for x, y in zip(lq2.tolist(), lk2.tolist()):
+        b = b + x * y
+    ea = math.exp(a)
+    eb = math.exp(b)
+    li = lambda_init(layer)
+    lam = (ea - eb) + li
+    return {
+        "lambda": lam, "lambda_init": li, "exp_a": ea, "exp_b": eb,
+        "lambda_f32": float(np.float32(lam)),
+        "lambda_init_f32": float(np.float32(li)),
+        "one_minus_init_f32": float(np.float32(1.0 - li)),
+    }
+
+
+# --------------------------------------------------------------------------
+# forward
+# --------------------------------------------------------------------------
+def causal_softmax(scores: np.ndarray, row_offset: int = 0) -> np.ndarray:
+    """Row softmax with the causal mask M.
+
+    scores[i, j] is query row (row_offset + i) against key j.  Entries with
+    j > row_offset + i are masked ([INTOAI] "A Deeper Dive Into Attention
+    Calculations": M is 0 where the query may see the key and -inf otherwise,
+    so those probabilities are exactly 0).  Two passes: subtract the row
+    maximum, exponentiate, divide by the row sum.
+    """
+    s = np.array(scores, dtype=np.float64, copy=True)
+    n_rows, n_cols = s.shape
+    rows = np.arange(n_rows)[:, None] + row_offset
+    cols = np.arange(n_cols)[None, :]
+    masked = cols > rows
+    s[masked] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    p[masked] = 0.0
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def attention_maps(q1, k1, q2, k2):
+    """A_k = causal_softmax(Q_k K_k^T / sqrt(d)) for one head, k = 1, 2.
+
+    [HADA] / [PRIOR] DiffAttn equation; d is the width of Q1 and K1.
+    """
+    q1, k1, q2, k2 = (_f64(x) for x in (q1, k1, q2, k2))
+    d = q1.shape[-1]
+    s = 1.0 / math.sqrt(d)
+    a1 = causal_softmax(s * (q1 @ k1.T))
+    a2 = causal_softmax(s * (q2 @ k2.T))
+    return a1, a2
+
+
+def rms_norm_rows(o: np.ndarray, eps: float = DEFAULT_EPS, weight=None):
+    """RMSNorm of each row over its full width: o * (mean(o^2) + eps)^(-1/2) * w.
+
+    Per head, independently ([HADA] "Estrutura multi-head e arquitetura
+    completa"; [INTOAI] "Differential Attention With Multiple Heads").
+    Returns (normalised rows, rstd per row).
+    """
+    o = _f64(o)
+    rstd = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    y = o * rstd
+    if weight is not None:
+        y = y * _f64(weight)
+    return y, rstd[..., 0]
+
+
+def head_forward(q1, q2, k1, k2, v, lam: float, lam_init: float,
+                 eps: float = DEFAULT_EPS, weight=None, block: int = 1024,
+                 want_saved: bool = False):
+    """DiffAttn for one head over a causal sequence, then norm and scale.
+
+    O = (A1 - lam * A2) V   ([HADA] / [PRIOR] DiffAttn equation, one product)
+    Y = (1 - lam_init) * RMSNorm(O)   ([INTOAI] multi-head section)
+
+    Query rows are processed in blocks of ``block`` rows against their causal
+    key range [0, last row of the block].  With ``want_saved`` it also returns
+    O1 = A1 V, O2 = A2 V, the log-sum-exp of each map's scaled scores, the
+    pre-norm O and rstd (the quantities the backward pass needs).
+    """
+    q1, q2, k1, k2, v = (_f64(x) for x in (q1, q2, k1, k2, v))
+    n, d = q1.shape
+    dv = v.shape[-1]
+    s = 1.0 / math.sqrt(d)
+    o = np.empty((n, dv))
+    saved = None
+    if want_saved:
+        saved = {"o1": np.empty((n, dv)), "o2": np.empty((n, dv)),
+                 "lse1": np.empty(n), "lse2": np.empty(n)}
+    for r0 in range(0, n, block):
+        r1 = min(n, r0 + block)
+        kend = r1                     # keys 0 .. r1-1 are the causal range
+        s1 = s * (q1[r0:r1] @ k1[:kend].T)
+        s2 = s * (q2[r0:r1] @ k2[:kend].T)
+        a1 = causal_softmax(s1, row_offset=r0)
+        a2 = causal_softmax(s2, row_offset=r0)
+        o[r0:r1] = (a1 - lam * a2) @ v[:kend]
+        if want_saved:
+            saved["o1"][r0:r1] = a1 @ v[:kend]
+            saved["o2"][r0:r1] = a2 @ v[:kend]
+            for name, sc in (("lse1", s1), ("lse2", s2)):
+                rows = np.arange(r1 - r0)[:, None] + r0
+                cols = np.arange(kend)[None, :]
+                sc = np.where(cols > rows, -np.inf, sc)
+                m = sc.max(axis=1)
+                saved[name][r0:r1] = m + np.log(np.exp(sc - m[:, None]).sum(axis=1))
+    y, rstd = rms_norm_rows(o, eps, weight)
+    y = (1.0 - lam_init) * y
+    if want_saved:
+        saved["o"] = o
+        saved["rstd"] = rstd
+        return y, saved
+    return y
+
+
+def forward(q1, q2, k1, k2, v, lam: float, lam_init: float, eps: float = DEFAULT_EPS,
+            weight=None, block: int = 1024, want_saved: bool = False, heads=None):
+    """Batched DiffAttn forward: tensors [B, H, N, d] and V [B, H, N, 2d].
+
+    ``weight`` is the per-channel RMSNorm weight, shape [H, 2d] or None (unit).
+    ``heads`` optionally restricts the work to a list of (b, h) pairs; the
+    other outputs are left as NaN.
+    Returns Y [B, H, N, 2d] (float64), and the saved quantities when asked.
+    """
+    q1 = np.asarray(q1)
+    B, H, N, _ = q1.shape
+    dv = np.asarray(v).shape[-1]
+    y = np.full((B, H, N, dv), np.nan)
+    saved = None
+    if want_saved:
+        saved = {k: np.full((B, H, N, dv), np.nan) for k in ("o1", "o2", "o")}
+        saved.update({k: np.full((B, H, N), np.nan) for k in ("lse1", "lse2", "rstd")})
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        w = None if weight is None else np.asarray(weight)[h]
+        r = head_forward(q1[b, h], q2[b, h], k1[b, h], k2[b, h], v[b, h], lam, lam_init,
+                         eps, w, block, want_saved)
+        if want_saved:
+            y[b, h], sv = r
+            for k in saved:
+                saved[k][b, h] = sv[k]
+        else:
+            y[b, h] = r
+    return (y, saved) if want_saved else y
+
+
+def forward_rows(q1, q2, k1, k2, v, rows, lam: float, lam_init: float,
+                 eps: float = DEFAULT_EPS, weight=None):
+    """DiffAttn output for selected query rows of one head only.
+
+    Row i sees keys 0..i.  Used to check sampled outputs at sizes where the
+    full oracle would take too long.  Same definition as ``head_forward``.
+    """
+    q1, q2, k1, k2, v = (_f64(x) for x in (q1, q2, k1, k2, v))
+    d = q1.shape[-1]
+    s = 1.0 / math.sqrt(d)
+    out = []
+    for i in rows:
+        i = int(i)
+        s1 = s * (k1[: i + 1] @ q1[i])
+        s2 = s * (k2[: i + 1] @ q2[i])
+        a1 = np.exp(s1 - s1.max())
+        a1 /= a1.sum()
+        a2 = np.exp(s2 - s2.max())
+        a2 /= a2.sum()
+        o = (a1 - lam * a2) @ v[: i + 1]
+        y, _ = rms_norm_rows(o[None, :], eps, weight)
+        out.append((1.0 - lam_init) * y[0])
+    return np.stack(out) if out else np.zeros((0, v.shape[-1]))
+
+
+def decode(q1, q2, k1c, k2c, vc, cache_len, lam: float, lam_init: float,
+           eps: float = DEFAULT_EPS, weight=None):
+    """One decode step: a single query per (b, h) against its cached keys.
+
+    q1, q2 [B, H, d]; k1c, k2c [B, H, L, d]; vc [B, H, L, 2d]; cache_len [B] or
+    None (= L).  The cache already holds the new token, so the query sits at
+    position len - 1 and sees keys 0 .. len - 1 (the causal mask of the
+    prefill, last row).  Returns Y [B, H, 2d].
+    """
+    q1 = np.asarray(q1)
+    B, H, d = q1.shape
+    L = np.asarray(k1c).shape[2]
+    dv = np.asarray(vc).shape[-1]
+    s = 1.0 / math.sqrt(d)
+    y = np.empty((B, H, dv))
+    for b in range(B):
+        n = L if cache_len is None else int(cache_len[b])
+        for h in range(H):
+            s1 = s * (_f64(k1c[b, h, :n]) @ _f64(q1[b, h]))
+            s2 = s * (_f64(k2c[b, h, :n]) @ _f64(q2[b, h]))
+            a1 = np.exp(s1 - s1.max())
+            a1 /= a1.sum()
+            a2 = np.exp(s2 - s2.max())
+            a2 /= a2.sum()
+            o = (a1 - lam * a2) @ _f64(vc[b, h, :n])
+            w = None if weight is None else np.asarray(weight)[h]
+            yy, _ = rms_norm_rows(o[None, :], eps, w)
+            y[b, h] = (1.0 - lam_init) * yy[0]
+    return y
+
+
+# --------------------------------------------------------------------------
+# backward (derived by the chain rule; the pages print no gradient formulas)
+# --------------------------------------------------------------------------
+def head_backward(q1, q2, k1, k2, v, dy, lam: float, lam_init: float,
+                  eps: float = DEFAULT_EPS, weight=None):
+    """Gradients of sum(Y * dY) for one head, with full N x N maps.
+
+    Forward: A_k = causal_softmax(s Q_k K_k^T), O = (A1 - lam A2) V,
+    Y = (1 - lam_init) * w * O * r with r = (mean(O^2) + eps)^(-1/2).
+
+    Chain rule, with g = (1 - lam_init) * w * dY and n = width of O:
+      G  = dL/dO = r * g - O * r^3 * rowsum(g * O) / n
+      dV = (A1 - lam A2)^T G
+      dA1 = G V^T,   dA2 = -lam G V^T
+      dS_k = A_k * (dA_k - rowsum(A_k * dA_k))      (softmax Jacobian)
+      dQ_k = s dS_k K_k,   dK_k = s dS_k^T Q_k
+      dlam = -sum(A2 * (G V^T)) = -sum_i rowsum(G * O2)
+    Returns a dict with dq1, dq2, dk1, dk2, dv, d_attn (= G) and dlam.
+    """
+    q1, q2, k1, k2, v, dy = (_f64(x) for x in (q1, q2, k1, k2, v, dy))
+    n, d = q1.shape
+    dv_w = v.shape[-1]
+    s = 1.0 / math.sqrt(d)
+    a1, a2 = attention_maps(q1, k1, q2, k2)
+    o = (a1 - lam * a2) @ v
+    r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    w = np.ones(dv_w) if weight is None else _f64(weight)
+    g = (1.0 - lam_init) * w * dy
+    G = r * g - o * r ** 3 * np.sum(g * o, axis=-1, keepdims=True) / dv_w
+    dv = (a1 - lam * a2).T @ G
+    gv = G @ v.T
+    da1 = gv
+    da2 = -lam * gv
+    ds1 = a1 * (da1 - np.sum(a1 * da1, axis=-1, keepdims=True))
+    ds2 = a2 * (da2 - np.sum(a2 * da2, axis=-1, keepdims=True))
+    return {
+        "dq1": s * ds1 @ k1, "dk1": s * ds1.T @ q1,
+        "dq2": s * ds2 @ k2, "dk2": s * ds2.T @ q2,
+        "dv": dv, "d_attn": G, "dlam": float(-np.sum(a2 * gv)),
+    }
+
+
+def backward(q1, q2, k1, k2, v, dy, lq1, lk1, lq2, lk2, layer: int,
+             eps: float = DEFAULT_EPS, weight=None, heads=None):
+    """Batched backward for tensors [B, H, N, *] and the four lambda vectors.
+
+    dlam sums over every (b, h) (lambda is one scalar per layer).  The lambda
+    vector gradients follow from lambda = exp(lq1.lk1) - exp(lq2.lk2) + init:
+      dlq1 = dlam e^a lk1, dlk1 = dlam e^a lq1,
+      dlq2 = -dlam e^b lk2, dlk2 = -dlam e^b lq2.
+    lambda_init is a constant of the layer index and receives no gradient.
+    ``heads`` restricts the per-head tensors to the listed (b, h) pairs (the
+    others stay NaN); dlam and the vector gradients then cover only those.
+    """
+    st = lambda_scalar(lq1, lk1, lq2, lk2, layer)
+    lam, li = st["lambda"], st["lambda_init"]
+    q1 = np.asarray(q1)
+    B, H, N, d = q1.shape
+    dvw = np.asarray(v).shape[-1]
+    out = {k: np.full((B, H, N, d), np.nan) for k in ("dq1", "dq2", "dk1", "dk2")}
+    out["dv"] = np.full((B, H, N, dvw), np.nan)
+    out["d_attn"] = np.full((B, H, N, dvw), np.nan)
+    dlam = 0.0
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        w = None if weight is None else np.asarray(weight)[h]
+        r = head_backward(q1[b, h], q2[b, h], k1[b, h], k2[b, h], v[b, h], dy[b, h],
+                          lam, li, eps, w)
+        for k in ("dq1", "dq2", "dk1", "dk2", "dv", "d_attn"):
+            out[k][b, h] = r[k]
+        dlam += r["dlam"]
+    lq1, lk1, lq2, lk2 = (_f64(x) for x in (lq1, lk1, lq2, lk2))
+    out["dlam"] = dlam
+    out["dlq1"] = dlam * st["exp_a"] * lk1
+    out["dlk1"] = dlam * st["exp_a"] * lq1
+    out["dlq2"] = -dlam * st["exp_b"] * lk2
+    out["dlk2"] = -dlam * st["exp_b"] * lq2
+    return out

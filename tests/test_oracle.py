@@ -1,0 +1,357 @@
+"""Pins of the float64 oracle against what the pages and mathematics fix.
+
+None of these tests compares the oracle with itself.  Each check is chosen so
+that a plausible mistake in the oracle (a dropped term, a wrong sign, a wrong
+index or scale, a transposed operand) fails at least one of them; the last
+test plants such mistakes in copies of the oracle and confirms that.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import diffattn_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def rand(r, *shape, scale=1.0):
+    return r.standard_normal(shape) * scale
+
+
+def sdpa_causal(q, k, v):
+    """torch's float64 CPU causal attention (scale 1/sqrt(q width))."""
+    t = [torch.from_numpy(np.ascontiguousarray(x)).double() for x in (q, k, v)]
+    return torch.nn.functional.scaled_dot_product_attention(
+        t[0], t[1], t[2], is_causal=True).numpy()
+
+
+# ---------------------------------------------------------------- lambda
+def test_lambda_init_against_page_endpoints():
+    g = json.load(open(os.path.join(GOLDEN, "lambda_init_endpoints.json")))
+    assert abs(orc.lambda_init(1) - g["layer_1"]) < 1e-15
+    assert abs(orc.lambda_init(200) - g["limit_deep_layers"]) < 1e-15
+    vals = [orc.lambda_init(l) for l in range(1, 60)]
+    assert all(b > a for a, b in zip(vals, vals[1:]))            # lower in early layers
+    decay = math.exp(-0.3)
+    for l in range(1, 40):                                        # gap to 0.8 shrinks by e^-0.3
+        gap0 = g["limit_deep_layers"] - orc.lambda_init(l)
+        gap1 = g["limit_deep_layers"] - orc.lambda_init(l + 1)
+        assert abs(gap1 - decay * gap0) < 1e-15
+    with pytest.raises(ValueError):
+        orc.lambda_init(0)
+
+
+def test_lambda_zero_vectors_is_lambda_init():
+    z = np.zeros(16, np.float32)
+    for l in (1, 4, 6, 8, 12):
+        st = orc.lambda_scalar(z, z, z, z, l)
+        assert st["lambda"] == orc.lambda_init(l)     # e^0 - e^0 = 0 exactly
+        assert st["exp_a"] == 1.0 and st["exp_b"] == 1.0
+
+
+def test_lambda_closed_form_logs():
+    # lq1 . lk1 = ln 3 and lq2 . lk2 = ln 2 give lambda = 3 - 2 + lambda_init
+    lq1 = np.zeros(8); lk1 = np.zeros(8); lq2 = np.zeros(8); lk2 = np.zeros(8)
+    lq1[3] = 1.0; lk1[3] = math.log(3.0)
+    lq2[5] = math.log(2.0); lk2[5] = 1.0
+    st = orc.lambda_scalar(lq1, lk1, lq2, lk2, 1)
+    assert abs(st["lambda"] - (1.0 + 0.2)) < 1e-14
+    assert abs(st["exp_a"] - 3.0) < 1e-14 and abs(st["exp_b"] - 2.0) < 1e-14
+    # the second pair enters with a minus sign and the first with a plus
+    st2 = orc.lambda_scalar(lq2, lk2, lq1, lk1, 1)
+    assert abs(st2["lambda"] - (-1.0 + 0.2)) < 1e-14
+    # only the dot product matters: spreading it over indices changes nothing
+    a = np.array([0.5, 0.25, -0.125, 0.0]); b = np.array([1.0, 2.0, 4.0, 3.0])
+    st3 = orc.lambda_scalar(a, b, np.zeros(4), np.zeros(4), 2)
+    assert abs(st3["exp_a"] - math.exp(0.5)) < 1e-15
+
+
+def test_lambda_f32_rounding_once():
+    r = rng(3)
+    v = [rand(r, 64, scale=0.1).astype(np.float32) for _ in range(4)]
+    st = orc.lambda_scalar(*v, 12)
+    assert st["lambda_f32"] == float(np.float32(st["lambda"]))
+    assert st["one_minus_init_f32"] == float(np.float32(1.0 - st["lambda_init"]))
+
+
+# ---------------------------------------------------------------- forward
+def test_rmsnorm_matches_torch():
+    r = rng(1)
+    x = rand(r, 7, 32)
+    w = rand(r, 32)
+    y, rstd = orc.rms_norm_rows(x, 1e-5, w)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (32,), torch.from_numpy(w), 1e-5)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-13, atol=1e-14)
+    # eps is added inside the root: a zero row stays zero and rstd = eps^-1/2
+    y0, r0 = orc.rms_norm_rows(np.zeros((1, 8)), 1e-5)
+    assert np.all(y0 == 0) and abs(r0[0] - 1e-5 ** -0.5) < 1e-9
+
+
+@pytest.mark.parametrize("n,d", [(1, 4), (13, 8), (64, 16), (97, 32)])
+def test_lambda_zero_is_causal_softmax_attention(n, d):
+    r = rng(n * 100 + d)
+    q1, k1, q2, k2 = (rand(r, 1, 1, n, d) for _ in range(4))
+    v = rand(r, 1, 1, n, 2 * d)
+    y, sv = orc.forward(q1, q2, k1, k2, v, 0.0, 0.3, want_saved=True, block=16)
+    ref = sdpa_causal(q1, k1, v)
+    np.testing.assert_allclose(sv["o"], ref, rtol=1e-12, atol=1e-13)
+    yref = 0.7 * torch.nn.functional.rms_norm(torch.from_numpy(ref), (2 * d,), eps=1e-5).numpy()
+    np.testing.assert_allclose(y, yref, rtol=1e-12, atol=1e-13)
+    # the second map's own output is softmax attention of (Q2, K2)
+    np.testing.assert_allclose(sv["o2"], sdpa_causal(q2, k2, v), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("lam", [0.2, 0.55, -0.3, 1.7])
+def test_identical_maps_scale_softmax_attention(lam):
+    r = rng(7)
+    n, d = 50, 16
+    q = rand(r, 1, 2, n, d)
+    k = rand(r, 1, 2, n, d)
+    v = rand(r, 1, 2, n, 2 * d)
+    _, sv = orc.forward(q, q, k, k, v, lam, 0.5, want_saved=True, block=17)
+    np.testing.assert_allclose(sv["o"], (1.0 - lam) * sdpa_causal(q, k, v), rtol=1e-11, atol=1e-12)
+
+
+def test_identical_maps_lambda_one_is_zero():
+    r = rng(8)
+    q = rand(r, 2, 3, 33, 8); k = rand(r, 2, 3, 33, 8); v = rand(r, 2, 3, 33, 16)
+    y = orc.forward(q, q, k, k, v, 1.0, 0.2)
+    assert np.all(y == 0.0)
+
+
+def test_rows_sum_to_one():
+    r = rng(9)
+    n, d = 40, 8
+    q1, k1, q2, k2 = (rand(r, n, d) for _ in range(4))
+    a1, a2 = orc.attention_maps(q1, k1, q2, k2)
+    np.testing.assert_allclose(a1.sum(1), 1.0, atol=1e-14)
+    np.testing.assert_allclose(a2.sum(1), 1.0, atol=1e-14)
+    assert np.all(np.triu(a1, 1) == 0) and np.all(np.triu(a2, 1) == 0)
+    # V = ones: every row of (A1 - lam A2) V equals 1 - lam
+    lam = 0.37
+    _, sv = orc.forward(q1[None, None], q2[None, None], k1[None, None], k2[None, None],
+                        np.ones((1, 1, n, 2 * d)), lam, 0.1, want_saved=True)
+    np.testing.assert_allclose(sv["o"], 1.0 - lam, atol=1e-14)
+
+
+def test_row_zero_attends_only_to_v0():
+    r = rng(10)
+    n, d = 24, 16
+    q1, k1, q2, k2 = (rand(r, 1, 1, n, d) for _ in range(4))
+    v = rand(r, 1, 1, n, 2 * d)
+    lam, li, eps = 0.61, 0.556, 1e-5
+    y, sv = orc.forward(q1, q2, k1, k2, v, lam, li, eps=eps, want_saved=True)
+    v0 = v[0, 0, 0]
+    np.testing.assert_allclose(sv["o"][0, 0, 0], (1 - lam) * v0, rtol=1e-14)
+    yexp = (1 - li) * (1 - lam) * v0 / math.sqrt((1 - lam) ** 2 * np.mean(v0 ** 2) + eps)
+    np.testing.assert_allclose(y[0, 0, 0], yexp, rtol=1e-13)
+
+
+def test_mask_perturbation_invariance():
+    r = rng(11)
+    n, d = 70, 16
+    q1, q2, k1, k2 = (rand(r, 1, 1, n, d) for _ in range(4))
+    v = rand(r, 1, 1, n, 2 * d)
+    y0 = orc.forward(q1, q2, k1, k2, v, 0.4, 0.2, block=32)
+    i0 = 41
+    k1p, k2p, vp = k1.copy(), k2.copy(), v.copy()
+    k1p[..., i0 + 1:, :] += 5.0
+    k2p[..., i0 + 1:, :] -= 3.0
+    vp[..., i0 + 1:, :] *= -7.0
+    y1 = orc.forward(q1, q2, k1p, k2p, vp, 0.4, 0.2, block=32)
+    assert np.array_equal(y0[..., : i0 + 1, :], y1[..., : i0 + 1, :])
+    assert not np.allclose(y0[..., i0 + 1:, :], y1[..., i0 + 1:, :])
+
+
+def brute_force(q1, q2, k1, k2, v, lam, li, eps):
+    """Scalar loops over every element (one head)."""
+    n, d = len(q1), len(q1[0])
+    dv = len(v[0])
+    s = 1.0 / math.sqrt(d)
+    out = []
+    for i in range(n):
+        maps = []
+        for q, k in ((q1, k1), (q2, k2)):
+            sc = []
+            for j in range(i + 1):
+                acc = 0.0
+                for t in range(d):
+                    acc += q[i][t] * k[j][t]
+                sc.append(acc * s)
+            mx = max(sc)
+            e = [math.exp(x - mx) for x in sc]
+            tot = sum(e)
+            maps.append([x / tot for x in e])
+        o = []
+        for c in range(dv):
+            acc = 0.0
+            for j in range(i + 1):
+                acc += (maps[0][j] - lam * maps[1][j]) * v[j][c]
+            o.append(acc)
+        ms = sum(x * x for x in o) / dv
+        rs = 1.0 / math.sqrt(ms + eps)
+        out.append([(1.0 - li) * x * rs for x in o])
+    return out
+
+
+@pytest.mark.parametrize("n,d,lam", [(1, 2, 0.5), (5, 4, 0.2), (16, 8, 0.83), (11, 3, -0.4)])
+def test_brute_force_twin(n, d, lam):
+    r = rng(n + 31 * d)
+    q1, q2, k1, k2 = (rand(r, n, d) for _ in range(4))
+    v = rand(r, n, 2 * d)
+    li = 0.666
+    bf = np.array(brute_force(q1.tolist(), q2.tolist(), k1.tolist(), k2.tolist(), v.tolist(),
+                              lam, li, 1e-5))
+    y = orc.forward(q1[None, None], q2[None, None], k1[None, None], k2[None, None],
+                    v[None, None], lam, li, block=4)[0, 0]
+    np.testing.assert_allclose(y, bf, rtol=1e-12, atol=1e-12)
+    rows = list(range(n))
+    np.testing.assert_allclose(orc.forward_rows(q1, q2, k1, k2, v, rows, lam, li), bf,
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_decode_equals_last_prefill_row():
+    r = rng(12)
+    B, H, L, d = 3, 2, 37, 16
+    q1, q2, k1, k2 = (rand(r, B, H, L, d) for _ in range(4))
+    v = rand(r, B, H, L, 2 * d)
+    lam, li = 0.45, 0.72
+    y = orc.forward(q1, q2, k1, k2, v, lam, li)
+    lens = np.array([L, 1, 20])
+    qd1 = np.stack([q1[b, :, lens[b] - 1] for b in range(B)])
+    qd2 = np.stack([q2[b, :, lens[b] - 1] for b in range(B)])
+    yd = orc.decode(qd1, qd2, k1, k2, v, lens, lam, li)
+    for b in range(B):
+        np.testing.assert_allclose(yd[b], y[b, :, lens[b] - 1], rtol=1e-12, atol=1e-13)
+    yfull = orc.decode(q1[:, :, -1], q2[:, :, -1], k1, k2, v, None, lam, li)
+    np.testing.assert_allclose(yfull, y[:, :, -1], rtol=1e-12, atol=1e-13)
+
+
+def test_saved_lse_is_log_normaliser():
+    r = rng(13)
+    n, d = 30, 8
+    q1, q2, k1, k2 = (rand(r, n, d) for _ in range(4))
+    v = rand(r, n, 2 * d)
+    _, sv = orc.head_forward(q1, q2, k1, k2, v, 0.3, 0.2, want_saved=True, block=7)
+    s = 1.0 / math.sqrt(d)
+    for i in (0, 5, 29):
+        ref = np.log(np.sum(np.exp(s * (k1[: i + 1] @ q1[i]))))
+        assert abs(sv["lse1"][i] - ref) < 1e-12
+    np.testing.assert_allclose(sv["o1"] - 0.3 * sv["o2"], sv["o"], atol=1e-13)
+
+
+# ---------------------------------------------------------------- backward
+def _loss(p, dy, layer, eps, weight):
+    st = orc.lambda_scalar(p["lq1"], p["lk1"], p["lq2"], p["lk2"], layer)
+    y = orc.forward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"], st["lambda"],
+                    st["lambda_init"], eps=eps, weight=weight)
+    return float(np.sum(y * dy))
+
+
+def _fd_check(n, d, B, H, layer, n_samples, seed, weight_on):
+    r = rng(seed)
+    p = {k: rand(r, B, H, n, d) for k in ("q1", "q2", "k1", "k2")}
+    p["v"] = rand(r, B, H, n, 2 * d)
+    for k in ("lq1", "lk1", "lq2", "lk2"):
+        p[k] = rand(r, d, scale=0.1)
+    dy = rand(r, B, H, n, 2 * d)
+    weight = (1.0 + 0.3 * rand(r, H, 2 * d)) if weight_on else None
+    eps = 1e-5
+    g = orc.backward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"], dy, p["lq1"], p["lk1"],
+                     p["lq2"], p["lk2"], layer, eps=eps, weight=weight)
+    h = 1e-6
+    for name, gname in (("q1", "dq1"), ("q2", "dq2"), ("k1", "dk1"), ("k2", "dk2"),
+                        ("v", "dv"), ("lq1", "dlq1"), ("lk1", "dlk1"), ("lq2", "dlq2"),
+                        ("lk2", "dlk2")):
+        x = p[name]
+        flat = x.reshape(-1)
+        idx = np.arange(flat.size) if flat.size <= n_samples else \
+            r.choice(flat.size, n_samples, replace=False)
+        fd = np.empty(len(idx))
+        for t, i in enumerate(idx):
+            old = flat[i]
+            flat[i] = old + h
+            lp = _loss(p, dy, layer, eps, weight)
+            flat[i] = old - h
+            lm = _loss(p, dy, layer, eps, weight)
+            flat[i] = old
+            fd[t] = (lp - lm) / (2 * h)
+        an = g[gname].reshape(-1)[idx]
+        scale = max(np.max(np.abs(an)), 1e-12)
+        assert np.max(np.abs(an - fd)) / scale < 2e-6, name
+    # gradient at the RMSNorm input: perturb O directly through the norm
+    st = orc.lambda_scalar(p["lq1"], p["lk1"], p["lq2"], p["lk2"], layer)
+    _, sv = orc.forward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"], st["lambda"],
+                        st["lambda_init"], eps=eps, weight=weight, want_saved=True)
+    o = sv["o"]
+    for (b, hh, i) in [(0, 0, 0), (B - 1, H - 1, n - 1), (0, H - 1, n // 2)]:
+        w = None if weight is None else weight[hh]
+        def f(row):
+            y, _ = orc.rms_norm_rows(row[None], eps, w)
+            return float(np.sum((1 - st["lambda_init"]) * y[0] * dy[b, hh, i]))
+        row = o[b, hh, i].copy()
+        fd = np.empty_like(row)
+        for c in range(row.size):
+            rp = row.copy(); rp[c] += h
+            rm = row.copy(); rm[c] -= h
+            fd[c] = (f(rp) - f(rm)) / (2 * h)
+        np.testing.assert_allclose(g["d_attn"][b, hh, i], fd, rtol=2e-6,
+                                   atol=2e-6 * np.max(np.abs(fd)))
+    # dlam = -sum over (b, h, i) of rowsum(G * O2)
+    assert abs(g["dlam"] + np.sum(g["d_attn"] * sv["o2"])) < 1e-9 * max(1, abs(g["dlam"]))
+
+
+def test_backward_finite_differences_small_full():
+    _fd_check(n=9, d=4, B=1, H=2, layer=3, n_samples=10 ** 9, seed=21, weight_on=True)
+
+
+def test_backward_finite_differences_one_head_n32():
+    # one head, N = 32, d = 64: the shape of a single head of the training workload
+    _fd_check(n=32, d=64, B=1, H=1, layer=6, n_samples=96, seed=22, weight_on=False)
+
+
+# ---------------------------------------------------------------- planted mistakes
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Copies of the oracle with one planted mistake each fail a pin above."""
+    r = rng(40)
+    n, d = 20, 8
+    q1, q2, k1, k2 = (rand(r, 1, 1, n, d) for _ in range(4))
+    v = rand(r, 1, 1, n, 2 * d)
+    ref = sdpa_causal(q1, k1, v)
+
+    def pins_hold():
+        _, sv = orc.forward(q1, q2, k1, k2, v, 0.0, 0.3, want_saved=True)
+        ok = np.allclose(sv["o"], ref, rtol=1e-10, atol=1e-11)
+        _, sv2 = orc.forward(q1, q1, k1, k1, v, 0.4, 0.3, want_saved=True)
+        ok &= np.allclose(sv2["o"], 0.6 * ref, rtol=1e-10, atol=1e-11)
+        return bool(ok)
+
+    assert pins_hold()
+    good_softmax = orc.causal_softmax
+
+    # 1. mask dropped
+    monkeypatch.setattr(orc, "causal_softmax",
+                        lambda s, row_offset=0: np.exp(s - s.max(1, keepdims=True)) /
+                        np.exp(s - s.max(1, keepdims=True)).sum(1, keepdims=True))
+    assert not pins_hold()
+    monkeypatch.setattr(orc, "causal_softmax", good_softmax)
+    # 2. mask off by one (query may not see itself)
+    def shifted(s, row_offset=0):
+        return good_softmax(s[:, :], row_offset=row_offset - 1) if s.shape[0] > 1 else good_softmax(s)
+    monkeypatch.setattr(orc, "causal_softmax", shifted)
+    assert not pins_hold()
+    monkeypatch.setattr(orc, "causal_softmax", good_softmax)
+    # 3. scale by 1/sqrt(2d) instead of 1/sqrt(d)
+    good_sqrt = orc.math.sqrt
+    monkeypatch.setattr(orc.math, "sqrt", lambda x: good_sqrt(2 * x))
+    assert not pins_hold()
+    monkeypatch.setattr(orc.math, "sqrt", good_sqrt)
+    assert pins_hold()
