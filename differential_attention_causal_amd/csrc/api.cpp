@@ -1,0 +1,310 @@
+// libdiffattn C-ABI: argument validation, workspace sizing and kernel launches.
+//
+// Every entry point validates its arguments on the host before any HIP call, so the
+// checks also run on a machine without a GPU. Launch failures are reported as
+// DIFFATTN_E_HIP with the hipError_t kept per thread.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "diffattn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+bool env_log() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("DIFFATTN_LOG");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+diffattn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DIFFATTN_OK;
+  g_last_hip = static_cast<int>(e);
+  if (env_log()) fprintf(stderr, "[diffattn] %s: hip error %d\n", what, static_cast<int>(e));
+  return DIFFATTN_E_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+bool overlap(Span a, Span b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+  return x < y + b.n && y < x + a.n;
+}
+
+// Any output span overlapping any input span, or two outputs overlapping each other.
+bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
+  for (int i = 0; i < no; ++i) {
+    for (int j = 0; j < ni; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < no; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+size_t elem_bytes(diffattn_dtype t) { return t == DIFFATTN_FP32 ? 4 : 2; }
+
+// Validates the problem descriptor. Sets *empty when there is nothing to compute.
+diffattn_status check_problem(const diffattn_problem* p, bool* empty) {
+  if (!p) return DIFFATTN_E_ARG;
+  if (p->batch < 0 || p->heads < 0 || p->seqlen < 0) return DIFFATTN_E_ARG;
+  if (p->head_dim <= 0) return DIFFATTN_E_ARG;
+  if (p->dtype != DIFFATTN_FP32 && p->dtype != DIFFATTN_BF16) return DIFFATTN_E_ARG;
+  if (!(p->rms_eps >= 0.0f) || !isfinite(p->rms_eps)) return DIFFATTN_E_ARG;
+  if (p->causal != 1) return DIFFATTN_E_UNSUPPORTED;
+  // Largest tensor: [B, H, N, 2d] float32 must stay far from int64 overflow.
+  int64_t t = 0;
+  if (__builtin_mul_overflow(p->batch, p->heads, &t) ||
+      __builtin_mul_overflow(t, p->seqlen, &t) ||
+      __builtin_mul_overflow(t, static_cast<int64_t>(2 * p->head_dim) * 4, &t) ||
+      t > (static_cast<int64_t>(1) << 46))
+    return DIFFATTN_E_ARG;
+  *empty = p->batch == 0 || p->heads == 0 || p->seqlen == 0;
+  return DIFFATTN_OK;
+}
+
+size_t decode_ws_bytes(const diffattn_problem* p) {
+  int ns = 0, sl = 0;
+  diffattn::decode_split_geometry(p->batch, p->heads, p->seqlen, &ns, &sl);
+  // per (b, h, split): two maps x (m, l, 2d accumulators)
+  return static_cast<size_t>(p->batch) * p->heads * ns * 2 * (2 + 2 * p->head_dim) *
+         sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* diffattn_status_string(diffattn_status s) {
+  switch (s) {
+    case DIFFATTN_OK: return "DIFFATTN_OK";
+    case DIFFATTN_E_ARG: return "DIFFATTN_E_ARG: invalid argument";
+    case DIFFATTN_E_UNSUPPORTED: return "DIFFATTN_E_UNSUPPORTED: unsupported configuration";
+    case DIFFATTN_E_WORKSPACE: return "DIFFATTN_E_WORKSPACE: workspace missing or too small";
+    case DIFFATTN_E_HIP: return "DIFFATTN_E_HIP: HIP runtime error";
+  }
+  return "DIFFATTN_E_?: unknown status";
+}
+
+int diffattn_last_hip_error(void) { return g_last_hip; }
+
+size_t diffattn_workspace_bytes(diffattn_op op, const diffattn_problem* p) {
+  bool empty = false;
+  if (check_problem(p, &empty) != DIFFATTN_OK || empty) return 0;
+  switch (op) {
+    case DIFFATTN_OP_FWD: return 0;
+    case DIFFATTN_OP_DECODE: return decode_ws_bytes(p);
+    case DIFFATTN_OP_BWD:
+      return diffattn::bwd_workspace_floats(p->batch, p->heads, p->seqlen, p->head_dim) *
+             sizeof(float);
+  }
+  return 0;
+}
+
+diffattn_status diffattn_lambda(int32_t dim, int32_t layer_idx, const float* lq1,
+                                const float* lk1, const float* lq2, const float* lk2,
+                                diffattn_lambda_state* state_out, void* stream) {
+  if (dim < 1 || dim > 1024 || layer_idx < 1) return DIFFATTN_E_ARG;
+  if (!lq1 || !lk1 || !lq2 || !lk2 || !state_out) return DIFFATTN_E_ARG;
+  if (!aligned(lq1, 4) || !aligned(lk1, 4) || !aligned(lq2, 4) || !aligned(lk2, 4) ||
+      !aligned(state_out, 8))
+    return DIFFATTN_E_ARG;
+  const size_t vb = static_cast<size_t>(dim) * sizeof(float);
+  const Span out[1] = {{state_out, sizeof(diffattn_lambda_state)}};
+  const Span in[4] = {{lq1, vb}, {lk1, vb}, {lq2, vb}, {lk2, vb}};
+  if (any_overlap(out, 1, in, 4)) return DIFFATTN_E_ARG;
+  return hip_status(diffattn::launch_lambda(dim, layer_idx, lq1, lk1, lq2, lk2, state_out,
+                                            static_cast<hipStream_t>(stream)),
+                    "lambda");
+}
+
+diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const void* q2,
+                             const void* k1, const void* k2, const void* v,
+                             const diffattn_lambda_state* lam, const float* rms_weight,
+                             void* out, const diffattn_saved* saved, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  bool empty = false;
+  diffattn_status st = check_problem(p, &empty);
+  if (st != DIFFATTN_OK) return st;
+  const int d = p->head_dim;
+  if (p->dtype == DIFFATTN_FP32) {
+    if (d != 16 && d != 32 && d != 64) return DIFFATTN_E_UNSUPPORTED;
+    if (saved) return DIFFATTN_E_UNSUPPORTED;
+    if (p->batch * p->heads > 65535) return DIFFATTN_E_UNSUPPORTED;
+  } else {
+    if (d != 64) return DIFFATTN_E_UNSUPPORTED;
+  }
+  if (empty) return DIFFATTN_OK;
+  if (!q1 || !q2 || !k1 || !k2 || !v || !lam || !out) return DIFFATTN_E_ARG;
+  const void* ptrs[6] = {q1, q2, k1, k2, v, out};
+  for (const void* x : ptrs)
+    if (!aligned(x, 16)) return DIFFATTN_E_ARG;
+  if (!aligned(lam, 8) || (rms_weight && !aligned(rms_weight, 16))) return DIFFATTN_E_ARG;
+  const size_t rows = static_cast<size_t>(p->batch) * p->heads * p->seqlen;
+  const size_t eb = elem_bytes(p->dtype);
+  const size_t qk = rows * d * eb, vb = rows * 2 * d * eb;
+  const Span in[7] = {{q1, qk}, {q2, qk}, {k1, qk}, {k2, qk}, {v, vb},
+                      {lam, sizeof(diffattn_lambda_state)},
+                      {rms_weight, static_cast<size_t>(p->heads) * 2 * d * sizeof(float)}};
+  diffattn::FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  if (saved) {
+    const diffattn_saved& s = *saved;
+    if (!s.lse1 || !s.lse2 || !s.o1 || !s.o2 || !s.rstd) return DIFFATTN_E_ARG;
+    if (!aligned(s.lse1, 4) || !aligned(s.lse2, 4) || !aligned(s.rstd, 4) ||
+        !aligned(s.o1, 16) || !aligned(s.o2, 16))
+      return DIFFATTN_E_ARG;
+    const size_t rb = rows * sizeof(float), ob = rows * 2 * d * sizeof(float);
+    const Span outs[6] = {{out, vb}, {s.lse1, rb}, {s.lse2, rb}, {s.o1, ob}, {s.o2, ob},
+                          {s.rstd, rb}};
+    if (any_overlap(outs, 6, in, 7)) return DIFFATTN_E_ARG;
+    a.saved = s;
+    a.training = true;
+  } else {
+    const Span outs[1] = {{out, vb}};
+    if (any_overlap(outs, 1, in, 7)) return DIFFATTN_E_ARG;
+  }
+  a.q1 = q1; a.q2 = q2; a.k1 = k1; a.k2 = k2; a.v = v;
+  a.lam = lam;
+  a.rms_weight = rms_weight;
+  a.out = out;
+  a.B = p->batch; a.H = p->heads; a.N = p->seqlen;
+  a.d = d;
+  a.eps = p->rms_eps;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == DIFFATTN_FP32) return hip_status(diffattn::launch_fwd_fp32(a, s), "fwd_fp32");
+  return hip_status(diffattn::launch_fwd_bf16(a, s), "fwd_bf16");
+}
+
+diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const void* q2,
+                                const void* k1c, const void* k2c, const void* vc,
+                                const int32_t* cache_len, const diffattn_lambda_state* lam,
+                                const float* rms_weight, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  diffattn_status st = check_problem(p, &empty);
+  if (st != DIFFATTN_OK) return st;
+  if (p->dtype != DIFFATTN_BF16 || p->head_dim != 64) return DIFFATTN_E_UNSUPPORTED;
+  if (p->batch * p->heads > 65535 || p->seqlen > (static_cast<int64_t>(1) << 31))
+    return DIFFATTN_E_UNSUPPORTED;
+  if (empty) return DIFFATTN_OK;
+  if (!q1 || !q2 || !k1c || !k2c || !vc || !lam || !out) return DIFFATTN_E_ARG;
+  const void* ptrs[6] = {q1, q2, k1c, k2c, vc, out};
+  for (const void* x : ptrs)
+    if (!aligned(x, 16)) return DIFFATTN_E_ARG;
+  if (!aligned(lam, 8) || (rms_weight && !aligned(rms_weight, 16)) ||
+      (cache_len && !aligned(cache_len, 4)))
+    return DIFFATTN_E_ARG;
+  const size_t need = decode_ws_bytes(p);
+  if (!workspace || workspace_bytes < need) return DIFFATTN_E_WORKSPACE;
+  if (!aligned(workspace, 16)) return DIFFATTN_E_ARG;
+  const int d = p->head_dim;
+  const size_t bh = static_cast<size_t>(p->batch) * p->heads;
+  const size_t qb = bh * d * 2, kb = bh * p->seqlen * d * 2, vb = bh * p->seqlen * 2 * d * 2;
+  const Span in[8] = {{q1, qb}, {q2, qb}, {k1c, kb}, {k2c, kb}, {vc, vb},
+                      {cache_len, static_cast<size_t>(p->batch) * 4},
+                      {lam, sizeof(diffattn_lambda_state)},
+                      {rms_weight, static_cast<size_t>(p->heads) * 2 * d * sizeof(float)}};
+  const Span outs[2] = {{out, bh * 2 * d * 2}, {workspace, need}};
+  if (any_overlap(outs, 2, in, 8)) return DIFFATTN_E_ARG;
+  diffattn::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q1 = q1; a.q2 = q2; a.k1 = k1c; a.k2 = k2c; a.v = vc;
+  a.cache_len = cache_len;
+  a.lam = lam;
+  a.rms_weight = rms_weight;
+  a.out = out;
+  a.partial = static_cast<float*>(workspace);
+  a.B = p->batch; a.H = p->heads; a.L = p->seqlen;
+  diffattn::decode_split_geometry(a.B, a.H, a.L, &a.n_split, &a.split_len);
+  a.d = d;
+  a.eps = p->rms_eps;
+  return hip_status(diffattn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)), "decode");
+}
+
+diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const void* q2,
+                             const void* k1, const void* k2, const void* v, const float* lq1,
+                             const float* lk1, const float* lq2, const float* lk2,
+                             const diffattn_lambda_state* lam, const float* rms_weight,
+                             const diffattn_saved* saved, const void* dout, void* dq1,
+                             void* dq2, void* dk1, void* dk2, void* dv, float* d_attn,
+                             float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  diffattn_status st = check_problem(p, &empty);
+  if (st != DIFFATTN_OK) return st;
+  if (p->dtype != DIFFATTN_BF16 || p->head_dim != 64) return DIFFATTN_E_UNSUPPORTED;
+  const int d = p->head_dim;
+  // The lambda-vector gradients exist even for an empty problem (they are then zero).
+  if (!lq1 || !lk1 || !lq2 || !lk2 || !lam || !dlq1 || !dlk1 || !dlq2 || !dlk2)
+    return DIFFATTN_E_ARG;
+  if (!empty) {
+    if (!q1 || !q2 || !k1 || !k2 || !v || !saved || !dout || !dq1 || !dq2 || !dk1 || !dk2 ||
+        !dv || !d_attn)
+      return DIFFATTN_E_ARG;
+    const diffattn_saved& s = *saved;
+    if (!s.lse1 || !s.lse2 || !s.o1 || !s.o2 || !s.rstd) return DIFFATTN_E_ARG;
+    const void* p16[14] = {q1, q2, k1, k2, v, dout, dq1, dq2, dk1, dk2, dv, d_attn, s.o1, s.o2};
+    for (const void* x : p16)
+      if (!aligned(x, 16)) return DIFFATTN_E_ARG;
+    if (!aligned(s.lse1, 4) || !aligned(s.lse2, 4) || !aligned(s.rstd, 4))
+      return DIFFATTN_E_ARG;
+  }
+  const void* p4[4] = {lq1, lk1, lq2, lk2};
+  for (const void* x : p4)
+    if (!aligned(x, 4)) return DIFFATTN_E_ARG;
+  if (!aligned(dlq1, 4) || !aligned(dlk1, 4) || !aligned(dlq2, 4) || !aligned(dlk2, 4) ||
+      !aligned(lam, 8) || (rms_weight && !aligned(rms_weight, 16)))
+    return DIFFATTN_E_ARG;
+  const size_t need = diffattn_workspace_bytes(DIFFATTN_OP_BWD, p);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DIFFATTN_E_WORKSPACE;
+  if (workspace && !aligned(workspace, 16)) return DIFFATTN_E_ARG;
+  const size_t rows = static_cast<size_t>(p->batch) * p->heads * p->seqlen;
+  const size_t qk = rows * d * 2, vb = rows * 2 * d * 2, rb = rows * 4, ob = rows * 2 * d * 4;
+  const size_t lb = static_cast<size_t>(d) * 4;
+  const diffattn_saved s = saved ? *saved : diffattn_saved{nullptr, nullptr, nullptr, nullptr, nullptr};
+  const Span in[16] = {{q1, qk}, {q2, qk}, {k1, qk}, {k2, qk}, {v, vb}, {dout, vb},
+                       {lq1, lb}, {lk1, lb}, {lq2, lb}, {lk2, lb},
+                       {lam, sizeof(diffattn_lambda_state)},
+                       {rms_weight, static_cast<size_t>(p->heads) * 2 * d * sizeof(float)},
+                       {s.lse1, rb}, {s.lse2, rb}, {s.o1, ob}, {s.o2, ob}};
+  const Span outs[11] = {{dq1, qk}, {dq2, qk}, {dk1, qk}, {dk2, qk}, {dv, vb}, {d_attn, ob},
+                         {dlq1, lb}, {dlk1, lb}, {dlq2, lb}, {dlk2, lb}, {workspace, need}};
+  if (any_overlap(outs, 11, in, 16) || overlap(outs[0], {s.rstd, rb})) return DIFFATTN_E_ARG;
+  for (int i = 0; i < 11; ++i)
+    if (overlap(outs[i], {s.rstd, rb})) return DIFFATTN_E_ARG;
+  diffattn::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q1 = q1; a.q2 = q2; a.k1 = k1; a.k2 = k2; a.v = v; a.dout = dout;
+  a.lq1 = lq1; a.lk1 = lk1; a.lq2 = lq2; a.lk2 = lk2;
+  a.lam = lam;
+  a.rms_weight = rms_weight;
+  a.saved = s;
+  a.dq1 = dq1; a.dq2 = dq2; a.dk1 = dk1; a.dk2 = dk2; a.dv = dv;
+  a.d_attn = d_attn;
+  a.dlq1 = dlq1; a.dlk1 = dlk1; a.dlq2 = dlq2; a.dlk2 = dlk2;
+  a.ws = static_cast<float*>(workspace);
+  a.B = empty ? 0 : p->batch; a.H = p->heads; a.N = p->seqlen;
+  a.d = d;
+  return hip_status(diffattn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream)), "bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,286 @@
+// Split-KV decode step for causal DiffAttn, bf16 cache, d = 64 (V and output 128 wide).
+//
+// One new query per (b, h) attends to every cached key 0 .. len-1 (it is the last row of
+// the causal mask; intoai.pub "A Deeper Dive Into Attention Calculations"), through both
+// maps of the DiffAttn equation (pt.news.hada.io "Como a atencao diferencial funciona").
+// Generating a token re-reads the whole K1/K2/V cache from HBM (priorstack.com, "The
+// Memory Wall: Why the KV Cache Constrains LLM Serving"), so the kernel is a streaming
+// read: every cache byte is loaded exactly once, with 16-byte loads, and no LDS staging.
+//
+// Pass 1 (decode_split_kernel), grid = splits x (B*H): a workgroup of 4 wavefronts takes
+// one split of the cache; each wavefront walks 64-key rounds of its share:
+//   * scores: 8 lanes per key, each lane a 16-byte slice of the K1 and K2 rows, so one
+//     wave instruction reads 8 whole rows (1 KiB contiguous); the 8 partial dot products
+//     are summed across the lanes;
+//   * per map: running max m, normaliser l, and p_j = exp2(s_j log2(e)/sqrt(d) - m);
+//   * values: 16 lanes per V row (16 bytes each), 4 rows per instruction; each lane keeps
+//     8 output channels of both accumulators.
+// The four wavefront states are merged in LDS and written as one partial
+// (m, l, acc[128]) per map and split.
+// Pass 2 (decode_combine_kernel), grid = B*H: exact log-sum-exp merge of the splits,
+// O = acc1/l1 - lambda acc2/l2, RMSNorm over the 128 channels, x (1 - lambda_init).
+#include "common.h"
+#include "launch.h"
+
+namespace diffattn {
+namespace dec {
+
+constexpr int D = 64;
+constexpr int DV = 128;
+constexpr int NT = 256;
+constexpr int KEYS_PER_ROUND = 64;          // per wavefront
+constexpr int PART = 2 + DV;                // m, l, acc[DV]
+
+__global__ void __launch_bounds__(NT) decode_split_kernel(
+    const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
+    const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
+    const bf16_t* __restrict__ v, const int32_t* __restrict__ cache_len,
+    float* __restrict__ partial, int64_t H, int64_t L, int n_split, int rounds) {
+  __shared__ float red[4][2][PART];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int split = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / H;
+  int64_t len = cache_len ? static_cast<int64_t>(cache_len[b]) : L;
+  len = len < 1 ? 1 : (len > L ? L : len);
+  const int64_t split_len = static_cast<int64_t>(KEYS_PER_ROUND) * 4 * rounds;
+  const int64_t s0 = static_cast<int64_t>(split) * split_len;
+  if (s0 >= len) return;  // the combine pass reads only splits that start below len
+
+  const bf16_t* K1 = k1 + bh * L * D;
+  const bf16_t* K2 = k2 + bh * L * D;
+  const bf16_t* V = v + bh * L * DV;
+
+  // Score lanes: key r = lane / 8 of each group of 8, channel slice c = lane % 8.
+  const int r = lane >> 3, c = lane & 7;
+  float qa[8], qb[8];
+  {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(q1 + bh * D + 8 * c);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(q2 + bh * D + 8 * c);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      qa[2 * t] = __uint_as_float(x[t] << 16);
+      qa[2 * t + 1] = __uint_as_float(x[t] & 0xffff0000u);
+      qb[2 * t] = __uint_as_float(y[t] << 16);
+      qb[2 * t + 1] = __uint_as_float(y[t] & 0xffff0000u);
+    }
+  }
+  // Value lanes: channel slice e = lane % 16 (channels 8e..8e+7), key phase f = lane / 16.
+  const int e = lane & 15, f = lane >> 4;
+
+  const float cs = kLog2e / 8.0f;  // log2(e) / sqrt(64)
+  float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
+  float acc1[8], acc2[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc1[t] = acc2[t] = 0.f;
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int64_t kb = s0 + (static_cast<int64_t>(wv) * rounds + rd) * KEYS_PER_ROUND;
+    if (kb >= len) break;
+    // ---- scores of the 64 keys kb + 8 g + r
+    u32x4 kx[8], ky[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int64_t key = kb + 8 * g + r;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      kx[g] = key < len ? *reinterpret_cast<const u32x4*>(K1 + key * D + 8 * c) : z;
+      ky[g] = key < len ? *reinterpret_cast<const u32x4*>(K2 + key * D + 8 * c) : z;
+    }
+    u32x4 vv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t key = kb + 4 * i + f;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      vv[i] = key < len ? *reinterpret_cast<const u32x4*>(V + key * DV + 8 * e) : z;
+    }
+    float s1[8], s2[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      float d1 = 0.f, d2 = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        d1 = fmaf(qa[2 * t], __uint_as_float(kx[g][t] << 16), d1);
+        d1 = fmaf(qa[2 * t + 1], __uint_as_float(kx[g][t] & 0xffff0000u), d1);
+        d2 = fmaf(qb[2 * t], __uint_as_float(ky[g][t] << 16), d2);
+        d2 = fmaf(qb[2 * t + 1], __uint_as_float(ky[g][t] & 0xffff0000u), d2);
+      }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        d1 += __shfl_xor(d1, o);
+        d2 += __shfl_xor(d2, o);
+      }
+      const bool ok = kb + 8 * g + r < len;
+      s1[g] = ok ? d1 * cs : -INFINITY;
+      s2[g] = ok ? d2 * cs : -INFINITY;
+    }
+    float mx1 = s1[0], mx2 = s2[0];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) {
+      mx1 = fmaxf(mx1, s1[g]);
+      mx2 = fmaxf(mx2, s2[g]);
+    }
+#pragma unroll
+    for (int o = 8; o < 64; o <<= 1) {
+      mx1 = fmaxf(mx1, __shfl_xor(mx1, o));
+      mx2 = fmaxf(mx2, __shfl_xor(mx2, o));
+    }
+    const float mn1 = fmaxf(m1, mx1), mn2 = fmaxf(m2, mx2);
+    const float al1 = fast_exp2(m1 - mn1), al2 = fast_exp2(m2 - mn2);
+    float p1[8], p2[8], sum1 = 0.f, sum2 = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      p1[g] = fast_exp2(s1[g] - mn1);
+      p2[g] = fast_exp2(s2[g] - mn2);
+      sum1 += p1[g];
+      sum2 += p2[g];
+    }
+#pragma unroll
+    for (int o = 8; o < 64; o <<= 1) {
+      sum1 += __shfl_xor(sum1, o);
+      sum2 += __shfl_xor(sum2, o);
+    }
+    l1 = fmaf(l1, al1, sum1);
+    l2 = fmaf(l2, al2, sum2);
+    m1 = mn1;
+    m2 = mn2;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc1[t] *= al1;
+      acc2[t] *= al2;
+    }
+    // ---- values: key 4 i + f, whose weight sits in register i/2 of lanes 8 * (key % 8)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int src = 32 * (i & 1) + 8 * f;
+      const float w1 = __shfl(p1[i >> 1], src);
+      const float w2 = __shfl(p2[i >> 1], src);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float lo = __uint_as_float(vv[i][t] << 16);
+        const float hi = __uint_as_float(vv[i][t] & 0xffff0000u);
+        acc1[2 * t] = fmaf(w1, lo, acc1[2 * t]);
+        acc1[2 * t + 1] = fmaf(w1, hi, acc1[2 * t + 1]);
+        acc2[2 * t] = fmaf(w2, lo, acc2[2 * t]);
+        acc2[2 * t + 1] = fmaf(w2, hi, acc2[2 * t + 1]);
+      }
+    }
+  }
+  // Sum the four key phases (lanes e, e+16, e+32, e+48 hold the same channels).
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    acc1[t] += __shfl_xor(acc1[t], 16);
+    acc1[t] += __shfl_xor(acc1[t], 32);
+    acc2[t] += __shfl_xor(acc2[t], 16);
+    acc2[t] += __shfl_xor(acc2[t], 32);
+  }
+  if (lane == 0) {
+    red[wv][0][0] = m1;
+    red[wv][0][1] = l1;
+    red[wv][1][0] = m2;
+    red[wv][1][1] = l2;
+  }
+  if (f == 0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      red[wv][0][2 + 8 * e + t] = acc1[t];
+      red[wv][1][2 + 8 * e + t] = acc2[t];
+    }
+  }
+  __syncthreads();
+  // Merge the 4 wavefront states: thread = (map, channel). Waves with no valid key have
+  // m = -inf and weight 0; wave 0 always has a valid key.
+  float* out = partial + (bh * n_split + split) * 2 * PART;
+  if (tid < 2 * DV) {
+    const int mp = tid / DV, ch = tid % DV;
+    float M = red[0][mp][0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, red[w][mp][0]);
+    float A = 0.f, S = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = fast_exp2(red[w][mp][0] - M);
+      A = fmaf(red[w][mp][2 + ch], sc, A);
+      S = fmaf(red[w][mp][1], sc, S);
+    }
+    out[mp * PART + 2 + ch] = A;
+    if (ch == 0) {
+      out[mp * PART + 0] = M;
+      out[mp * PART + 1] = S;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(DV) decode_combine_kernel(
+    const float* __restrict__ partial, const int32_t* __restrict__ cache_len,
+    const diffattn_lambda_state* __restrict__ lamst, const float* __restrict__ rms_w,
+    bf16_t* __restrict__ out, int64_t H, int64_t L, int n_split, int64_t split_len,
+    float eps) {
+  __shared__ float wsum[2];
+  const int ch = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / H;
+  int64_t len = cache_len ? static_cast<int64_t>(cache_len[b]) : L;
+  len = len < 1 ? 1 : (len > L ? L : len);
+  const int nv = static_cast<int>((len + split_len - 1) / split_len);
+  const float* P = partial + bh * n_split * 2 * PART;
+  float o[2];
+#pragma unroll
+  for (int mp = 0; mp < 2; ++mp) {
+    float M = -INFINITY;
+    for (int s = 0; s < nv; ++s) M = fmaxf(M, P[s * 2 * PART + mp * PART]);
+    float A = 0.f, S = 0.f;
+    for (int s = 0; s < nv; ++s) {
+      const float* ps = P + s * 2 * PART + mp * PART;
+      const float sc = fast_exp2(ps[0] - M);
+      S = fmaf(ps[1], sc, S);
+      A = fmaf(ps[2 + ch], sc, A);
+    }
+    o[mp] = A / S;
+  }
+  const float lam = lamst->lambda_f;
+  const float y = o[0] - lam * o[1];
+  float ss = wave_sum(y * y);
+  if ((ch & 63) == 0) wsum[ch >> 6] = ss;
+  __syncthreads();
+  ss = wsum[0] + wsum[1];
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
+  const float w = rms_w ? rms_w[(bh % H) * DV + ch] : 1.0f;
+  out[bh * DV + ch] = f32_to_bf16(lamst->one_minus_init_f * (w * (y * rstd)));
+}
+
+}  // namespace dec
+
+void decode_split_geometry(int64_t B, int64_t H, int64_t L, int* n_split, int* split_len) {
+  // Rounds of 64 keys per wavefront: as many as keep >= 4096 workgroups in flight.
+  const int64_t BH = B * H;
+  int rounds = 8;
+  while (rounds > 1) {
+    const int64_t sl = static_cast<int64_t>(dec::KEYS_PER_ROUND) * 4 * rounds;
+    if (BH * ((L + sl - 1) / sl) >= 4096) break;
+    rounds >>= 1;
+  }
+  const int64_t sl = static_cast<int64_t>(dec::KEYS_PER_ROUND) * 4 * rounds;
+  *split_len = static_cast<int>(sl);
+  *n_split = static_cast<int>((L + sl - 1) / sl);
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
+  using namespace dec;
+  const int rounds = a.split_len / (KEYS_PER_ROUND * 4);
+  const int64_t BH = a.B * a.H;
+  hipLaunchKernelGGL(decode_split_kernel, dim3(a.n_split, static_cast<unsigned>(BH)), dim3(NT),
+                     0, s, static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
+                     static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
+                     static_cast<const bf16_t*>(a.v), a.cache_len, a.partial, a.H, a.L,
+                     a.n_split, rounds);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(BH)), dim3(DV), 0, s,
+                     a.partial, a.cache_len, a.lam, a.rms_weight, static_cast<bf16_t*>(a.out),
+                     a.H, a.L, a.n_split, static_cast<int64_t>(a.split_len), a.eps);
+  return hipGetLastError();
+}
+
+}  // namespace diffattn

@@ -1,0 +1,65 @@
+// Host-side launchers implemented in the .hip files; called only by api.cpp after the
+// arguments have been validated. Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "diffattn.h"
+
+namespace diffattn {
+
+// All tensors contiguous [B, H, N, feature]; shapes already validated.
+struct FwdArgs {
+  const void *q1, *q2, *k1, *k2, *v;
+  const diffattn_lambda_state* lam;
+  const float* rms_weight;   // [H, 2d] or nullptr
+  void* out;
+  diffattn_saved saved;      // all-null fields = inference
+  bool training;
+  int64_t B, H, N;
+  int d;
+  float eps;
+};
+
+struct DecodeArgs {
+  const void *q1, *q2, *k1, *k2, *v;
+  const int32_t* cache_len;
+  const diffattn_lambda_state* lam;
+  const float* rms_weight;
+  void* out;
+  float* partial;            // workspace
+  int64_t B, H, L;
+  int n_split, split_len;
+  int d;
+  float eps;
+};
+
+struct BwdArgs {
+  const void *q1, *q2, *k1, *k2, *v, *dout;
+  const float *lq1, *lk1, *lq2, *lk2;
+  const diffattn_lambda_state* lam;
+  const float* rms_weight;
+  diffattn_saved saved;
+  void *dq1, *dq2, *dk1, *dk2, *dv;
+  float* d_attn;
+  float *dlq1, *dlk1, *dlq2, *dlk2;
+  float* ws;                 // workspace (float32)
+  int64_t B, H, N;
+  int d;
+};
+
+hipError_t launch_lambda(int dim, int layer, const float* lq1, const float* lk1,
+                         const float* lq2, const float* lk2, diffattn_lambda_state* out,
+                         hipStream_t s);
+hipError_t launch_fwd_fp32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+
+// Decode split geometry shared by the workspace query and the launcher.
+void decode_split_geometry(int64_t B, int64_t H, int64_t L, int* n_split, int* split_len);
+// Backward workspace floats.
+size_t bwd_workspace_floats(int64_t B, int64_t H, int64_t N, int d);
+
+}  // namespace diffattn

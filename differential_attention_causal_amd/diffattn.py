@@ -1,0 +1,239 @@
+"""ctypes binding of libdiffattn (argument marshalling only).
+
+Every function here checks tensor placement and shapes, fills the C structs and
+calls the C-ABI of ``include/diffattn.h`` on torch's current stream.  All
+arithmetic happens in the library's HIP kernels; there is no fallback of any
+kind: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import struct
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdiffattn.so")
+
+OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4
+FP32, BF16 = 0, 1
+OP_FWD, OP_DECODE, OP_BWD = 0, 1, 2
+
+# Every symbol declared in include/diffattn.h.
+EXPORTS = ("diffattn_lambda", "diffattn_fwd", "diffattn_decode", "diffattn_bwd",
+           "diffattn_workspace_bytes", "diffattn_status_string", "diffattn_last_hip_error")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("head_dim", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+class Saved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("lse1", "lse2", "o1", "o2", "rstd")]
+
+
+LAMBDA_STATE_BYTES = 48  # 4 doubles + 4 floats
+_STATE_FMT = "<4d4f"
+
+
+class DiffAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip: int = 0):
+        self.status = status
+        msg = _lib().diffattn_status_string(status).decode()
+        if status == E_HIP:
+            msg += f" (hipError_t {hip})"
+        super().__init__(f"{fn}: {msg}")
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libdiffattn.so not built at {LIB_PATH}; run "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        lib.diffattn_status_string.restype = ctypes.c_char_p
+        lib.diffattn_status_string.argtypes = [ctypes.c_int]
+        lib.diffattn_last_hip_error.restype = ctypes.c_int
+        lib.diffattn_last_hip_error.argtypes = []
+        lib.diffattn_workspace_bytes.restype = ctypes.c_size_t
+        lib.diffattn_workspace_bytes.argtypes = [ctypes.c_int, ctypes.POINTER(Problem)]
+        lib.diffattn_lambda.restype = ctypes.c_int
+        lib.diffattn_lambda.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P]
+        lib.diffattn_fwd.restype = ctypes.c_int
+        lib.diffattn_fwd.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P,
+                                     ctypes.POINTER(Saved), P, ctypes.c_size_t, P]
+        lib.diffattn_decode.restype = ctypes.c_int
+        lib.diffattn_decode.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
+                                        ctypes.c_size_t, P]
+        lib.diffattn_bwd.restype = ctypes.c_int
+        lib.diffattn_bwd.argtypes = ([ctypes.POINTER(Problem)] + [P] * 11 +
+                                     [ctypes.POINTER(Saved)] + [P] * 12 +
+                                     [ctypes.c_size_t, P])
+        _LIB = lib
+    return _LIB
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it was not built)."""
+    return _lib()
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise DiffAttnError(fn, status, _lib().diffattn_last_hip_error() if status == E_HIP else 0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FP32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("libdiffattn tensors must live in GPU memory")
+            if not t.is_contiguous():
+                raise ValueError("libdiffattn tensors must be contiguous")
+
+
+def problem(batch, heads, seqlen, head_dim, dtype_code, eps=1e-5) -> Problem:
+    return Problem(int(batch), int(heads), int(seqlen), int(head_dim), 1, float(eps),
+                   int(dtype_code))
+
+
+def workspace_bytes(op: int, p: Problem) -> int:
+    return int(_lib().diffattn_workspace_bytes(op, ctypes.byref(p)))
+
+
+# ------------------------------------------------------------------ lambda
+def lambda_(lq1, lk1, lq2, lk2, layer: int) -> torch.Tensor:
+    """Device lambda state (48 bytes, uint8 tensor) for one layer."""
+    _need_cuda(lq1, lk1, lq2, lk2)
+    for t in (lq1, lk1, lq2, lk2):
+        if t.dtype != torch.float32 or t.dim() != 1 or t.numel() != lq1.numel():
+            raise ValueError("lambda vectors must be float32 [d] of equal length")
+    st = torch.empty(LAMBDA_STATE_BYTES, dtype=torch.uint8, device=lq1.device)
+    _check("diffattn_lambda", _lib().diffattn_lambda(
+        lq1.numel(), int(layer), _ptr(lq1), _ptr(lk1), _ptr(lq2), _ptr(lk2), _ptr(st),
+        _stream(lq1.device)))
+    return st
+
+
+def lambda_state_tensor(lam: float, lam_init: float, device, exp_a=1.0, exp_b=1.0) -> torch.Tensor:
+    """A hand-made device lambda state (for example lambda = 0)."""
+    import numpy as np
+    raw = struct.pack(_STATE_FMT, lam, lam_init, exp_a, exp_b, float(np.float32(lam)),
+                      float(np.float32(lam_init)), float(np.float32(1.0 - lam_init)), 0.0)
+    return torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(device)
+
+
+def read_lambda_state(st: torch.Tensor) -> Dict[str, float]:
+    raw = bytes(st.cpu().numpy().tobytes())
+    v = struct.unpack(_STATE_FMT, raw)
+    return {"lambda": v[0], "lambda_init": v[1], "exp_a": v[2], "exp_b": v[3],
+            "lambda_f32": v[4], "lambda_init_f32": v[5], "one_minus_init_f32": v[6]}
+
+
+# ------------------------------------------------------------------ forward
+def alloc_saved(B, H, N, d, device) -> Dict[str, torch.Tensor]:
+    f = dict(dtype=torch.float32, device=device)
+    return {"lse1": torch.empty(B, H, N, **f), "lse2": torch.empty(B, H, N, **f),
+            "o1": torch.empty(B, H, N, 2 * d, **f), "o2": torch.empty(B, H, N, 2 * d, **f),
+            "rstd": torch.empty(B, H, N, **f)}
+
+
+def _saved_struct(sv: Optional[Dict[str, torch.Tensor]]):
+    if sv is None:
+        return None
+    return Saved(*(sv[k].data_ptr() for k in ("lse1", "lse2", "o1", "o2", "rstd")))
+
+
+def forward(q1, q2, k1, k2, v, lam_state, rms_weight=None, eps: float = 1e-5,
+            out: Optional[torch.Tensor] = None, saved: Optional[Dict[str, torch.Tensor]] = None):
+    """Causal DiffAttn forward. Q/K [B,H,N,d], V [B,H,N,2d] (float32 or bfloat16).
+
+    Returns Y [B,H,N,2d].  ``saved`` (from ``alloc_saved``) requests the training
+    saves.
+    """
+    _need_cuda(q1, q2, k1, k2, v, lam_state, rms_weight, out)
+    B, H, N, d = q1.shape
+    for t in (q2, k1, k2):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q1.dtype:
+            raise ValueError("Q1, Q2, K1, K2 must share shape and dtype")
+    if tuple(v.shape) != (B, H, N, 2 * d) or v.dtype != q1.dtype:
+        raise ValueError("V must be [B, H, N, 2d] of the same dtype")
+    if out is None:
+        out = torch.empty_like(v)
+    p = problem(B, H, N, d, _dtype_code(q1), eps)
+    svs = _saved_struct(saved)
+    _check("diffattn_fwd", _lib().diffattn_fwd(
+        ctypes.byref(p), _ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), _ptr(lam_state),
+        _ptr(rms_weight), _ptr(out), ctypes.byref(svs) if svs is not None else None, None, 0,
+        _stream(q1.device)))
+    return out
+
+
+# ------------------------------------------------------------------ decode
+def decode(q1, q2, k1c, k2c, vc, lam_state, cache_len=None, rms_weight=None, eps: float = 1e-5,
+           out=None, workspace=None):
+    """One decode step: q [B,H,d], caches [B,H,L,d] / [B,H,L,2d], cache_len int32 [B]."""
+    _need_cuda(q1, q2, k1c, k2c, vc, lam_state, cache_len, rms_weight, out, workspace)
+    B, H, L, d = k1c.shape
+    p = problem(B, H, L, d, _dtype_code(k1c), eps)
+    if out is None:
+        out = torch.empty(B, H, 2 * d, dtype=vc.dtype, device=vc.device)
+    need = workspace_bytes(OP_DECODE, p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=vc.device)
+    _check("diffattn_decode", _lib().diffattn_decode(
+        ctypes.byref(p), _ptr(q1), _ptr(q2), _ptr(k1c), _ptr(k2c), _ptr(vc), _ptr(cache_len),
+        _ptr(lam_state), _ptr(rms_weight), _ptr(out), _ptr(workspace), workspace.numel(),
+        _stream(vc.device)))
+    return out
+
+
+# ------------------------------------------------------------------ backward
+def backward(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, lam_state, saved, dout, rms_weight=None,
+             eps: float = 1e-5, workspace=None):
+    """Gradients of sum(Y * dout); returns a dict of device tensors."""
+    _need_cuda(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, lam_state, dout, rms_weight, workspace)
+    B, H, N, d = q1.shape
+    p = problem(B, H, N, d, _dtype_code(q1), eps)
+    g = {"dq1": torch.empty_like(q1), "dq2": torch.empty_like(q2), "dk1": torch.empty_like(k1),
+         "dk2": torch.empty_like(k2), "dv": torch.empty_like(v),
+         "d_attn": torch.empty(B, H, N, 2 * d, dtype=torch.float32, device=q1.device)}
+    for k in ("dlq1", "dlk1", "dlq2", "dlk2"):
+        g[k] = torch.empty(d, dtype=torch.float32, device=q1.device)
+    need = workspace_bytes(OP_BWD, p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    svs = _saved_struct(saved)
+    _check("diffattn_bwd", _lib().diffattn_bwd(
+        ctypes.byref(p), _ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), _ptr(lq1), _ptr(lk1),
+        _ptr(lq2), _ptr(lk2), _ptr(lam_state), _ptr(rms_weight),
+        ctypes.byref(svs) if svs is not None else None, _ptr(dout),
+        _ptr(g["dq1"]), _ptr(g["dq2"]), _ptr(g["dk1"]), _ptr(g["dk2"]), _ptr(g["dv"]),
+        _ptr(g["d_attn"]), _ptr(g["dlq1"]), _ptr(g["dlk1"]), _ptr(g["dlq2"]), _ptr(g["dlk2"]),
+        _ptr(workspace), workspace.numel(), _stream(q1.device)))
+    return g

@@ -1,0 +1,194 @@
+/*
+ * libdiffattn - causal differential attention (DiffAttn) for AMD MI355X (gfx950).
+ *
+ * What the library computes (per batch element b and head h):
+ *
+ *   S1 = Q1 K1^T / sqrt(d),  S2 = Q2 K2^T / sqrt(d)              (d = width of Q1, K1)
+ *   A_k = softmax over keys j <= i of row i of S_k                (causal mask M)
+ *   O   = (A1 - lambda * A2) V                                    (V and O are 2d wide)
+ *   Y   = (1 - lambda_init) * w * O * (mean(O^2) + eps)^(-1/2)    (per-head RMSNorm)
+ *   lambda      = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init
+ *   lambda_init = 0.8 - 0.6 * exp(-0.3 * (l - 1))                 (l = layer index >= 1)
+ *
+ * Sources:
+ *   DiffAttn equation, lambda and lambda_init: "Differential Transformer: Transformer que
+ *     cancela ruido de atencao" (pt.news.hada.io), section "Como a atencao diferencial
+ *     funciona"; the same DiffAttn and lambda formulas in "Differential Transformer:
+ *     Canceling Context Noise with Differential Attention" (priorstack.com, Attention
+ *     Mechanism tag page), section "Cancelling Context Noise Through Attention Map
+ *     Subtraction".
+ *   Causal mask M (0 where key j <= query i, -inf otherwise, giving probability 0):
+ *     "A Simple Principle From Noise-Cancelling Headphones Supercharges Transformers Like
+ *     Never Before" (intoai.pub), section "A Deeper Dive Into Attention Calculations".
+ *   lambda shared by all heads of a layer; per-head RMSNorm followed by the factor
+ *     (1 - lambda_init): same intoai.pub page, section "Differential Attention With
+ *     Multiple Heads"; pt.news.hada.io, section "Estrutura multi-head e arquitetura
+ *     completa".
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers unless stated otherwise. Layout is contiguous
+ *     row-major [B, H, N, feature] (feature = d for Q1/Q2/K1/K2, 2d for V and outputs).
+ *   - The caller owns every buffer, including the workspace whose size is given by
+ *     diffattn_workspace_bytes. The library keeps no state between calls and allocates
+ *     no device memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *   - A call returns a status and never aborts. Argument checks run on the host before
+ *     any HIP call, so they also work on a machine without a GPU. A failed launch returns
+ *     DIFFATTN_E_HIP and diffattn_last_hip_error() gives the hipError_t value.
+ *   - Outputs must not overlap inputs (DIFFATTN_E_ARG).
+ *   - A problem with batch, heads or seqlen equal to 0 is valid and does nothing.
+ *   - Supported: DIFFATTN_FP32 forward with d in {16, 32, 64}; DIFFATTN_BF16 forward,
+ *     decode and backward with d = 64. Accumulation is float32 everywhere. Other
+ *     combinations return DIFFATTN_E_UNSUPPORTED.
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DIFFATTN_OK = 0,
+  DIFFATTN_E_ARG = 1,          /* null/misaligned pointer, bad size, overlap, bad layer */
+  DIFFATTN_E_UNSUPPORTED = 2,  /* dtype / head_dim / mode combination not implemented */
+  DIFFATTN_E_WORKSPACE = 3,    /* workspace NULL or smaller than diffattn_workspace_bytes */
+  DIFFATTN_E_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} diffattn_status;
+
+typedef enum { DIFFATTN_FP32 = 0, DIFFATTN_BF16 = 1 } diffattn_dtype;
+
+typedef enum { DIFFATTN_OP_FWD = 0, DIFFATTN_OP_DECODE = 1, DIFFATTN_OP_BWD = 2 } diffattn_op;
+
+typedef struct {
+  int64_t batch;      /* B >= 0 */
+  int64_t heads;      /* H >= 0 */
+  int64_t seqlen;     /* N >= 0 (forward/backward) or cache capacity L (decode) */
+  int32_t head_dim;   /* d: width of Q1, Q2, K1, K2; V and outputs are 2d wide */
+  int32_t causal;     /* must be 1 */
+  float rms_eps;      /* eps of the per-head RMSNorm, >= 0, added inside the square root */
+  diffattn_dtype dtype; /* element type of Q/K/V, outputs and gradients */
+} diffattn_problem;
+
+/* The per-layer lambda scalar, as written by diffattn_lambda into device memory and read
+ * by every kernel. Kernels consume only the float fields. A caller may also write this
+ * struct itself (for example lambda = 0 to get plain causal softmax attention). */
+typedef struct {
+  double lambda;            /* exp(a) - exp(b) + lambda_init, in float64 */
+  double lambda_init;       /* 0.8 - 0.6 * exp(-0.3 * (l - 1)), in float64 */
+  double exp_a;             /* exp(lq1 . lk1) */
+  double exp_b;             /* exp(lq2 . lk2) */
+  float lambda_f;           /* lambda rounded once to float32 (nearest even) */
+  float lambda_init_f;      /* lambda_init rounded once to float32 */
+  float one_minus_init_f;   /* (1 - lambda_init) in float64, rounded once to float32 */
+  float pad;
+} diffattn_lambda_state;
+
+/* Quantities the forward saves for the backward (training mode). All float32, device
+ * memory owned by the caller. lse_k[i] = log(sum over j <= i of exp(S_k[i, j])) in natural
+ * log units; o1 = A1 V and o2 = A2 V (before the lambda combine); rstd = the RMSNorm
+ * factor (mean(O^2) + eps)^(-1/2) of each row. */
+typedef struct {
+  float* lse1;  /* [B, H, N] */
+  float* lse2;  /* [B, H, N] */
+  float* o1;    /* [B, H, N, 2d] */
+  float* o2;    /* [B, H, N, 2d] */
+  float* rstd;  /* [B, H, N] */
+} diffattn_saved;
+
+/* lambda and lambda_init for one layer, computed on the device in float64 (dot products
+ * summed in index order) and rounded once to float32.
+ * Source: pt.news.hada.io, "Como a atencao diferencial funciona", lambda and lambda_init
+ * equations; one scalar per layer shared by all heads (intoai.pub, "Differential Attention
+ * With Multiple Heads").
+ *   dim        length of each lambda vector (the head width d), 1 <= dim <= 1024
+ *   layer_idx  l >= 1
+ *   lq1..lk2   device float32 vectors [dim]
+ *   state_out  device pointer to one diffattn_lambda_state (8-byte aligned)
+ * Errors: E_ARG for a NULL pointer, dim out of range or layer_idx < 1. */
+diffattn_status diffattn_lambda(int32_t dim, int32_t layer_idx, const float* lq1,
+                                const float* lk1, const float* lq2, const float* lk2,
+                                diffattn_lambda_state* state_out, void* stream);
+
+/* Causal DiffAttn forward with the per-head RMSNorm and (1 - lambda_init) scale fused in.
+ * Source: the DiffAttn equation (pt.news.hada.io "Como a atencao diferencial funciona";
+ * priorstack.com "Cancelling Context Noise Through Attention Map Subtraction"), causal
+ * mask (intoai.pub "A Deeper Dive Into Attention Calculations"), RMSNorm and scale
+ * (intoai.pub "Differential Attention With Multiple Heads").
+ *   q1, q2, k1, k2  [B, H, N, d] of p->dtype;  v [B, H, N, 2d] of p->dtype
+ *   lam             device diffattn_lambda_state (from diffattn_lambda)
+ *   rms_weight      device float32 [H, 2d] per-channel RMSNorm weight, or NULL for ones
+ *   out             [B, H, N, 2d] of p->dtype (output Y)
+ *   saved           host pointer to a struct of device pointers, or NULL (inference).
+ *                   Non-NULL: every field must be a valid device buffer (bf16 only).
+ *   workspace       may be NULL when diffattn_workspace_bytes(OP_FWD) is 0
+ * Pointers must be 16-byte aligned. */
+diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const void* q2,
+                             const void* k1, const void* k2, const void* v,
+                             const diffattn_lambda_state* lam, const float* rms_weight,
+                             void* out, const diffattn_saved* saved, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* One autoregressive decode step: a single new query per (b, h) against its K1/K2/V cache.
+ * The cache already holds the new token, so the query sits at position len - 1 and sees
+ * cached keys 0 .. len - 1 (the last row of the causal mask). Keys are processed in
+ * splits whose partial softmax states are merged exactly (log-sum-exp merge).
+ * Source: autoregressive generation (intoai.pub, "Let's First Learn About The
+ * Decoder-Only Transformer") over the DiffAttn equation above; the whole cache is read
+ * from HBM every step (priorstack.com, "Multi-Head Latent Attention: Scaling LLM Serving
+ * Throughput via Low-Rank KV Compression", section "The Memory Wall: Why the KV Cache
+ * Constrains LLM Serving").
+ *   q1, q2      [B, H, d]
+ *   k1c, k2c    [B, H, L, d] (p->seqlen = L);  vc [B, H, L, 2d]
+ *   cache_len   device int32 [B] or NULL (= L for every sequence). Values are clamped to
+ *               [1, L] on the device.
+ *   out         [B, H, 2d]
+ *   workspace   device buffer of at least diffattn_workspace_bytes(OP_DECODE, p) bytes
+ * bf16 only, d = 64, 16-byte aligned pointers. */
+diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const void* q2,
+                                const void* k1c, const void* k2c, const void* vc,
+                                const int32_t* cache_len, const diffattn_lambda_state* lam,
+                                const float* rms_weight, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Backward of the forward above for the loss sum(Y * dout), recomputing A1 and A2 from
+ * the saved log-sum-exps. The pages print no gradient formulas; these follow from the
+ * forward by the chain rule:
+ *   G   = dL/dO = r g - O r^3 rowsum(g O) / 2d,  g = (1 - lambda_init) w dout, r = rstd
+ *   dV  = (A1 - lambda A2)^T G;   dS1 = A1 (G V^T - D1);   dS2 = -lambda A2 (G V^T - D2)
+ *   D_k = rowsum(G * O_k);  dQ_k = dS_k K_k / sqrt(d);  dK_k = dS_k^T Q_k / sqrt(d)
+ *   dlambda = -sum over (b, h, i) of D2;  dlq1 = dlambda e^a lk1;  dlk1 = dlambda e^a lq1;
+ *   dlq2 = -dlambda e^b lk2;  dlk2 = -dlambda e^b lq2   (lambda_init gets no gradient)
+ *   inputs  q1..v, lq1..lk2 (device float32 [d]), lam, rms_weight (or NULL), saved (from
+ *           diffattn_fwd in training mode on the same inputs), dout [B, H, N, 2d]
+ *   outputs dq1, dq2, dk1, dk2 [B, H, N, d]; dv [B, H, N, 2d] (all p->dtype);
+ *           d_attn [B, H, N, 2d] float32 = G, the gradient at the RMSNorm input;
+ *           dlq1, dlk1, dlq2, dlk2 device float32 [d]
+ *   workspace at least diffattn_workspace_bytes(OP_BWD, p) bytes
+ * bf16 only, d = 64, 16-byte aligned pointers. */
+diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const void* q2,
+                             const void* k1, const void* k2, const void* v, const float* lq1,
+                             const float* lk1, const float* lq2, const float* lk2,
+                             const diffattn_lambda_state* lam, const float* rms_weight,
+                             const diffattn_saved* saved, const void* dout, void* dq1,
+                             void* dq2, void* dk1, void* dk2, void* dv, float* d_attn,
+                             float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes an operation needs for problem p (0 if none; also 0 for an invalid p). */
+size_t diffattn_workspace_bytes(diffattn_op op, const diffattn_problem* p);
+
+/* Static human-readable name of a status code. */
+const char* diffattn_status_string(diffattn_status s);
+
+/* hipError_t of the last DIFFATTN_E_HIP returned on the calling thread (0 if none). */
+int diffattn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

@@ -1,0 +1,174 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol,
+and rejects invalid arguments with a status code before any HIP call.
+
+Every call here is invalid on purpose, so no kernel is ever launched; the fake
+device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from differential_attention_causal_amd import diffattn as da
+
+# Host logic only. The calls below carry fake device addresses and are all invalid, so
+# none may reach a kernel; on a machine with a GPU the module is skipped rather than
+# trusting that with real hardware attached.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="host-only argument checks with fake addresses")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "diffattn.h")
+
+A = 1 << 20  # fake 16-byte aligned addresses, spaced far apart
+def addr(i):
+    return ctypes.c_void_p(A * (i + 1))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(diffattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(da.EXPORTS)
+    lib = da.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = da.lib()
+    for s in range(5):
+        assert lib.diffattn_status_string(s).decode().startswith("DIFFATTN_")
+    assert lib.diffattn_last_hip_error() == 0
+
+
+def fwd(p, ptrs=None, saved=None):
+    ptrs = ptrs or [addr(i) for i in range(8)]
+    return da.lib().diffattn_fwd(ctypes.byref(p), *ptrs, saved, None, 0, None)
+
+
+def test_forward_argument_checks():
+    bf = lambda **kw: da.problem(**{**dict(batch=1, heads=2, seqlen=64, head_dim=64,
+                                           dtype_code=da.BF16), **kw})
+    lib = da.lib()
+    assert lib.diffattn_fwd(None, *[addr(i) for i in range(8)], None, None, 0, None) == da.E_ARG
+    assert fwd(bf(batch=-1)) == da.E_ARG
+    assert fwd(bf(seqlen=-5)) == da.E_ARG
+    assert fwd(bf(head_dim=0)) == da.E_ARG
+    assert fwd(bf(head_dim=128)) == da.E_UNSUPPORTED
+    assert fwd(bf(head_dim=16)) == da.E_UNSUPPORTED
+    assert fwd(da.problem(1, 2, 64, 48, da.FP32)) == da.E_UNSUPPORTED
+    p = bf(); p.causal = 0
+    assert fwd(p) == da.E_UNSUPPORTED
+    p = bf(); p.rms_eps = -1.0
+    assert fwd(p) == da.E_ARG
+    p = bf(); p.rms_eps = float("nan")
+    assert fwd(p) == da.E_ARG
+    p = bf(); p.dtype = 7
+    assert fwd(p) == da.E_ARG
+    # null tensor pointers
+    for i in range(7):
+        ptrs = [addr(j) for j in range(8)]
+        if i == 6:
+            i = 7  # out (index 6 is the optional RMSNorm weight)
+        ptrs[i] = None
+        assert fwd(bf(), ptrs) == da.E_ARG
+    # misaligned pointer
+    ptrs = [addr(j) for j in range(8)]
+    ptrs[2] = ctypes.c_void_p(A * 3 + 2)
+    assert fwd(bf(), ptrs) == da.E_ARG
+    # output overlapping an input
+    ptrs = [addr(j) for j in range(8)]
+    ptrs[7] = ctypes.c_void_p(A * 1 + 64)
+    assert fwd(bf(), ptrs) == da.E_ARG
+    # saved buffers with a null field
+    sv = da.Saved(A * 20, A * 21, A * 22, None, A * 24)
+    assert fwd(bf(), saved=ctypes.byref(sv)) == da.E_ARG
+    # float32 with training saves is not implemented
+    sv = da.Saved(A * 20, A * 21, A * 22, A * 23, A * 24)
+    assert fwd(da.problem(1, 2, 64, 16, da.FP32), saved=ctypes.byref(sv)) == da.E_UNSUPPORTED
+    # overflow of the element count
+    assert fwd(bf(batch=1 << 40, heads=1 << 20)) == da.E_ARG
+
+
+def test_empty_problems_are_noops():
+    # nothing to compute: valid, no pointer needed, no HIP call
+    nul = [None] * 8
+    for kw in (dict(batch=0), dict(heads=0), dict(seqlen=0)):
+        p = da.problem(**{**dict(batch=2, heads=2, seqlen=16, head_dim=64,
+                                 dtype_code=da.BF16), **kw})
+        assert fwd(p, nul) == da.OK
+        assert da.workspace_bytes(da.OP_DECODE, p) == 0
+        assert da.lib().diffattn_decode(ctypes.byref(p), *[None] * 9, None, 0, None) == da.OK
+
+
+def test_lambda_argument_checks():
+    lib = da.lib()
+    ptr = [addr(i) for i in range(5)]
+    assert lib.diffattn_lambda(0, 1, *ptr, None) == da.E_ARG
+    assert lib.diffattn_lambda(2000, 1, *ptr, None) == da.E_ARG
+    assert lib.diffattn_lambda(64, 0, *ptr, None) == da.E_ARG
+    assert lib.diffattn_lambda(64, -3, *ptr, None) == da.E_ARG
+    assert lib.diffattn_lambda(64, 1, None, *ptr[1:], None) == da.E_ARG
+    assert lib.diffattn_lambda(64, 1, *ptr[:4], None, None) == da.E_ARG
+    assert lib.diffattn_lambda(64, 1, *ptr[:4], ctypes.c_void_p(A * 9 + 4), None) == da.E_ARG
+    # state overlapping a lambda vector
+    assert lib.diffattn_lambda(64, 1, *ptr[:4], ctypes.c_void_p(A + 8), None) == da.E_ARG
+
+
+def test_decode_argument_checks():
+    lib = da.lib()
+    p = da.problem(64, 16, 8192, 64, da.BF16)
+    need = da.workspace_bytes(da.OP_DECODE, p)
+    assert need > 0
+    ptrs = [addr(i * 64) for i in range(9)]   # q1 q2 k1 k2 v len lam w out
+    ws = addr(64 * 40)
+    call = lambda p, ptrs, ws, n: lib.diffattn_decode(ctypes.byref(p), *ptrs, ws, n, None)
+    assert call(p, ptrs, None, need) == da.E_WORKSPACE
+    assert call(p, ptrs, ws, need - 4) == da.E_WORKSPACE
+    assert call(da.problem(64, 16, 8192, 64, da.FP32), ptrs, ws, need) == da.E_UNSUPPORTED
+    assert call(da.problem(64, 16, 8192, 32, da.BF16), ptrs, ws, need) == da.E_UNSUPPORTED
+    bad = list(ptrs); bad[0] = None
+    assert call(p, bad, ws, need) == da.E_ARG
+    bad = list(ptrs); bad[8] = ptrs[2]      # out aliases the K1 cache
+    assert call(p, bad, ws, need) == da.E_ARG
+    bad = list(ptrs); bad[5] = ctypes.c_void_p(A * 5 * 64 + 2)   # misaligned cache_len
+    assert call(p, bad, ws, need) == da.E_ARG
+
+
+def test_backward_argument_checks():
+    lib = da.lib()
+    p = da.problem(2, 2, 128, 64, da.BF16)
+    need = da.workspace_bytes(da.OP_BWD, p)
+    assert need > 0
+    ptrs = [addr(i * 64) for i in range(27)]
+    sv = da.Saved(*(A * 64 * (40 + i) for i in range(5)))
+    def call(p, ptrs, saved, ws, n):
+        args = ptrs[:11] + [saved] + ptrs[11:22]
+        return lib.diffattn_bwd(ctypes.byref(p), *args, ws, n, None)
+    ws = addr(64 * 60)
+    assert call(p, ptrs, ctypes.byref(sv), None, need) == da.E_WORKSPACE
+    assert call(p, ptrs, ctypes.byref(sv), ws, need - 1) == da.E_WORKSPACE
+    assert call(p, ptrs, None, ws, need) == da.E_ARG
+    assert call(da.problem(2, 2, 128, 16, da.BF16), ptrs, ctypes.byref(sv), ws, need) == \
+        da.E_UNSUPPORTED
+    bad = list(ptrs); bad[12] = ptrs[0]     # dq1 aliases q1
+    assert call(p, bad, ctypes.byref(sv), ws, need) == da.E_ARG
+    bad = list(ptrs); bad[5] = None         # lq1
+    assert call(p, bad, ctypes.byref(sv), ws, need) == da.E_ARG
+
+
+def test_workspace_queries():
+    assert da.workspace_bytes(da.OP_FWD, da.problem(4, 8, 2048, 64, da.BF16)) == 0
+    p = da.problem(64, 16, 8192, 64, da.BF16)
+    # per (b, h, split): 2 maps x (m, l, 128 accumulators) float32
+    n = da.workspace_bytes(da.OP_DECODE, p)
+    assert n % (64 * 16 * 2 * 130 * 4) == 0
+    bad = da.problem(-1, 1, 1, 64, da.BF16)
+    assert da.workspace_bytes(da.OP_BWD, bad) == 0

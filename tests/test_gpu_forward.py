@@ -1,0 +1,213 @@
+"""GPU parity of lambda and the causal forward against the float64 oracle.
+
+Tolerances: lambda and the mask bit-exact; float32 outputs within 1e-5 normwise
+relative error per (b, h); bf16 outputs (after RMSNorm and the 1 - lambda_init
+scale) within 2e-2 max-abs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from differential_attention_causal_amd import diffattn as da
+from differential_attention_causal_amd import synth
+from oracle import diffattn_oracle as orc
+from tests.helpers import DEV, draw, lam_pair, normwise_rel, np64
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+FP32_TOL = 1e-5
+
+
+def ulp_diff(a: float, b: float) -> float:
+    return abs(a - b) / np.spacing(max(abs(a), abs(b)))
+
+
+@pytest.mark.parametrize("layer", [1, 2, 4, 6, 8, 12, 30])
+@pytest.mark.parametrize("d", [16, 64])
+def test_lambda_bitwise(layer, d):
+    w = synth.custom("fwd", 1, 1, 1, d, layer, "fp32", number=200 + d + layer)
+    x, h = draw(w)
+    st, ls = lam_pair(x, h, layer)
+    got = da.read_lambda_state(st)
+    for k in ("lambda_f32", "lambda_init_f32", "one_minus_init_f32"):
+        assert np.float32(got[k]).tobytes() == np.float32(ls[k]).tobytes(), k
+    for k in ("lambda", "lambda_init", "exp_a", "exp_b"):
+        assert ulp_diff(got[k], ls[k]) <= 1.0, (k, got[k], ls[k])
+    assert got["lambda_init"] == orc.lambda_init(layer) or \
+        ulp_diff(got["lambda_init"], orc.lambda_init(layer)) <= 1.0
+
+
+def test_lambda_zero_vectors():
+    z = torch.zeros(64, dtype=torch.float32, device=DEV)
+    for layer in (1, 5, 12):
+        got = da.read_lambda_state(da.lambda_(z, z, z, z, layer))
+        li = orc.lambda_init(layer)
+        assert np.float32(got["lambda_f32"]) == np.float32(li)
+        assert got["exp_a"] == 1.0 and got["exp_b"] == 1.0
+
+
+def _run_fwd(w, seed=None, weight=None):
+    x, h = draw(w, seed)
+    st, ls = lam_pair(x, h, w.layer)
+    y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, rms_weight=weight)
+    torch.cuda.synchronize()
+    return x, h, st, ls, y
+
+
+def test_fp32_tiny_workload():
+    w = synth.WORKLOADS[1]
+    x, h, st, ls, y = _run_fwd(w)
+    ref = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
+                      ls["lambda_init"])
+    err = normwise_rel(np64(y), ref, axes=(2, 3))
+    assert np.all(err <= FP32_TOL), err
+
+
+@pytest.mark.parametrize("d,n", [(16, 1), (16, 65), (32, 50), (64, 130)])
+def test_fp32_shapes(d, n):
+    w = synth.custom("fwd", 2, 3, n, d, 3, "fp32", number=300 + n + d)
+    x, h, st, ls, y = _run_fwd(w)
+    ref = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
+                      ls["lambda_init"])
+    assert np.all(normwise_rel(np64(y), ref, axes=(2, 3)) <= FP32_TOL)
+
+
+@pytest.mark.parametrize("b,hh,n", [(1, 1, 1), (1, 2, 31), (2, 1, 64), (1, 1, 127), (1, 3, 128),
+                                    (2, 2, 129), (1, 2, 200), (1, 1, 513), (1, 1, 1000)])
+def test_bf16_small_shapes(b, hh, n):
+    w = synth.custom("fwd", b, hh, n, 64, 4, "bf16", number=400 + n)
+    x, h, st, ls, y = _run_fwd(w)
+    ref = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
+                      ls["lambda_init"])
+    assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
+
+
+def test_bf16_rms_weight():
+    w = synth.custom("fwd", 1, 3, 300, 64, 2, "bf16", number=450)
+    g = torch.Generator(device=DEV).manual_seed(7)
+    weight = 1.0 + 0.25 * torch.randn(3, 128, generator=g, device=DEV)
+    x, h, st, ls, y = _run_fwd(w, weight=weight)
+    ref = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
+                      ls["lambda_init"], weight=np64(weight))
+    assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
+
+
+def test_bf16_prefill_workload():
+    """B4 H8 N2048 d64, layer 4: four heads in full, every head on sampled rows."""
+    w = synth.WORKLOADS[2]
+    x, h, st, ls, y = _run_fwd(w)
+    yh = np64(y)
+    heads = [(0, 0), (1, 3), (2, 5), (3, 7)]
+    ref = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
+                      ls["lambda_init"], heads=heads)
+    for b, hh in heads:
+        assert np.max(np.abs(yh[b, hh] - ref[b, hh])) <= BF16_TOL
+    rows = [0, 1, 127, 128, 129, 1023, 2047]
+    for b in range(w.batch):
+        for hh in range(w.heads):
+            r = orc.forward_rows(h["q1"][b, hh], h["q2"][b, hh], h["k1"][b, hh], h["k2"][b, hh],
+                                 h["v"][b, hh], rows, ls["lambda"], ls["lambda_init"])
+            assert np.max(np.abs(yh[b, hh, rows] - r)) <= BF16_TOL
+
+
+def test_bf16_long_context_sampled():
+    """B1 H16 N32768 d64, layer 12: sampled rows of every head (the launch that is timed)."""
+    w = synth.WORKLOADS[3]
+    x = synth.make_inputs(w, DEV)
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
+    torch.cuda.synchronize()
+    lv = {k: np64(x[k]) for k in ("lq1", "lk1", "lq2", "lk2")}
+    ls = orc.lambda_scalar(lv["lq1"], lv["lk1"], lv["lq2"], lv["lk2"], w.layer)
+    rng = np.random.default_rng(5)
+    base = [0, 1, 31, 32, 127, 128, 4095, 16384, 32766, 32767]
+    for hh in range(w.heads):
+        rows = sorted(set(base + rng.integers(0, w.seqlen, 6).tolist()))
+        sl = {k: np64(x[k][0, hh]) for k in ("q1", "q2", "k1", "k2", "v")}
+        r = orc.forward_rows(sl["q1"], sl["q2"], sl["k1"], sl["k2"], sl["v"], rows,
+                             ls["lambda"], ls["lambda_init"])
+        got = np64(y[0, hh, rows])
+        assert np.max(np.abs(got - r)) <= BF16_TOL, hh
+    # every row is finite
+    assert torch.isfinite(y.float()).all().item()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_mask_bitwise(dtype):
+    """Keys after row i0 changed: rows 0..i0 are bit-identical."""
+    d = 64 if dtype == "bf16" else 16
+    w = synth.custom("fwd", 1, 2, 333, d, 3, dtype, number=500)
+    x, h = draw(w)
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    y0 = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
+    i0 = 150
+    k1 = x["k1"].clone(); k2 = x["k2"].clone(); v = x["v"].clone()
+    k1[:, :, i0 + 1:] += 3.0
+    k2[:, :, i0 + 1:] *= -2.0
+    v[:, :, i0 + 1:] += 5.0
+    y1 = da.forward(x["q1"], x["q2"], k1, k2, v, st)
+    torch.cuda.synchronize()
+    assert torch.equal(y0[:, :, : i0 + 1], y1[:, :, : i0 + 1])
+    assert not torch.equal(y0[:, :, i0 + 1:], y1[:, :, i0 + 1:])
+
+
+def test_determinism_bitwise():
+    w = synth.custom("fwd", 2, 4, 777, 64, 5, "bf16", number=510)
+    x, h = draw(w)
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    ya = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
+    yb = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb)
+
+
+def test_special_cases_lambda_zero_and_identical_maps():
+    w = synth.custom("fwd", 1, 2, 260, 64, 1, "bf16", number=520)
+    x, h = draw(w)
+    # lambda = 0: plain causal softmax attention, then norm and scale
+    st0 = da.lambda_state_tensor(0.0, 0.3, DEV)
+    y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st0)
+    ref = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], 0.0, 0.3)
+    assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
+    # identical maps with lambda = 1: exactly zero
+    st1 = da.lambda_state_tensor(1.0, 0.2, DEV)
+    y1 = da.forward(x["q1"], x["q1"], x["k1"], x["k1"], x["v"], st1)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y1).item() == 0
+
+
+def test_training_saves():
+    w = synth.custom("train", 1, 2, 300, 64, 6, "bf16", number=530)
+    x, h = draw(w)
+    st, ls = lam_pair(x, h, w.layer)
+    sv = da.alloc_saved(1, 2, 300, 64, DEV)
+    y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, saved=sv)
+    y_inf = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_inf)
+    ref, rs = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
+                          ls["lambda_init"], want_saved=True)
+    assert np.max(np.abs(np64(sv["lse1"]) - rs["lse1"])) <= 2e-3
+    assert np.max(np.abs(np64(sv["lse2"]) - rs["lse2"])) <= 2e-3
+    assert np.max(np.abs(np64(sv["o1"]) - rs["o1"])) <= 2e-2
+    assert np.max(np.abs(np64(sv["o2"]) - rs["o2"])) <= 2e-2
+    assert np.max(np.abs(np64(sv["rstd"]) / rs["rstd"] - 1.0)) <= 2e-2
+
+
+def test_empty_sequence():
+    q = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty(1, 2, 0, 128, dtype=torch.bfloat16, device=DEV)
+    st = da.lambda_state_tensor(0.5, 0.2, DEV)
+    y = da.forward(q, q.clone(), q.clone(), q.clone(), v, st)
+    assert y.shape == (1, 2, 0, 128)
+
+
+def test_unsupported_head_dim_raises():
+    q = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device=DEV)
+    st = da.lambda_state_tensor(0.5, 0.2, DEV)
+    with pytest.raises(da.DiffAttnError):
+        da.forward(q, q.clone(), q.clone(), q.clone(), v, st)
