@@ -1,0 +1,261 @@
+"""Benchmark of libdiffattn on one MI355X; prints one JSON line.
+
+Headline (``value``): causal DiffAttn forward throughput in TFLOP/s on the
+long-context workload B1 H16 N32768 d64 (V 128 wide), bf16, layer 12.  One step
+is lambda + forward over that batch, with the inputs already resident in HBM.
+FLOPs are counted as 12 d P per head (P = N(N+1)/2 causal pairs: two QK^T of
+width d and two PV of width 2d), the work the exact blockwise algorithm executes.
+
+Also reported in the same line:
+  decode  - one split-KV decode step, 64 sequences x 16 heads against caches of
+            8192 tokens: HBM GB/s = (cache + query + output bytes) / step time.
+  train   - forward (with saves) + backward on B8 H12 N4096 when the backward
+            kernels are present: TFLOP/s under 12 d P + 20 d P per head.
+  roofline - for the dominant kernel (the forward), achieved TFLOP/s from HIP
+            events around each forward launch in the timed region, against the
+            bf16 dense MFMA peak of 2500 TFLOP/s.
+  cpu_baseline - the float64 oracle on the host cores, on a bounded sample of the
+            forward workload (the last rows of head 0, ~10-30 s of CPU work).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs fwd,decode,train]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DiffAttn fwd TFLOP/s + % bf16 MFMA peak; decode-step HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def causal_pairs(n: int) -> int:
+    return n * (n + 1) // 2
+
+
+def fwd_flops(w) -> float:
+    return 12.0 * w.head_dim * causal_pairs(w.seqlen) * w.batch * w.heads
+
+
+def decode_bytes(w) -> int:
+    bh = w.batch * w.heads
+    cache = bh * w.seqlen * (w.head_dim * 2 + 2 * w.head_dim) * 2   # K1, K2, V bf16
+    return cache + bh * 2 * w.head_dim * 2 + bh * 2 * w.head_dim * 2  # + q1, q2 + out
+
+
+def time_steps(step, steps: int, warmup: int, inner_events=None):
+    """Runs warmup + timed steps; returns (ms per step, list of inner kernel ms)."""
+    import torch
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    inner = []
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)] if inner_events else [None] * steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        step(pairs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ms = start.elapsed_time(stop) / steps
+    if inner_events:
+        inner = [a.elapsed_time(b) for a, b in pairs]
+    return ms, wall, inner
+
+
+def leg_forward(steps, warmup):
+    import torch
+    from differential_attention_causal_amd import diffattn as da
+    from differential_attention_causal_amd import synth
+    w = synth.WORKLOADS[3]
+    x = synth.make_inputs(w, "cuda:0")
+    out = torch.empty_like(x["v"])
+    torch.cuda.synchronize()
+
+    def step(ev):
+        st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+        if ev:
+            ev[0].record()
+        da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, out=out)
+        if ev:
+            ev[1].record()
+
+    ms, wall, inner = time_steps(step, steps, warmup, inner_events=True)
+    fl = fwd_flops(w)
+    kern_ms = sum(inner) / len(inner)
+    achieved = fl / (kern_ms * 1e-3) / 1e12
+    return w, {
+        "ms_per_step": ms, "wall_ms_per_step": wall, "tflops": fl / (ms * 1e-3) / 1e12,
+        "fwd_kernel_ms": kern_ms, "flops_per_launch": fl,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "formula_tflops_8dP": fl * 8.0 / 12.0 / (ms * 1e-3) / 1e12,
+    }
+
+
+def leg_decode(steps, warmup):
+    import torch
+    from differential_attention_causal_amd import diffattn as da
+    from differential_attention_causal_amd import synth
+    w = synth.WORKLOADS[4]
+    x = synth.make_inputs(w, "cuda:0")
+    out = torch.empty(w.batch, w.heads, w.dv, dtype=torch.bfloat16, device="cuda:0")
+    p = da.problem(w.batch, w.heads, w.seqlen, w.head_dim, da.BF16)
+    ws = torch.empty(da.workspace_bytes(da.OP_DECODE, p), dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+
+    def step(ev):
+        st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+        if ev:
+            ev[0].record()
+        da.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, out=out, workspace=ws)
+        if ev:
+            ev[1].record()
+
+    ms, wall, inner = time_steps(step, steps, warmup, inner_events=True)
+    nb = decode_bytes(w)
+    kern_ms = sum(inner) / len(inner)
+    gbs = nb / (kern_ms * 1e-3) / 1e9
+    return {
+        "workload": w.name, "value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
+        "ms_per_step": ms, "decode_ms": kern_ms, "bytes_per_step": nb,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+    }
+
+
+def leg_train(steps, warmup):
+    import torch
+    from differential_attention_causal_amd import diffattn as da
+    from differential_attention_causal_amd import synth
+    w = synth.WORKLOADS[5]
+    x = synth.make_inputs(w, "cuda:0")
+    sv = da.alloc_saved(w.batch, w.heads, w.seqlen, w.head_dim, "cuda:0")
+    out = torch.empty_like(x["v"])
+    p = da.problem(w.batch, w.heads, w.seqlen, w.head_dim, da.BF16)
+    ws = torch.empty(max(16, da.workspace_bytes(da.OP_BWD, p)), dtype=torch.uint8,
+                     device="cuda:0")
+    torch.cuda.synchronize()
+
+    def step(ev):
+        st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+        da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, out=out, saved=sv)
+        if ev:
+            ev[0].record()
+        da.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lq1"], x["lk1"], x["lq2"],
+                    x["lk2"], st, sv, x["dout"], workspace=ws)
+        if ev:
+            ev[1].record()
+
+    ms, wall, inner = time_steps(step, steps, warmup, inner_events=True)
+    pairs = causal_pairs(w.seqlen) * w.batch * w.heads
+    fl = (12.0 + 20.0) * w.head_dim * pairs
+    bwd_ms = sum(inner) / len(inner)
+    return {
+        "workload": w.name, "value": fl / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "ms_per_step": ms, "bwd_ms": bwd_ms,
+        "bwd_tflops": 20.0 * w.head_dim * pairs / (bwd_ms * 1e-3) / 1e12,
+    }
+
+
+def cpu_baseline(budget_s: float = 12.0, cap_s: float = 30.0):
+    """The float64 oracle on the host: last rows of head 0 of the forward workload."""
+    import numpy as np
+    import torch
+    from differential_attention_causal_amd import synth
+    from oracle import diffattn_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        blas_threads = None
+    w = synth.WORKLOADS[3]
+    x = synth.make_inputs(w, "cuda:0")
+    torch.cuda.synchronize()
+    h = {k: x[k][0, 0].float().cpu().double().numpy() for k in ("q1", "q2", "k1", "k2", "v")}
+    lv = {k: x[k].cpu().double().numpy() for k in ("lq1", "lk1", "lq2", "lk2")}
+    del x
+    ls = orc.lambda_scalar(lv["lq1"], lv["lk1"], lv["lq2"], lv["lk2"], w.layer)
+    n = w.seqlen
+    done_pairs, rows_done, t0 = 0, 0, time.perf_counter()
+    chunk = 128
+    hi = n
+    while hi > 0:
+        lo = max(0, hi - chunk)
+        rows = list(range(lo, hi))
+        orc.forward_rows(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], rows, ls["lambda"],
+                         ls["lambda_init"])
+        done_pairs += sum(i + 1 for i in rows)
+        rows_done += len(rows)
+        hi = lo
+        el = time.perf_counter() - t0
+        if el >= budget_s or el >= cap_s:
+            break
+    el = time.perf_counter() - t0
+    fl = 12.0 * w.head_dim * done_pairs
+    cores = blas_threads or len(os.sched_getaffinity(0))
+    return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 oracle forward_rows on the last {rows_done} query rows of head 0 "
+                      f"of B1 H16 N32768 d64 ({done_pairs} causal pairs, {el:.1f} s; "
+                      f"12 d P FLOP convention); host cpus {len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="fwd,decode,train")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward and decode shard over (batch, "
+              "head) with no exchange, so there is no multi-GPU path to time; run with "
+              "--gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    legs = set(args.legs.split(","))
+    w, fwd = leg_forward(args.steps, args.warmup)
+    rec = {
+        "metric": METRIC, "value": fwd["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": fwd["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs, generated on the GPU)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
+                   "seq_len": w.seqlen, "head_dim": w.head_dim, "v_width": w.dv,
+                   "layer": w.layer, "flop_convention": "12 d P per head"},
+        "pct_bf16_mfma_peak": 100.0 * fwd["tflops"] / PEAK_BF16_TFLOPS,
+        "roofline": fwd["roofline"],
+        "fwd_kernel_ms": fwd["fwd_kernel_ms"],
+        "formula_tflops_8dP": fwd["formula_tflops_8dP"],
+    }
+    if "decode" in legs:
+        rec["decode"] = leg_decode(args.steps, args.warmup)
+    if "train" in legs:
+        try:
+            rec["train"] = leg_train(max(1, args.steps // 2), args.warmup)
+        except Exception as e:  # backward not available in this build
+            rec["train"] = {"error": str(e)}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

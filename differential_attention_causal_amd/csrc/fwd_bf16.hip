@@ -31,6 +31,8 @@
 //  * workgroups run longest-first (the last query tiles have the most keys), and
 //    consecutive workgroup ids take different heads so that the tiles of one head land
 //    on the same XCD (ids are dealt to the 8 XCDs round-robin) and share its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -45,6 +47,7 @@ constexpr int NT = 256;       // threads per workgroup
 constexpr int K_TILE = BC * D;      // bf16 elements, rows of 128 B
 constexpr int V_TILE = DV * BC;     // bf16 elements, V^T rows of 128 B
 constexpr int STAGE = 2 * K_TILE + V_TILE;
+constexpr int NBUF = 3;       // LDS ring of stages
 
 // 16-byte unit swizzle of a K row (key index within the stage). Lanes 0..7 of an MFMA
 // operand read rows {0,1,2,3,8,9,10,11} (+16, +4 ...) which this maps to distinct units.
@@ -64,25 +67,26 @@ struct StageRegs {
   u32x4 k1[2], k2[2], v[4];
 };
 
+// Keys at or beyond N are clamped to row N-1: their scores are masked by the causal
+// predicate (key > query for every stored row), and their values are finite, so a zero
+// weight times them is zero. This keeps the loads branch-free.
 __device__ __forceinline__ void load_stage(StageRegs& r, const bf16_t* __restrict__ K1,
                                            const bf16_t* __restrict__ K2,
-                                           const bf16_t* __restrict__ V, int64_t k0,
-                                           int64_t N, int tid) {
+                                           const bf16_t* __restrict__ V, int k0, int N,
+                                           int tid) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int c = tid + NT * t;
     const int row = c >> 3, u = c & 7;
-    const int64_t key = k0 + row;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    r.k1[t] = key < N ? *reinterpret_cast<const u32x4*>(K1 + key * D + u * 8) : z;
-    r.k2[t] = key < N ? *reinterpret_cast<const u32x4*>(K2 + key * D + u * 8) : z;
+    const int key = min(k0 + row, N - 1);
+    r.k1[t] = *reinterpret_cast<const u32x4*>(K1 + key * D + u * 8);
+    r.k2[t] = *reinterpret_cast<const u32x4*>(K2 + key * D + u * 8);
   }
   const int kg = tid >> 4, dg = tid & 15;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int64_t key = k0 + 4 * kg + t;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    r.v[t] = key < N ? *reinterpret_cast<const u32x4*>(V + key * DV + dg * 8) : z;
+    const int key = min(k0 + 4 * kg + t, N - 1);
+    r.v[t] = *reinterpret_cast<const u32x4*>(V + key * DV + dg * 8);
   }
 }
 
@@ -126,35 +130,125 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& s, int base) {
   return __builtin_convertvector(t, bf16x8);
 }
 
-// Online-softmax update of one map for one 32-key sub-tile. s holds raw dot products;
-// c = log2(e) / sqrt(d). Returns exp2 weights in s; updates m (log2 domain, scaled), l
-// (this lane's partial normaliser) and alpha (rescale factor for acc).
-__device__ __forceinline__ float softmax_step(f32x16& s, float& m, float& l, float c) {
-  float mx = s[0];
+// ---------------------------------------------------------------------------------
+// One 32-key sub-tile of the pipeline. The softmax uses a lazily updated row maximum:
+// m only moves when a new score exceeds it by more than kTau (in log2 units), so the
+// accumulators are rescaled rarely; until then p = exp2(s c - m) <= 2^kTau. The final
+// O = acc / l and the log-sum-exp m + log2(l) do not depend on which m was used.
+constexpr float kTau = 8.0f;
+
+struct Scores {
+  f32x16 s1, s2;
+};
+
+// S^T = K Q^T for both maps (8 MFMAs). koff: per-lane element offsets of the K operand
+// rows for the 4 channel blocks; sub selects the 32-key half of the stage.
+__device__ __forceinline__ void qk_tile(Scores& S, const bf16_t* __restrict__ K1s,
+                                        const bf16_t* __restrict__ K2s, const int* koff,
+                                        int sub, const bf16x8* qf1, const bf16x8* qf2) {
 #pragma unroll
-  for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mn = fmaxf(m, mx * c);
-  const float alpha = fast_exp2(m - mn);
-  float sum = 0.f;
+  for (int j = 0; j < 16; ++j) S.s1[j] = S.s2[j] = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    s[j] = fast_exp2(fmaf(s[j], c, -mn));
-    sum += s[j];
+  for (int kb = 0; kb < 4; ++kb) {
+    const int off = sub * 32 * D + koff[kb];
+    S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(K1s + off), qf1[kb], S.s1, 0, 0, 0);
+    S.s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(K2s + off), qf2[kb], S.s2, 0, 0, 0);
   }
-  l = fmaf(l, alpha, sum);
-  m = mn;
-  return alpha;
 }
 
-__global__ void __launch_bounds__(NT) fwd_bf16_kernel(
+__device__ __forceinline__ float max16(const f32x16& s) {
+  float a = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int j = 2; j < 16; j += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[j], s[j + 1]));
+  return a;
+}
+
+// Row maxima of a fresh score tile (scaled, log2 domain), merged across lane halves.
+__device__ __forceinline__ void tile_max(const Scores& S, float c, float& t1, float& t2) {
+  float a = max16(S.s1), b = max16(S.s2);
+  a = fmaxf(a, __shfl_xor(a, 32));
+  b = fmaxf(b, __shfl_xor(b, 32));
+  t1 = a * c;
+  t2 = b * c;
+}
+
+// p = exp2(s c - m) for 16 scores; returns the bf16 operands of the two PV k-steps and
+// adds the fp32 weights to l.
+__device__ __forceinline__ void exp_tile(const f32x16& s, float c, float m, float& l,
+                                         bf16x8& pa, bf16x8& pb) {
+  f32x8 x, y;
+  float sa = 0.f, sb = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = fast_exp2(fmaf(s[e], c, -m));
+    y[e] = fast_exp2(fmaf(s[8 + e], c, -m));
+    sa += x[e];
+    sb += y[e];
+  }
+  l += sa + sb;
+  pa = __builtin_convertvector(x, bf16x8);
+  pb = __builtin_convertvector(y, bf16x8);
+}
+
+__device__ __forceinline__ void pv_tile(f32x16* acc1, f32x16* acc2, const bf16_t* __restrict__ Vt,
+                                        const int* voff, int sub, const bf16x8& p1a,
+                                        const bf16x8& p1b, const bf16x8& p2a,
+                                        const bf16x8& p2b) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const bf16x8 va = lds_read8(Vt + (voff[b] ^ (32 * sub)));
+    const bf16x8 vb = lds_read8(Vt + (voff[b] ^ (32 * sub + 16)));
+    acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1a, acc1[b], 0, 0, 0);
+    acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p2a, acc2[b], 0, 0, 0);
+    acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p1b, acc1[b], 0, 0, 0);
+    acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p2b, acc2[b], 0, 0, 0);
+  }
+}
+
+// Causal predicate on a sub-tile starting at key ks: key > query -> -inf.
+__device__ __forceinline__ void mask_tile(Scores& S, int ks, int q, int h) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (ks + key_of(j, h) > q) {
+      S.s1[j] = -INFINITY;
+      S.s2[j] = -INFINITY;
+    }
+  }
+}
+
+// Lazy max update for the next tile. The branch is taken when some row of the wave grew
+// by more than kTau, but each row moves its own maximum only on its own trigger (the
+// others multiply by exactly 1), so every row's result depends on its own scores only.
+__device__ __forceinline__ void maybe_rescale(float t1, float t2, float& m1, float& m2,
+                                              float& l1, float& l2, f32x16* acc1,
+                                              f32x16* acc2) {
+  const bool n1 = t1 > m1 + kTau, n2 = t2 > m2 + kTau;
+  if (__builtin_expect(__any(n1 || n2), 0)) {
+    const float a1 = n1 ? fast_exp2(m1 - t1) : 1.0f;
+    const float a2 = n2 ? fast_exp2(m2 - t2) : 1.0f;
+    m1 = n1 ? t1 : m1;
+    m2 = n2 ? t2 : m2;
+    l1 *= a1;
+    l2 *= a2;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        acc1[b][j] *= a1;
+        acc2[b][j] *= a2;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
     const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
     const bf16_t* __restrict__ v, const diffattn_lambda_state* __restrict__ lamst,
     const float* __restrict__ rms_w, bf16_t* __restrict__ out, float* __restrict__ sv_lse1,
     float* __restrict__ sv_lse2, float* __restrict__ sv_o1, float* __restrict__ sv_o2,
-    float* __restrict__ sv_rstd, int64_t BH, int64_t H, int64_t N, int nqb, float eps) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
+    float* __restrict__ sv_rstd, int BH, int H, int N, int nqb, float eps) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];  // NBUF stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,29 +257,40 @@ __global__ void __launch_bounds__(NT) fwd_bf16_kernel(
   const int h = lane >> 5;
 
   // Longest-first over query tiles; consecutive ids walk the heads.
-  const int64_t bid = blockIdx.x;
-  const int64_t bh = bid % BH;
-  const int qb = nqb - 1 - static_cast<int>(bid / BH);
-  const int64_t q0 = static_cast<int64_t>(qb) * BR;
-  const int64_t q0w = q0 + 32 * wv;
+  const int bid = blockIdx.x;
+  const int bh = bid % BH;
+  const int qb = nqb - 1 - bid / BH;
+  const int q0 = qb * BR;
+  const int q0w = q0 + 32 * wv;
+  const int64_t hoff = static_cast<int64_t>(bh) * N;
 
-  const bf16_t* Q1 = q1 + bh * N * D;
-  const bf16_t* Q2 = q2 + bh * N * D;
-  const bf16_t* K1 = k1 + bh * N * D;
-  const bf16_t* K2 = k2 + bh * N * D;
-  const bf16_t* V = v + bh * N * DV;
+  const bf16_t* Q1 = q1 + hoff * D;
+  const bf16_t* Q2 = q2 + hoff * D;
+  const bf16_t* K1 = k1 + hoff * D;
+  const bf16_t* K2 = k2 + hoff * D;
+  const bf16_t* V = v + hoff * DV;
 
   // Q^T operand: lane holds query q0w + m, channels 16 kb + 8 h .. + 7.
   bf16x8 qf1[4], qf2[4];
   {
-    const int64_t q = q0w + m;
+    const int q = min(q0w + m, N - 1);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      u32x4 a = q < N ? *reinterpret_cast<const u32x4*>(Q1 + q * D + 16 * kb + 8 * h) : z;
-      u32x4 b = q < N ? *reinterpret_cast<const u32x4*>(Q2 + q * D + 16 * kb + 8 * h) : z;
-      qf1[kb] = __builtin_bit_cast(bf16x8, a);
-      qf2[kb] = __builtin_bit_cast(bf16x8, b);
+      qf1[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Q1 + q * D + 16 * kb + 8 * h));
+      qf2[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Q2 + q * D + 16 * kb + 8 * h));
+    }
+  }
+  // Per-lane LDS operand offsets (elements within a stage).
+  int koff[4], voff[4];
+  {
+    const int kr = perm_row(m);
+    const int ks = k_swz(kr);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) koff[kb] = kr * D + 8 * ((2 * kb + h) ^ ks);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int row = 32 * b + m;
+      voff[b] = 2 * K_TILE + row * BC + 8 * (h ^ v_swz(row));
     }
   }
 
@@ -198,76 +303,67 @@ __global__ void __launch_bounds__(NT) fwd_bf16_kernel(
     for (int j = 0; j < 16; ++j) acc1[b][j] = acc2[b][j] = 0.f;
   }
 
-  const int64_t kend = (q0 + BR < N) ? q0 + BR : N;
-  const int n_stages = static_cast<int>((kend + BC - 1) / BC);
+  const int kend = min(N, q0 + BR);
+  const int n_stages = (kend + BC - 1) / BC;
+  const int n_full = q0 / BC;  // stages whose keys are all < q0: no mask for any row
+  const int qrow = q0w + m;
 
+  // One pipeline step: QK^T of the next sub-tile (tile index nt, sub-tile ksub of the
+  // stage in kbuf) while the current tile's exponentials are formed, then PV of the
+  // current tile (sub-tile vsub of vbuf) while the next tile's row maxima are taken.
+  auto step = [&](auto mask_tag, Scores& cur, Scores& nxt, const bf16_t* kbuf, int ksub,
+                  const bf16_t* vbuf, int vsub, int nt) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    qk_tile(nxt, kbuf, kbuf + K_TILE, koff, ksub, qf1, qf2);
+    bf16x8 p1a, p1b, p2a, p2b;
+    exp_tile(cur.s1, c, m1, l1, p1a, p1b);
+    exp_tile(cur.s2, c, m2, l2, p2a, p2b);
+    if (kMask) mask_tile(nxt, 32 * nt, qrow, h);
+    pv_tile(acc1, acc2, vbuf, voff, vsub, p1a, p1b, p2a, p2b);
+    float t1, t2;
+    tile_max(nxt, c, t1, t2);
+    maybe_rescale(t1, t2, m1, m2, l1, l2, acc1, acc2);
+  };
+  // Stage s: sub-tiles 2s (in A) and 2s+1, and the QK^T of sub-tile 2s+2 (stage s+1).
+  // Stage s+1 was fetched into registers when stage s opened; it is written to its LDS
+  // buffer here, opened at the barrier, and stage s+2 is fetched.
+  Scores A, B;
   StageRegs regs;
+  auto stage = [&](auto mask_tag, int s) __attribute__((always_inline)) {
+    const bf16_t* bs = smem + (s % NBUF) * STAGE;
+    const bf16_t* bn = smem + ((s + 1) % NBUF) * STAGE;
+    step(mask_tag, A, B, bs, 1, bs, 0, 2 * s + 1);
+    store_stage(regs, smem + ((s + 1) % NBUF) * STAGE, tid);
+    __syncthreads();
+    if (s + 2 < n_stages) load_stage(regs, K1, K2, V, (s + 2) * BC, N, tid);
+    step(mask_tag, B, A, bn, 0, bs, 1, 2 * s + 2);
+  };
+  using NoMask = std::integral_constant<bool, false>;
+  using Mask = std::integral_constant<bool, true>;
+
+  // Prologue: stage 0 resident, stage 1 in flight, scores and max of sub-tile 0.
   load_stage(regs, K1, K2, V, 0, N, tid);
   store_stage(regs, smem, tid);
-
-  for (int st = 0; st < n_stages; ++st) {
-    __syncthreads();
-    const bool more = st + 1 < n_stages;
-    if (more) load_stage(regs, K1, K2, V, static_cast<int64_t>(st + 1) * BC, N, tid);
-    const bf16_t* buf = smem + (st & 1) * STAGE;
-    const bf16_t* K1s = buf;
-    const bf16_t* K2s = buf + K_TILE;
-    const bf16_t* Vt = buf + 2 * K_TILE;
-    const int64_t k0 = static_cast<int64_t>(st) * BC;
-
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int64_t ks = k0 + 32 * sb;
-      if (ks > q0w + 31) continue;  // whole sub-tile above this wave's diagonal
-      f32x16 s1, s2;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s1[j] = s2[j] = 0.f;
-      const int krow = 32 * sb + perm_row(m);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int off = krow * D + 8 * ((2 * kb + h) ^ k_swz(krow));
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(K1s + off), qf1[kb], s1, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(K2s + off), qf2[kb], s2, 0, 0, 0);
-      }
-      if (ks + 31 > q0w) {  // diagonal sub-tile: key <= query
-        const int64_t q = q0w + m;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int64_t key = ks + key_of(j, h);
-          if (key > q) {
-            s1[j] = -INFINITY;
-            s2[j] = -INFINITY;
-          }
-        }
-      }
-      const float a1 = softmax_step(s1, m1, l1, c);
-      const float a2 = softmax_step(s2, m2, l2, c);
-      if (__any((a1 != 1.0f) || (a2 != 1.0f))) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            acc1[b][j] *= a1;
-            acc2[b][j] *= a2;
-          }
-        }
-      }
-      const bf16x8 p1a = to_bf16x8(s1, 0), p1b = to_bf16x8(s1, 8);
-      const bf16x8 p2a = to_bf16x8(s2, 0), p2b = to_bf16x8(s2, 8);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int row = 32 * b + m;
-        const int base = row * BC;
-        const int sw = v_swz(row);
-        const bf16x8 va = lds_read8(Vt + base + 8 * ((4 * sb + 0 + h) ^ sw));
-        const bf16x8 vb = lds_read8(Vt + base + 8 * ((4 * sb + 2 + h) ^ sw));
-        acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1a, acc1[b], 0, 0, 0);
-        acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p2a, acc2[b], 0, 0, 0);
-        acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p1b, acc1[b], 0, 0, 0);
-        acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p2b, acc2[b], 0, 0, 0);
-      }
-    }
-    if (more) store_stage(regs, smem + ((st + 1) & 1) * STAGE, tid);
+  __syncthreads();
+  if (n_stages > 1) load_stage(regs, K1, K2, V, BC, N, tid);
+  qk_tile(A, smem, smem + K_TILE, koff, 0, qf1, qf2);
+  if (n_full == 0) mask_tile(A, 0, qrow, h);
+  {
+    float t1, t2;
+    tile_max(A, c, t1, t2);
+    maybe_rescale(t1, t2, m1, m2, l1, l2, acc1, acc2);
+  }
+  int s = 0;
+  for (; s + 1 < n_full; ++s) stage(NoMask{}, s);
+  for (; s + 1 < n_stages; ++s) stage(Mask{}, s);
+  {
+    // Last stage: sub-tiles 2s and 2s+1, nothing further to fetch.
+    const bf16_t* bs = smem + (s % NBUF) * STAGE;
+    step(Mask{}, A, B, bs, 1, bs, 0, 2 * s + 1);
+    bf16x8 p1a, p1b, p2a, p2b;
+    exp_tile(B.s1, c, m1, l1, p1a, p1b);
+    exp_tile(B.s2, c, m2, l2, p2a, p2b);
+    pv_tile(acc1, acc2, bs, voff, 1, p1a, p1b, p2a, p2b);
   }
 
   // Epilogue: combine the two lane halves' normalisers, form O, RMSNorm, scale, store.
@@ -291,37 +387,37 @@ __global__ void __launch_bounds__(NT) fwd_bf16_kernel(
   }
   ss += __shfl_xor(ss, 32);
   const float rstd = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
-  const int64_t q = q0w + m;
-  if (q < N) {
-    const int64_t hh = bh % H;
-    bf16_t* Y = out + (bh * N + q) * DV;
+  if (qrow < N) {
+    const int hh = bh % H;
+    bf16_t* Y = out + (hoff + qrow) * DV;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         const int col = 32 * b + 8 * jg + 4 * h;
+        f32x4 w = {1.f, 1.f, 1.f, 1.f};
+        if (rms_w) w = *reinterpret_cast<const f32x4*>(rms_w + hh * DV + col);
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float o = acc1[b][4 * jg + e] - lam * acc2[b][4 * jg + e];
-          const float w = rms_w ? rms_w[hh * DV + col + e] : 1.0f;
-          y[e] = g * (w * (o * rstd));
+          y[e] = g * (w[e] * (o * rstd));
         }
         u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
         *reinterpret_cast<u32x2*>(Y + col) = pk;
         if (sv_o1) {
           f32x4 a = {acc1[b][4 * jg], acc1[b][4 * jg + 1], acc1[b][4 * jg + 2], acc1[b][4 * jg + 3]};
           f32x4 bb = {acc2[b][4 * jg], acc2[b][4 * jg + 1], acc2[b][4 * jg + 2], acc2[b][4 * jg + 3]};
-          *reinterpret_cast<f32x4*>(sv_o1 + (bh * N + q) * DV + col) = a;
-          *reinterpret_cast<f32x4*>(sv_o2 + (bh * N + q) * DV + col) = bb;
+          *reinterpret_cast<f32x4*>(sv_o1 + (hoff + qrow) * DV + col) = a;
+          *reinterpret_cast<f32x4*>(sv_o2 + (hoff + qrow) * DV + col) = bb;
         }
       }
     }
     if (sv_lse1 && h == 0) {
       // lse_k = ln(sum_j exp(S_kj)) = (m_k + log2 l_k) * ln 2, m_k in the scaled log2 domain.
-      sv_lse1[bh * N + q] = (m1 + __log2f(l1)) * kLn2;
-      sv_lse2[bh * N + q] = (m2 + __log2f(l2)) * kLn2;
-      sv_rstd[bh * N + q] = rstd;
+      sv_lse1[hoff + qrow] = (m1 + __log2f(l1)) * kLn2;
+      sv_lse2[hoff + qrow] = (m2 + __log2f(l2)) * kLn2;
+      sv_rstd[hoff + qrow] = rstd;
     }
   }
 }
@@ -333,15 +429,25 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const int64_t BH = a.B * a.H;
   const int nqb = static_cast<int>((a.N + BR - 1) / BR);
   const int64_t nblk = BH * nqb;
+  const size_t lds = static_cast<size_t>(NBUF) * STAGE * sizeof(bf16_t);
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
   const diffattn_saved& sv = a.saved;
-  hipLaunchKernelGGL(fwd_bf16_kernel, dim3(static_cast<unsigned>(nblk)), dim3(NT), 0, s,
+  hipLaunchKernelGGL(fwd_bf16_kernel, dim3(static_cast<unsigned>(nblk)), dim3(NT), lds, s,
                      static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
                      static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
                      static_cast<const bf16_t*>(a.v), a.lam, a.rms_weight,
                      static_cast<bf16_t*>(a.out), a.training ? sv.lse1 : nullptr,
                      a.training ? sv.lse2 : nullptr, a.training ? sv.o1 : nullptr,
-                     a.training ? sv.o2 : nullptr, a.training ? sv.rstd : nullptr, BH, a.H,
-                     a.N, nqb, a.eps);
+                     a.training ? sv.o2 : nullptr, a.training ? sv.rstd : nullptr,
+                     static_cast<int>(BH), static_cast<int>(a.H), static_cast<int>(a.N), nqb,
+                     a.eps);
   return hipGetLastError();
 }
 
