@@ -24,8 +24,13 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed float32 ops (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaN inputs are supported, so max/min need no canonicalisation of MFMA results
+    "-fno-honor-nans",
     "-Wall", "-Wno-unused-function",
 ]
+
+# Per-file extra flags (none at present).
+FILE_FLAGS = {}
 
 
 def hipcc() -> str:
@@ -38,7 +43,8 @@ def hipcc() -> str:
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + ["-I", INCLUDE, "-I", CSRC] + lang + \
+    cmd = [hipcc()] + HIPCC_FLAGS + FILE_FLAGS.get(src, []) + list(extra) + \
+        ["-I", INCLUDE, "-I", CSRC] + lang + \
         ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"

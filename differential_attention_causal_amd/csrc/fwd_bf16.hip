@@ -22,12 +22,19 @@
 //  * the key rows fed to the MFMA are permuted (bits 2 and 3 of the row swapped) so
 //    that the score registers are directly the B operand of O^T += V^T P^T, with each
 //    lane's 8 keys contiguous in the transposed V tile;
-//  * K1, K2 (64 keys x 64) and V^T (128 x 64 keys) tiles are staged through LDS, double
-//    buffered, with XOR swizzles that keep the 16-byte reads conflict-free; V is
-//    transposed in registers on its way to LDS;
-//  * the diagonal tile applies the causal predicate key <= query as an integer compare;
-//    tiles above the diagonal are skipped, rows beyond N and keys beyond N are zero
-//    filled and masked by the same predicate;
+//  * K1, K2 (64 keys x 64) and V^T tiles go through a ring of three LDS stages with one
+//    barrier per 64 keys; V is transposed in registers on its way to LDS. Every LDS
+//    operand read is a per-lane base register plus a compile-time offset (the stage loop
+//    is unrolled over the ring), and the layouts keep those reads and the transposing
+//    writes free of bank conflicts;
+//  * software pipeline per 32-key sub-tile: the QK^T MFMAs of the next sub-tile are
+//    issued with the exponentials of the current one, and its PV MFMAs with the next
+//    sub-tile's row maxima;
+//  * the running max moves lazily (see maybe_rescale), so the 256 accumulator registers
+//    are rescaled only a handful of times per row;
+//  * stages wholly below the query tile run without mask code; the last two stages apply
+//    the causal predicate key <= query as an integer compare. Keys beyond N are clamped
+//    loads that the same predicate masks; rows beyond N are not stored;
 //  * workgroups run longest-first (the last query tiles have the most keys), and
 //    consecutive workgroup ids take different heads so that the tiles of one head land
 //    on the same XCD (ids are dealt to the 8 XCDs round-robin) and share its L2.
@@ -44,17 +51,24 @@ constexpr int DV = 128;
 constexpr int BR = 128;       // query rows per workgroup
 constexpr int BC = 64;        // keys per LDS stage
 constexpr int NT = 256;       // threads per workgroup
-constexpr int K_TILE = BC * D;      // bf16 elements, rows of 128 B
-constexpr int V_TILE = DV * BC;     // bf16 elements, V^T rows of 128 B
-constexpr int STAGE = 2 * K_TILE + V_TILE;
 constexpr int NBUF = 3;       // LDS ring of stages
 
-// 16-byte unit swizzle of a K row (key index within the stage). Lanes 0..7 of an MFMA
-// operand read rows {0,1,2,3,8,9,10,11} (+16, +4 ...) which this maps to distinct units.
+// LDS layout (bytes): [V^T stage 0..2][K1 stage 0..2][K2 stage 0..2].
+// V^T stage: 4 blocks, one per (32-key half sb, 16-key step t) = block 2 sb + t; a block
+// holds 128 channel rows of 16 keys (32 B), padded by 32 B so the four blocks start in
+// different banks. Inside a row the two 16-byte halves are swapped on bit 2 of the row.
+// K stage: 64 key rows of 128 B; 16-byte unit u of row r is stored at u ^ k_swz(r).
+constexpr int VROW = 32;
+constexpr int VBLK = DV * VROW + 32;          // 4128
+constexpr int VSTAGE = 4 * VBLK;              // 16512
+constexpr int KSTAGE = BC * D * 2;            // 8192
+constexpr int V_BASE = 0;
+constexpr int K1_BASE = NBUF * VSTAGE;        // 49536
+constexpr int K2_BASE = K1_BASE + NBUF * KSTAGE;
+constexpr int LDS_BYTES = K2_BASE + NBUF * KSTAGE;  // 98688
+static_assert(K1_BASE % 16 == 0 && K2_BASE % 16 == 0, "16-byte aligned regions");
+
 __device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
-// 16-byte unit swizzle of a V^T row (output channel). Distinct for 8 consecutive rows
-// (operand reads) and for rows 8 apart (the transposing writes).
-__device__ __forceinline__ int v_swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
 
 // Physical key (0..31 within a 32-key sub-tile) held in score register j by lane half h.
 __device__ __forceinline__ int key_of(int j, int h) { return 16 * (j >> 3) + 8 * h + (j & 7); }
@@ -67,44 +81,46 @@ struct StageRegs {
   u32x4 k1[2], k2[2], v[4];
 };
 
-// Keys at or beyond N are clamped to row N-1: their scores are masked by the causal
-// predicate (key > query for every stored row), and their values are finite, so a zero
-// weight times them is zero. This keeps the loads branch-free.
-__device__ __forceinline__ void load_stage(StageRegs& r, const bf16_t* __restrict__ K1,
-                                           const bf16_t* __restrict__ K2,
-                                           const bf16_t* __restrict__ V, int k0, int N,
-                                           int tid) {
+// Tile loads are raw buffer loads through a resource descriptor that starts at the
+// stage's first key and covers the rows that remain below N: rows at or beyond N read as
+// zero in hardware (their scores are masked by the causal predicate, key > query for
+// every stored row). The per-thread offsets are constant, so a stage costs no vector ALU
+// work for addressing.
+constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer, no swizzle
+
+struct HeadRsrc {
+  __amdgpu_buffer_rsrc_t k1, k2, v;
+};
+
+// k0: first key of the stage; kvo / vvo: this thread's constant byte offsets in a K / V
+// tile. The descriptors cover the head's N rows, so rows at or beyond N read as zero.
+__device__ __forceinline__ void load_stage(StageRegs& r, const HeadRsrc& rs, int k0, int kvo,
+                                           int vvo) {
+  // K: 16-byte chunk c = tid + 256 t of the 64 x 128-byte tile (row c / 8, unit c % 8).
+  const int ko = kvo + k0 * (D * 2);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int c = tid + NT * t;
-    const int row = c >> 3, u = c & 7;
-    const int key = min(k0 + row, N - 1);
-    r.k1[t] = *reinterpret_cast<const u32x4*>(K1 + key * D + u * 8);
-    r.k2[t] = *reinterpret_cast<const u32x4*>(K2 + key * D + u * 8);
+    r.k1[t] = __builtin_amdgcn_raw_buffer_load_b128(rs.k1, ko + 4096 * t, 0, 0);
+    r.k2[t] = __builtin_amdgcn_raw_buffer_load_b128(rs.k2, ko + 4096 * t, 0, 0);
   }
-  const int kg = tid >> 4, dg = tid & 15;
+  // V: thread (kg = tid % 16, dg = tid / 16) takes keys 4kg..4kg+3, channels 8dg..8dg+7.
+  const int vo = vvo + k0 * (DV * 2);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int key = min(k0 + 4 * kg + t, N - 1);
-    r.v[t] = *reinterpret_cast<const u32x4*>(V + key * DV + dg * 8);
-  }
+  for (int t = 0; t < 4; ++t) r.v[t] = __builtin_amdgcn_raw_buffer_load_b128(rs.v, vo + 256 * t, 0, 0);
 }
 
-__device__ __forceinline__ void store_stage(const StageRegs& r, bf16_t* __restrict__ st,
-                                            int tid) {
-  bf16_t* K1s = st;
-  bf16_t* K2s = st + K_TILE;
-  bf16_t* Vt = st + 2 * K_TILE;
+// kw / kw2: this thread's K1 / K2 write address in ring slot 0 (chunk tid; chunk
+// tid + 256 is 32 rows further); vw0 / vw1: its V^T write address for channels c < 4 and
+// c >= 4 of its 8 (the 16-byte half flips with bit 2 of the channel row).
+__device__ __forceinline__ void store_stage(const StageRegs& r, char* __restrict__ lds,
+                                            int buf, int kw, int kw2, int vw0, int vw1) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int c = tid + NT * t;
-    const int row = c >> 3, u = c & 7;
-    const int off = row * D + 8 * (u ^ k_swz(row));
-    *reinterpret_cast<u32x4*>(K1s + off) = r.k1[t];
-    *reinterpret_cast<u32x4*>(K2s + off) = r.k2[t];
+    *reinterpret_cast<u32x4*>(lds + kw + buf * KSTAGE + 4096 * t) = r.k1[t];
+    *reinterpret_cast<u32x4*>(lds + kw2 + buf * KSTAGE + 4096 * t) = r.k2[t];
   }
-  // 4 keys x 8 channels per thread -> 8 channel rows of 4 keys each.
-  const int kg = tid >> 4, dg = tid & 15;
+  // Transpose 4 keys x 8 channels to 8 channel rows of 4 keys (8 bytes each). The 16
+  // lanes sharing dg write 16 different 8-byte slots of one row position: no conflicts.
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     // channel c of keys (4kg, 4kg+1) and (4kg+2, 4kg+3), low half = earlier key
@@ -112,54 +128,45 @@ __device__ __forceinline__ void store_stage(const StageRegs& r, bf16_t* __restri
     const uint32_t x2 = r.v[2][c >> 1], x3 = r.v[3][c >> 1];
     const uint32_t lo = (c & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
     const uint32_t hi = (c & 1) ? ((x2 >> 16) | (x3 & 0xffff0000u)) : ((x2 & 0xffffu) | (x3 << 16));
-    const int row = 8 * dg + c;
-    const int off = row * BC + 8 * ((kg >> 1) ^ v_swz(row)) + 4 * (kg & 1);
     u32x2 w = {lo, hi};
-    *reinterpret_cast<u32x2*>(Vt + off) = w;
+    *reinterpret_cast<u32x2*>(lds + (c < 4 ? vw0 : vw1) + buf * VSTAGE + c * VROW) = w;
   }
 }
 
-__device__ __forceinline__ bf16x8 lds_read8(const bf16_t* p) {
+__device__ __forceinline__ bf16x8 lds_read8(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& s, int base) {
-  f32x8 t;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = s[base + e];
-  return __builtin_convertvector(t, bf16x8);
-}
-
 // ---------------------------------------------------------------------------------
-// One 32-key sub-tile of the pipeline. The softmax uses a lazily updated row maximum:
-// m only moves when a new score exceeds it by more than kTau (in log2 units), so the
-// accumulators are rescaled rarely; until then p = exp2(s c - m) <= 2^kTau. The final
-// O = acc / l and the log-sum-exp m + log2(l) do not depend on which m was used.
+// The softmax uses a lazily updated row maximum: m only moves when a new score exceeds
+// it by more than kTau (in log2 units), so the accumulators are rescaled rarely; until
+// then p = exp2(s c - m) <= 2^kTau. The final O = acc / l and the log-sum-exp
+// m + log2(l) do not depend on which m was used.
 constexpr float kTau = 8.0f;
 
 struct Scores {
   f32x16 s1, s2;
 };
 
-// S^T = K Q^T for both maps (8 MFMAs). koff: per-lane element offsets of the K operand
-// rows for the 4 channel blocks; sub selects the 32-key half of the stage.
-__device__ __forceinline__ void qk_tile(Scores& S, const bf16_t* __restrict__ K1s,
-                                        const bf16_t* __restrict__ K2s, const int* koff,
-                                        int sub, const bf16x8* qf1, const bf16x8* qf2) {
+// S^T = K Q^T for both maps (8 MFMAs). kaddr: per-lane LDS byte addresses of the K1
+// operand rows for the 4 channel blocks; koff: stage and sub-tile byte offset.
+__device__ __forceinline__ void qk_tile(Scores& S, const char* lds, const int* kaddr, int koff,
+                                        const bf16x8* qf1, const bf16x8* qf2) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) S.s1[j] = S.s2[j] = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const int off = sub * 32 * D + koff[kb];
-    S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(K1s + off), qf1[kb], S.s1, 0, 0, 0);
-    S.s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(K2s + off), qf2[kb], S.s2, 0, 0, 0);
+    const char* p = lds + kaddr[kb] + koff;
+    S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(p), qf1[kb], S.s1, 0, 0, 0);
+    S.s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(p + (K2_BASE - K1_BASE)),
+                                                   qf2[kb], S.s2, 0, 0, 0);
   }
 }
 
 __device__ __forceinline__ float max16(const f32x16& s) {
   float a = fmaxf(s[0], s[1]);
 #pragma unroll
-  for (int j = 2; j < 16; j += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[j], s[j + 1]));
+  for (int j = 2; j < 16; j += 2) a = fmaxf(a, fmaxf(s[j], s[j + 1]));
   return a;
 }
 
@@ -190,14 +197,16 @@ __device__ __forceinline__ void exp_tile(const f32x16& s, float c, float m, floa
   pb = __builtin_convertvector(y, bf16x8);
 }
 
-__device__ __forceinline__ void pv_tile(f32x16* acc1, f32x16* acc2, const bf16_t* __restrict__ Vt,
-                                        const int* voff, int sub, const bf16x8& p1a,
-                                        const bf16x8& p1b, const bf16x8& p2a,
-                                        const bf16x8& p2b) {
+// O^T += V^T P^T for both maps (16 MFMAs). vaddr: per-lane V^T byte address; voff: stage
+// and sub-tile byte offset.
+__device__ __forceinline__ void pv_tile(f32x16* acc1, f32x16* acc2, const char* lds, int vaddr,
+                                        int voff, const bf16x8& p1a, const bf16x8& p1b,
+                                        const bf16x8& p2a, const bf16x8& p2b) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const bf16x8 va = lds_read8(Vt + (voff[b] ^ (32 * sub)));
-    const bf16x8 vb = lds_read8(Vt + (voff[b] ^ (32 * sub + 16)));
+    const char* p = lds + vaddr + voff + b * 32 * VROW;
+    const bf16x8 va = lds_read8(p);
+    const bf16x8 vb = lds_read8(p + VBLK);
     acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1a, acc1[b], 0, 0, 0);
     acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p2a, acc2[b], 0, 0, 0);
     acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p1b, acc1[b], 0, 0, 0);
@@ -241,6 +250,9 @@ __device__ __forceinline__ void maybe_rescale(float t1, float t2, float& m1, flo
   }
 }
 
+using NoMask = std::integral_constant<bool, false>;
+using Mask = std::integral_constant<bool, true>;
+
 __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
     const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
@@ -248,7 +260,7 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     const float* __restrict__ rms_w, bf16_t* __restrict__ out, float* __restrict__ sv_lse1,
     float* __restrict__ sv_lse2, float* __restrict__ sv_o1, float* __restrict__ sv_o2,
     float* __restrict__ sv_rstd, int BH, int H, int N, int nqb, float eps) {
-  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];  // NBUF stages
+  extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -280,18 +292,32 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
       qf2[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Q2 + q * D + 16 * kb + 8 * h));
     }
   }
-  // Per-lane LDS operand offsets (elements within a stage).
-  int koff[4], voff[4];
+  // Per-lane LDS operand addresses (bytes).
+  int kaddr[4];
   {
     const int kr = perm_row(m);
     const int ks = k_swz(kr);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) koff[kb] = kr * D + 8 * ((2 * kb + h) ^ ks);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int row = 32 * b + m;
-      voff[b] = 2 * K_TILE + row * BC + 8 * (h ^ v_swz(row));
-    }
+    for (int kb = 0; kb < 4; ++kb) kaddr[kb] = K1_BASE + kr * 128 + 16 * ((2 * kb + h) ^ ks);
+  }
+  int vaddr = V_BASE + m * VROW + 16 * (h ^ ((m >> 2) & 1));
+  HeadRsrc rs;
+  rs.k1 = __builtin_amdgcn_make_buffer_rsrc((void*)K1, 0, N * D * 2, kBufFlags);
+  rs.k2 = __builtin_amdgcn_make_buffer_rsrc((void*)K2, 0, N * D * 2, kBufFlags);
+  rs.v = __builtin_amdgcn_make_buffer_rsrc((void*)V, 0, N * DV * 2, kBufFlags);
+  // Tile load offsets and LDS write addresses of this thread (see load/store_stage).
+  const int kvo = 16 * tid;
+  const int kgi = tid & 15, dgi = tid >> 4;
+  const int vvo = 4 * kgi * DV * 2 + 16 * dgi;
+  int kw, kw2, vw0, vw1;
+  {
+    const int row = tid >> 3, u = tid & 7;
+    kw = K1_BASE + row * 128 + 16 * (u ^ k_swz(row));
+    kw2 = kw + (K2_BASE - K1_BASE);
+    const int blk = kgi >> 2, uu = (kgi >> 1) & 1, half = kgi & 1;
+    const int vb = V_BASE + blk * VBLK + 8 * half + 8 * dgi * VROW;
+    vw0 = vb + 16 * uu;
+    vw1 = vb + 16 * (uu ^ 1);
   }
 
   const float c = kLog2e / 8.0f;  // log2(e) / sqrt(64)
@@ -308,45 +334,66 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   const int n_full = q0 / BC;  // stages whose keys are all < q0: no mask for any row
   const int qrow = q0w + m;
 
-  // One pipeline step: QK^T of the next sub-tile (tile index nt, sub-tile ksub of the
-  // stage in kbuf) while the current tile's exponentials are formed, then PV of the
-  // current tile (sub-tile vsub of vbuf) while the next tile's row maxima are taken.
-  auto step = [&](auto mask_tag, Scores& cur, Scores& nxt, const bf16_t* kbuf, int ksub,
-                  const bf16_t* vbuf, int vsub, int nt) __attribute__((always_inline)) {
+  // One pipeline step: QK^T of the next sub-tile (K operand bases kb + byte offset
+  // kofs) while the current tile's exponentials are formed, then PV of the current tile
+  // (V^T base vb + byte offset vofs) while the next tile's row maxima are taken.
+  auto step = [&](auto mask_tag, Scores& cur, Scores& nxt, const int* kb, int kofs, int vb,
+                  int vofs, int nt) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    qk_tile(nxt, kbuf, kbuf + K_TILE, koff, ksub, qf1, qf2);
+    qk_tile(nxt, lds, kb, kofs, qf1, qf2);
     bf16x8 p1a, p1b, p2a, p2b;
     exp_tile(cur.s1, c, m1, l1, p1a, p1b);
     exp_tile(cur.s2, c, m2, l2, p2a, p2b);
     if (kMask) mask_tile(nxt, 32 * nt, qrow, h);
-    pv_tile(acc1, acc2, vbuf, voff, vsub, p1a, p1b, p2a, p2b);
+    pv_tile(acc1, acc2, lds, vb, vofs, p1a, p1b, p2a, p2b);
     float t1, t2;
     tile_max(nxt, c, t1, t2);
     maybe_rescale(t1, t2, m1, m2, l1, l2, acc1, acc2);
   };
+  // The per-lane LDS bases follow the ring: kcur / vcur address ring slot s % 3 (the
+  // stage being consumed) and kw.. the slot (s + 1) % 3 being filled; each advances by
+  // one slot per stage, wrapping after three.
+  int kcur[4] = {kaddr[0], kaddr[1], kaddr[2], kaddr[3]};
+  int vcur = vaddr;
+  kw += KSTAGE;
+  kw2 += KSTAGE;
+  vw0 += VSTAGE;
+  vw1 += VSTAGE;
+  int slot = 0;
   // Stage s: sub-tiles 2s (in A) and 2s+1, and the QK^T of sub-tile 2s+2 (stage s+1).
-  // Stage s+1 was fetched into registers when stage s opened; it is written to its LDS
-  // buffer here, opened at the barrier, and stage s+2 is fetched.
+  // Stage s+1 was fetched into registers when stage s opened; it is written to its slot
+  // here, opened at the barrier, and stage s+2 is fetched.
   Scores A, B;
   StageRegs regs;
   auto stage = [&](auto mask_tag, int s) __attribute__((always_inline)) {
-    const bf16_t* bs = smem + (s % NBUF) * STAGE;
-    const bf16_t* bn = smem + ((s + 1) % NBUF) * STAGE;
-    step(mask_tag, A, B, bs, 1, bs, 0, 2 * s + 1);
-    store_stage(regs, smem + ((s + 1) % NBUF) * STAGE, tid);
+    const int kstep = slot == 2 ? -2 * KSTAGE : KSTAGE;
+    const int vstep = slot == 2 ? -2 * VSTAGE : VSTAGE;
+    const int wk = slot == 1 ? -2 * KSTAGE : KSTAGE;   // the filled slot is one ahead
+    const int wv = slot == 1 ? -2 * VSTAGE : VSTAGE;
+    int knext[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) knext[i] = kcur[i] + kstep;
+    step(mask_tag, A, B, kcur, 32 * 128, vcur, 0, 2 * s + 1);
+    store_stage(regs, lds, 0, kw, kw2, vw0, vw1);
     __syncthreads();
-    if (s + 2 < n_stages) load_stage(regs, K1, K2, V, (s + 2) * BC, N, tid);
-    step(mask_tag, B, A, bn, 0, bs, 1, 2 * s + 2);
+    if (s + 2 < n_stages) load_stage(regs, rs, (s + 2) * BC, kvo, vvo);
+    step(mask_tag, B, A, knext, 0, vcur, 2 * VBLK, 2 * s + 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kcur[i] = knext[i];
+    vcur += vstep;
+    kw += wk;
+    kw2 += wk;
+    vw0 += wv;
+    vw1 += wv;
+    slot = slot == 2 ? 0 : slot + 1;
   };
-  using NoMask = std::integral_constant<bool, false>;
-  using Mask = std::integral_constant<bool, true>;
 
   // Prologue: stage 0 resident, stage 1 in flight, scores and max of sub-tile 0.
-  load_stage(regs, K1, K2, V, 0, N, tid);
-  store_stage(regs, smem, tid);
+  load_stage(regs, rs, 0, kvo, vvo);
+  store_stage(regs, lds, 0, kw - KSTAGE, kw2 - KSTAGE, vw0 - VSTAGE, vw1 - VSTAGE);
   __syncthreads();
-  if (n_stages > 1) load_stage(regs, K1, K2, V, BC, N, tid);
-  qk_tile(A, smem, smem + K_TILE, koff, 0, qf1, qf2);
+  if (n_stages > 1) load_stage(regs, rs, BC, kvo, vvo);
+  qk_tile(A, lds, kcur, 0, qf1, qf2);
   if (n_full == 0) mask_tile(A, 0, qrow, h);
   {
     float t1, t2;
@@ -354,16 +401,15 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     maybe_rescale(t1, t2, m1, m2, l1, l2, acc1, acc2);
   }
   int s = 0;
-  for (; s + 1 < n_full; ++s) stage(NoMask{}, s);
-  for (; s + 1 < n_stages; ++s) stage(Mask{}, s);
+  for (; s + 1 < n_full; ++s) stage(NoMask{}, s);   // stages wholly below the query tile
+  for (; s + 1 < n_stages; ++s) stage(Mask{}, s);   // at most two touching the diagonal
   {
     // Last stage: sub-tiles 2s and 2s+1, nothing further to fetch.
-    const bf16_t* bs = smem + (s % NBUF) * STAGE;
-    step(Mask{}, A, B, bs, 1, bs, 0, 2 * s + 1);
+    step(Mask{}, A, B, kcur, 32 * 128, vcur, 0, 2 * s + 1);
     bf16x8 p1a, p1b, p2a, p2b;
     exp_tile(B.s1, c, m1, l1, p1a, p1b);
     exp_tile(B.s2, c, m2, l2, p2a, p2b);
-    pv_tile(acc1, acc2, bs, voff, 1, p1a, p1b, p2a, p2b);
+    pv_tile(acc1, acc2, lds, vcur, 2 * VBLK, p1a, p1b, p2a, p2b);
   }
 
   // Epilogue: combine the two lane halves' normalisers, form O, RMSNorm, scale, store.
@@ -429,17 +475,15 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const int64_t BH = a.B * a.H;
   const int nqb = static_cast<int>((a.N + BR - 1) / BR);
   const int64_t nblk = BH * nqb;
-  const size_t lds = static_cast<size_t>(NBUF) * STAGE * sizeof(bf16_t);
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   const diffattn_saved& sv = a.saved;
-  hipLaunchKernelGGL(fwd_bf16_kernel, dim3(static_cast<unsigned>(nblk)), dim3(NT), lds, s,
+  hipLaunchKernelGGL(fwd_bf16_kernel, dim3(static_cast<unsigned>(nblk)), dim3(NT), LDS_BYTES, s,
                      static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
                      static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
                      static_cast<const bf16_t*>(a.v), a.lam, a.rms_weight,
