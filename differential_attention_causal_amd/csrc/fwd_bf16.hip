@@ -15,60 +15,62 @@
 // O = acc1 / l1 - lambda acc2 / l2 formed, normalised and scaled. That is exact in real
 // arithmetic; nothing is approximated.
 //
-// Work decomposition (one workgroup = 4 wavefronts = 128 query rows of one (b, h)):
+// Work decomposition: one workgroup = 8 wavefronts = 256 query rows of one (b, h), two
+// wavefronts per SIMD so that one wave's softmax (vector ALU) overlaps the other's
+// matrix-core work.
 //  * each wavefront owns 32 query rows and computes the transposed score tile
 //    S^T = K Q^T (32 keys x 32 queries) with v_mfma_f32_32x32x16_bf16, so each lane
 //    holds 16 scores of ONE query; the row max needs one exchange with lane ^ 32;
-//  * the key rows fed to the MFMA are permuted (bits 2 and 3 of the row swapped) so
-//    that the score registers are directly the B operand of O^T += V^T P^T, with each
-//    lane's 8 keys contiguous in the transposed V tile;
-//  * K1, K2 (64 keys x 64) and V^T tiles go through a ring of three LDS stages with one
-//    barrier per 64 keys; V is transposed in registers on its way to LDS. Every LDS
-//    operand read is a per-lane base register plus a compile-time offset (the stage loop
-//    is unrolled over the ring), and the layouts keep those reads and the transposing
-//    writes free of bank conflicts;
-//  * software pipeline per 32-key sub-tile: the QK^T MFMAs of the next sub-tile are
-//    issued with the exponentials of the current one, and its PV MFMAs with the next
-//    sub-tile's row maxima;
-//  * the running max moves lazily (see maybe_rescale), so the 256 accumulator registers
-//    are rescaled only a handful of times per row;
-//  * stages wholly below the query tile run without mask code; the last two stages apply
-//    the causal predicate key <= query as an integer compare. Keys beyond N are clamped
-//    loads that the same predicate masks; rows beyond N are not stored;
+//  * the key rows fed to the MFMA are permuted (bits 2 and 3 of the row swapped) so that
+//    the score registers are directly the B operand of O^T += V^T P^T;
+//  * K1, K2 and V tiles of 64 keys go from HBM straight into LDS (buffer loads with the
+//    LDS as destination, double buffered, one barrier per tile). Rows at or beyond N read
+//    as zero. The V^T operand comes out of the row-major V tile with the transposing LDS
+//    read ds_read_b64_tr_b16: in each group of 16 lanes, lane 4a+b receives element b of
+//    the 8 bytes that lanes 4j+a (j = 0..3) addressed; so lane 4j+a of group G points at
+//    key 8(G/2)+j, channels 32 blk + 16(G%2) + 4a .. +3, and every MFMA lane ends up with
+//    8 consecutive keys of one channel;
+//  * LDS swizzles keep every operand read free of bank conflicts; operand addresses are a
+//    per-lane base plus compile-time offsets;
+//  * the running max moves lazily (see maybe_rescale), so the accumulators are rescaled
+//    only a handful of times per row;
+//  * sub-tiles wholly below a wave's rows run without mask code; the diagonal sub-tile
+//    applies the causal predicate key <= query as an integer compare; later ones are
+//    skipped;
 //  * workgroups run longest-first (the last query tiles have the most keys), and
-//    consecutive workgroup ids take different heads so that the tiles of one head land
-//    on the same XCD (ids are dealt to the 8 XCDs round-robin) and share its L2.
-#include <type_traits>
-
+//    consecutive workgroup ids take different heads so that the tiles of one head land on
+//    the same XCD (ids are dealt to the 8 XCDs round-robin) and share its L2.
 #include "common.h"
 #include "launch.h"
 
 namespace diffattn {
 namespace fwdbf16 {
 
+#define LDS_AS __attribute__((address_space(3)))
+
 constexpr int D = 64;
 constexpr int DV = 128;
-constexpr int BR = 128;       // query rows per workgroup
-constexpr int BC = 64;        // keys per LDS stage
-constexpr int NT = 256;       // threads per workgroup
-constexpr int NBUF = 3;       // LDS ring of stages
+constexpr int NW = 8;         // wavefronts per workgroup
+constexpr int NT = 64 * NW;   // threads per workgroup
+constexpr int BR = 32 * NW;   // query rows per workgroup
+constexpr int BC = 64;        // keys per tile
 
-// LDS layout (bytes): [V^T stage 0..2][K1 stage 0..2][K2 stage 0..2].
-// V^T stage: 4 blocks, one per (32-key half sb, 16-key step t) = block 2 sb + t; a block
-// holds 128 channel rows of 16 keys (32 B), padded by 32 B so the four blocks start in
-// different banks. Inside a row the two 16-byte halves are swapped on bit 2 of the row.
-// K stage: 64 key rows of 128 B; 16-byte unit u of row r is stored at u ^ k_swz(r).
-constexpr int VROW = 32;
-constexpr int VBLK = DV * VROW + 32;          // 4128
-constexpr int VSTAGE = 4 * VBLK;              // 16512
-constexpr int KSTAGE = BC * D * 2;            // 8192
-constexpr int V_BASE = 0;
-constexpr int K1_BASE = NBUF * VSTAGE;        // 49536
-constexpr int K2_BASE = K1_BASE + NBUF * KSTAGE;
-constexpr int LDS_BYTES = K2_BASE + NBUF * KSTAGE;  // 98688
-static_assert(K1_BASE % 16 == 0 && K2_BASE % 16 == 0, "16-byte aligned regions");
+// LDS slot (bytes): K1 [64 keys][128 B] | K2 [64 keys][128 B] | V in 4 regions of 32
+// channels, [64 keys][64 B] each. Two slots.
+constexpr int K1_OFF = 0;
+constexpr int K2_OFF = 8192;
+constexpr int V_OFF = 16384;
+constexpr int SLOT = 32768;
+constexpr int LDS_BYTES = 2 * SLOT;
 
-__device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
+// K rows: 16-byte unit u stored at u ^ k_swz(row). Bits (b0 ^ b2, b1, b3): the 16 rows a
+// group of 16 operand lanes reads land in 16 different bank slots of 256 bytes, and any 8
+// of them in 8 slots of 128 bytes.
+__device__ __forceinline__ int k_swz(int row) {
+  return ((row ^ (row >> 2)) & 1) | (row & 2) | ((row >> 1) & 4);
+}
+// V rows (64 B, four 16-byte chunks): chunk c stored at c ^ v_swz(row).
+__device__ __forceinline__ int v_swz(int row) { return 2 * ((row >> 1) & 1); }
 
 // Physical key (0..31 within a 32-key sub-tile) held in score register j by lane half h.
 __device__ __forceinline__ int key_of(int j, int h) { return 16 * (j >> 3) + 8 * h + (j & 7); }
@@ -77,64 +79,61 @@ __device__ __forceinline__ int perm_row(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-struct StageRegs {
-  u32x4 k1[2], k2[2], v[4];
+constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer, no swizzle
+
+// Per-thread DMA source offsets (bytes, for tile key 0) of the four 1 KB blocks a wave
+// moves per tile: K1 block w and K2 block w (8 key rows each); V blocks w and w + 8
+// (16 key rows of one 32-channel region each; V block i covers region i / 4, rows
+// 16 (i % 4) .. +15, so block w + 8 is the same rows two regions further).
+struct DmaPlan {
+  int k;
+  int v;
 };
 
-// Tile loads are raw buffer loads through a resource descriptor that starts at the
-// stage's first key and covers the rows that remain below N: rows at or beyond N read as
-// zero in hardware (their scores are masked by the causal predicate, key > query for
-// every stored row). The per-thread offsets are constant, so a stage costs no vector ALU
-// work for addressing.
-constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer, no swizzle
+__device__ __forceinline__ DmaPlan dma_plan(int wv, int lane) {
+  DmaPlan p;
+  {
+    const int row = 8 * wv + (lane >> 3), pu = lane & 7;
+    p.k = row * (D * 2) + 16 * (pu ^ k_swz(row));
+  }
+  {
+    const int region = wv >> 2;
+    const int row = 16 * (wv & 3) + (lane >> 2), pc = lane & 3;
+    p.v = row * (DV * 2) + 64 * region + 16 * (pc ^ v_swz(row));
+  }
+  return p;
+}
 
 struct HeadRsrc {
   __amdgpu_buffer_rsrc_t k1, k2, v;
 };
 
-// k0: first key of the stage; kvo / vvo: this thread's constant byte offsets in a K / V
-// tile. The descriptors cover the head's N rows, so rows at or beyond N read as zero.
-__device__ __forceinline__ void load_stage(StageRegs& r, const HeadRsrc& rs, int k0, int kvo,
-                                           int vvo) {
-  // K: 16-byte chunk c = tid + 256 t of the 64 x 128-byte tile (row c / 8, unit c % 8).
-  const int ko = kvo + k0 * (D * 2);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    r.k1[t] = __builtin_amdgcn_raw_buffer_load_b128(rs.k1, ko + 4096 * t, 0, 0);
-    r.k2[t] = __builtin_amdgcn_raw_buffer_load_b128(rs.k2, ko + 4096 * t, 0, 0);
-  }
-  // V: thread (kg = tid % 16, dg = tid / 16) takes keys 4kg..4kg+3, channels 8dg..8dg+7.
-  const int vo = vvo + k0 * (DV * 2);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) r.v[t] = __builtin_amdgcn_raw_buffer_load_b128(rs.v, vo + 256 * t, 0, 0);
-}
-
-// kw / kw2: this thread's K1 / K2 write address in ring slot 0 (chunk tid; chunk
-// tid + 256 is 32 rows further); vw0 / vw1: its V^T write address for channels c < 4 and
-// c >= 4 of its 8 (the 16-byte half flips with bit 2 of the channel row).
-__device__ __forceinline__ void store_stage(const StageRegs& r, char* __restrict__ lds,
-                                            int buf, int kw, int kw2, int vw0, int vw1) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    *reinterpret_cast<u32x4*>(lds + kw + buf * KSTAGE + 4096 * t) = r.k1[t];
-    *reinterpret_cast<u32x4*>(lds + kw2 + buf * KSTAGE + 4096 * t) = r.k2[t];
-  }
-  // Transpose 4 keys x 8 channels to 8 channel rows of 4 keys (8 bytes each). The 16
-  // lanes sharing dg write 16 different 8-byte slots of one row position: no conflicts.
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    // channel c of keys (4kg, 4kg+1) and (4kg+2, 4kg+3), low half = earlier key
-    const uint32_t x0 = r.v[0][c >> 1], x1 = r.v[1][c >> 1];
-    const uint32_t x2 = r.v[2][c >> 1], x3 = r.v[3][c >> 1];
-    const uint32_t lo = (c & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-    const uint32_t hi = (c & 1) ? ((x2 >> 16) | (x3 & 0xffff0000u)) : ((x2 & 0xffffu) | (x3 << 16));
-    u32x2 w = {lo, hi};
-    *reinterpret_cast<u32x2*>(lds + (c < 4 ? vw0 : vw1) + buf * VSTAGE + c * VROW) = w;
-  }
+// Issues this wave's share of tile k0 into LDS slot `slot` (lane l's 16 bytes land at
+// block base + 16 l).
+__device__ __forceinline__ void dma_tile(const HeadRsrc& rs, const DmaPlan& p, char* lds,
+                                         int slot, int k0, int wv) {
+  LDS_AS char* base = (LDS_AS char*)(lds) + slot * SLOT;
+  const int ko = p.k + k0 * (D * 2);
+  const int vo = p.v + k0 * (DV * 2);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k1, (LDS_AS void*)(base + K1_OFF + 1024 * wv), 16, ko, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k2, (LDS_AS void*)(base + K2_OFF + 1024 * wv), 16, ko, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (LDS_AS void*)(base + V_OFF + 1024 * wv), 16, vo, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (LDS_AS void*)(base + V_OFF + 1024 * (wv + 8)), 16,
+                                           vo + 128, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 lds_read8(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+// Keys e = 0..3 of the lane's 8 from the first read, e = 4..7 from rows 4 further.
+__device__ __forceinline__ bf16x8 lds_read_tr(const char* p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * 64));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // ---------------------------------------------------------------------------------
@@ -149,7 +148,7 @@ struct Scores {
 };
 
 // S^T = K Q^T for both maps (8 MFMAs). kaddr: per-lane LDS byte addresses of the K1
-// operand rows for the 4 channel blocks; koff: stage and sub-tile byte offset.
+// operand rows for the 4 channel blocks (slot 0, sub-tile 0); koff: slot and sub-tile.
 __device__ __forceinline__ void qk_tile(Scores& S, const char* lds, const int* kaddr, int koff,
                                         const bf16x8* qf1, const bf16x8* qf2) {
 #pragma unroll
@@ -157,9 +156,8 @@ __device__ __forceinline__ void qk_tile(Scores& S, const char* lds, const int* k
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const char* p = lds + kaddr[kb] + koff;
-    S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(p), qf1[kb], S.s1, 0, 0, 0);
-    S.s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(p + (K2_BASE - K1_BASE)),
-                                                   qf2[kb], S.s2, 0, 0, 0);
+    S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(p + K1_OFF), qf1[kb], S.s1, 0, 0, 0);
+    S.s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(p + K2_OFF), qf2[kb], S.s2, 0, 0, 0);
   }
 }
 
@@ -170,7 +168,7 @@ __device__ __forceinline__ float max16(const f32x16& s) {
   return a;
 }
 
-// Row maxima of a fresh score tile (scaled, log2 domain), merged across lane halves.
+// Row maxima of a score tile (scaled, log2 domain), merged across lane halves.
 __device__ __forceinline__ void tile_max(const Scores& S, float c, float& t1, float& t2) {
   float a = max16(S.s1), b = max16(S.s2);
   a = fmaxf(a, __shfl_xor(a, 32));
@@ -180,33 +178,42 @@ __device__ __forceinline__ void tile_max(const Scores& S, float c, float& t1, fl
 }
 
 // p = exp2(s c - m) for 16 scores; returns the bf16 operands of the two PV k-steps and
-// adds the fp32 weights to l.
+// adds their sum to l. The sum is taken over the bf16-rounded weights, the same values
+// the PV product multiplies, two per v_dot2 against (1, 1).
 __device__ __forceinline__ void exp_tile(const f32x16& s, float c, float m, float& l,
                                          bf16x8& pa, bf16x8& pb) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   f32x8 x, y;
-  float sa = 0.f, sb = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     x[e] = fast_exp2(fmaf(s[e], c, -m));
     y[e] = fast_exp2(fmaf(s[8 + e], c, -m));
-    sa += x[e];
-    sb += y[e];
   }
-  l += sa + sb;
   pa = __builtin_convertvector(x, bf16x8);
   pb = __builtin_convertvector(y, bf16x8);
+  const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  float sa = l, sb = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 a2 = {pa[2 * e], pa[2 * e + 1]};
+    const bf16x2 b2 = {pb[2 * e], pb[2 * e + 1]};
+    sa = __builtin_amdgcn_fdot2_f32_bf16(a2, one, sa, false);
+    sb = __builtin_amdgcn_fdot2_f32_bf16(b2, one, sb, false);
+  }
+  l = sa + sb;
 }
 
-// O^T += V^T P^T for both maps (16 MFMAs). vaddr: per-lane V^T byte address; voff: stage
-// and sub-tile byte offset.
+// O^T += V^T P^T for both maps (16 MFMAs). vaddr: per-lane base of the transposing reads
+// (slot 0, region 0, sub-tile 0); voff: slot and sub-tile offset. Region b is 4096 bytes
+// further, k-step t 16 key rows (1024 bytes).
 __device__ __forceinline__ void pv_tile(f32x16* acc1, f32x16* acc2, const char* lds, int vaddr,
                                         int voff, const bf16x8& p1a, const bf16x8& p1b,
                                         const bf16x8& p2a, const bf16x8& p2b) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const char* p = lds + vaddr + voff + b * 32 * VROW;
-    const bf16x8 va = lds_read8(p);
-    const bf16x8 vb = lds_read8(p + VBLK);
+    const char* p = lds + vaddr + voff + V_OFF + 4096 * b;
+    const bf16x8 va = lds_read_tr(p);
+    const bf16x8 vb = lds_read_tr(p + 1024);
     acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1a, acc1[b], 0, 0, 0);
     acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p2a, acc2[b], 0, 0, 0);
     acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p1b, acc1[b], 0, 0, 0);
@@ -225,9 +232,9 @@ __device__ __forceinline__ void mask_tile(Scores& S, int ks, int q, int h) {
   }
 }
 
-// Lazy max update for the next tile. The branch is taken when some row of the wave grew
-// by more than kTau, but each row moves its own maximum only on its own trigger (the
-// others multiply by exactly 1), so every row's result depends on its own scores only.
+// Lazy max update. The branch is taken when some row of the wave grew by more than
+// kTau, but each row moves its own maximum only on its own trigger (the others multiply
+// by exactly 1), so every row's result depends on its own scores only.
 __device__ __forceinline__ void maybe_rescale(float t1, float t2, float& m1, float& m2,
                                               float& l1, float& l2, f32x16* acc1,
                                               f32x16* acc2) {
@@ -250,21 +257,18 @@ __device__ __forceinline__ void maybe_rescale(float t1, float t2, float& m1, flo
   }
 }
 
-using NoMask = std::integral_constant<bool, false>;
-using Mask = std::integral_constant<bool, true>;
-
-__global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
+__global__ void __launch_bounds__(NT) fwd_bf16_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
     const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
     const bf16_t* __restrict__ v, const diffattn_lambda_state* __restrict__ lamst,
     const float* __restrict__ rms_w, bf16_t* __restrict__ out, float* __restrict__ sv_lse1,
     float* __restrict__ sv_lse2, float* __restrict__ sv_o1, float* __restrict__ sv_o2,
     float* __restrict__ sv_rstd, int BH, int H, int N, int nqb, float eps) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;
   const int h = lane >> 5;
 
@@ -278,9 +282,15 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
 
   const bf16_t* Q1 = q1 + hoff * D;
   const bf16_t* Q2 = q2 + hoff * D;
-  const bf16_t* K1 = k1 + hoff * D;
-  const bf16_t* K2 = k2 + hoff * D;
-  const bf16_t* V = v + hoff * DV;
+  HeadRsrc rs;
+  rs.k1 = __builtin_amdgcn_make_buffer_rsrc((void*)(k1 + hoff * D), 0, N * D * 2, kBufFlags);
+  rs.k2 = __builtin_amdgcn_make_buffer_rsrc((void*)(k2 + hoff * D), 0, N * D * 2, kBufFlags);
+  rs.v = __builtin_amdgcn_make_buffer_rsrc((void*)(v + hoff * DV), 0, N * DV * 2, kBufFlags);
+  const DmaPlan plan = dma_plan(wv, lane);
+
+  const int kend = min(N, q0 + BR);
+  const int n_tiles = (kend + BC - 1) / BC;
+  dma_tile(rs, plan, lds, 0, 0, wv);
 
   // Q^T operand: lane holds query q0w + m, channels 16 kb + 8 h .. + 7.
   bf16x8 qf1[4], qf2[4];
@@ -292,32 +302,20 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
       qf2[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Q2 + q * D + 16 * kb + 8 * h));
     }
   }
-  // Per-lane LDS operand addresses (bytes).
+  // Per-lane LDS operand addresses (bytes, slot 0, sub-tile 0).
   int kaddr[4];
   {
     const int kr = perm_row(m);
     const int ks = k_swz(kr);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) kaddr[kb] = K1_BASE + kr * 128 + 16 * ((2 * kb + h) ^ ks);
+    for (int kb = 0; kb < 4; ++kb) kaddr[kb] = kr * 128 + 16 * ((2 * kb + h) ^ ks);
   }
-  int vaddr = V_BASE + m * VROW + 16 * (h ^ ((m >> 2) & 1));
-  HeadRsrc rs;
-  rs.k1 = __builtin_amdgcn_make_buffer_rsrc((void*)K1, 0, N * D * 2, kBufFlags);
-  rs.k2 = __builtin_amdgcn_make_buffer_rsrc((void*)K2, 0, N * D * 2, kBufFlags);
-  rs.v = __builtin_amdgcn_make_buffer_rsrc((void*)V, 0, N * DV * 2, kBufFlags);
-  // Tile load offsets and LDS write addresses of this thread (see load/store_stage).
-  const int kvo = 16 * tid;
-  const int kgi = tid & 15, dgi = tid >> 4;
-  const int vvo = 4 * kgi * DV * 2 + 16 * dgi;
-  int kw, kw2, vw0, vw1;
+  int vaddr;
   {
-    const int row = tid >> 3, u = tid & 7;
-    kw = K1_BASE + row * 128 + 16 * (u ^ k_swz(row));
-    kw2 = kw + (K2_BASE - K1_BASE);
-    const int blk = kgi >> 2, uu = (kgi >> 1) & 1, half = kgi & 1;
-    const int vb = V_BASE + blk * VBLK + 8 * half + 8 * dgi * VROW;
-    vw0 = vb + 16 * uu;
-    vw1 = vb + 16 * (uu ^ 1);
+    const int G = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
+    const int row = 8 * (G >> 1) + j;                 // + 32 sb + 16 t + 4 (second read)
+    const int cp = 2 * (G & 1) + (a >> 1);
+    vaddr = row * 64 + 16 * (cp ^ v_swz(row)) + 8 * (a & 1);
   }
 
   const float c = kLog2e / 8.0f;  // log2(e) / sqrt(64)
@@ -328,88 +326,37 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc1[b][j] = acc2[b][j] = 0.f;
   }
-
-  const int kend = min(N, q0 + BR);
-  const int n_stages = (kend + BC - 1) / BC;
-  const int n_full = q0 / BC;  // stages whose keys are all < q0: no mask for any row
   const int qrow = q0w + m;
+  // Sub-tiles (32 keys) below this wave's rows need no mask; sub-tile `diag` holds the
+  // diagonal; later ones are skipped.
+  const int diag = q0w / 32;
 
-  // One pipeline step: QK^T of the next sub-tile (K operand bases kb + byte offset
-  // kofs) while the current tile's exponentials are formed, then PV of the current tile
-  // (V^T base vb + byte offset vofs) while the next tile's row maxima are taken.
-  auto step = [&](auto mask_tag, Scores& cur, Scores& nxt, const int* kb, int kofs, int vb,
-                  int vofs, int nt) __attribute__((always_inline)) {
-    constexpr bool kMask = decltype(mask_tag)::value;
-    qk_tile(nxt, lds, kb, kofs, qf1, qf2);
-    bf16x8 p1a, p1b, p2a, p2b;
-    exp_tile(cur.s1, c, m1, l1, p1a, p1b);
-    exp_tile(cur.s2, c, m2, l2, p2a, p2b);
-    if (kMask) mask_tile(nxt, 32 * nt, qrow, h);
-    pv_tile(acc1, acc2, lds, vb, vofs, p1a, p1b, p2a, p2b);
-    float t1, t2;
-    tile_max(nxt, c, t1, t2);
-    maybe_rescale(t1, t2, m1, m2, l1, l2, acc1, acc2);
-  };
-  // The per-lane LDS bases follow the ring: kcur / vcur address ring slot s % 3 (the
-  // stage being consumed) and kw.. the slot (s + 1) % 3 being filled; each advances by
-  // one slot per stage, wrapping after three.
-  int kcur[4] = {kaddr[0], kaddr[1], kaddr[2], kaddr[3]};
-  int vcur = vaddr;
-  kw += KSTAGE;
-  kw2 += KSTAGE;
-  vw0 += VSTAGE;
-  vw1 += VSTAGE;
-  int slot = 0;
-  // Stage s: sub-tiles 2s (in A) and 2s+1, and the QK^T of sub-tile 2s+2 (stage s+1).
-  // Stage s+1 was fetched into registers when stage s opened; it is written to its slot
-  // here, opened at the barrier, and stage s+2 is fetched.
-  Scores A, B;
-  StageRegs regs;
-  auto stage = [&](auto mask_tag, int s) __attribute__((always_inline)) {
-    const int kstep = slot == 2 ? -2 * KSTAGE : KSTAGE;
-    const int vstep = slot == 2 ? -2 * VSTAGE : VSTAGE;
-    const int wk = slot == 1 ? -2 * KSTAGE : KSTAGE;   // the filled slot is one ahead
-    const int wv = slot == 1 ? -2 * VSTAGE : VSTAGE;
-    int knext[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) knext[i] = kcur[i] + kstep;
-    step(mask_tag, A, B, kcur, 32 * 128, vcur, 0, 2 * s + 1);
-    store_stage(regs, lds, 0, kw, kw2, vw0, vw1);
-    __syncthreads();
-    if (s + 2 < n_stages) load_stage(regs, rs, (s + 2) * BC, kvo, vvo);
-    step(mask_tag, B, A, knext, 0, vcur, 2 * VBLK, 2 * s + 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kcur[i] = knext[i];
-    vcur += vstep;
-    kw += wk;
-    kw2 += wk;
-    vw0 += wv;
-    vw1 += wv;
-    slot = slot == 2 ? 0 : slot + 1;
-  };
-
-  // Prologue: stage 0 resident, stage 1 in flight, scores and max of sub-tile 0.
-  load_stage(regs, rs, 0, kvo, vvo);
-  store_stage(regs, lds, 0, kw - KSTAGE, kw2 - KSTAGE, vw0 - VSTAGE, vw1 - VSTAGE);
-  __syncthreads();
-  if (n_stages > 1) load_stage(regs, rs, BC, kvo, vvo);
-  qk_tile(A, lds, kcur, 0, qf1, qf2);
-  if (n_full == 0) mask_tile(A, 0, qrow, h);
-  {
-    float t1, t2;
-    tile_max(A, c, t1, t2);
-    maybe_rescale(t1, t2, m1, m2, l1, l2, acc1, acc2);
-  }
-  int s = 0;
-  for (; s + 1 < n_full; ++s) stage(NoMask{}, s);   // stages wholly below the query tile
-  for (; s + 1 < n_stages; ++s) stage(Mask{}, s);   // at most two touching the diagonal
-  {
-    // Last stage: sub-tiles 2s and 2s+1, nothing further to fetch.
-    step(Mask{}, A, B, kcur, 32 * 128, vcur, 0, 2 * s + 1);
-    bf16x8 p1a, p1b, p2a, p2b;
-    exp_tile(B.s1, c, m1, l1, p1a, p1b);
-    exp_tile(B.s2, c, m2, l2, p2a, p2b);
-    pv_tile(acc1, acc2, lds, vcur, 2 * VBLK, p1a, p1b, p2a, p2b);
+  // One loop over 32-key sub-tiles with a single copy of the body. The operand bases
+  // follow the tile: sub-tile jt lives in slot (jt / 2) % 2 at half jt % 2.
+  const int n_sub = min(2 * n_tiles, diag + 1);
+  int koff = 0, voff = 0;
+  for (int jt = 0; jt < 2 * n_tiles; ++jt) {
+    const int t = jt >> 1;
+    if ((jt & 1) == 0) {
+      __syncthreads();  // tile t resident (each wave waited for its own loads); other slot free
+      if (t + 1 < n_tiles) dma_tile(rs, plan, lds, (t + 1) & 1, (t + 1) * BC, wv);
+    }
+    if (jt < n_sub) {
+      Scores S;
+      qk_tile(S, lds, kaddr, koff, qf1, qf2);
+      if (jt == diag) mask_tile(S, 32 * jt, qrow, h);
+      float t1, t2;
+      tile_max(S, c, t1, t2);
+      maybe_rescale(t1, t2, m1, m2, l1, l2, acc1, acc2);
+      bf16x8 p1a, p1b, p2a, p2b;
+      exp_tile(S.s1, c, m1, l1, p1a, p1b);
+      exp_tile(S.s2, c, m2, l2, p2a, p2b);
+      pv_tile(acc1, acc2, lds, vaddr, voff, p1a, p1b, p2a, p2b);
+    }
+    // next sub-tile: other half of this slot, or first half of the other slot
+    const int nt = (jt + 1) >> 1;
+    koff = (nt & 1) * SLOT + ((jt + 1) & 1) * (32 * 128);
+    voff = (nt & 1) * SLOT + ((jt + 1) & 1) * (32 * 64);
   }
 
   // Epilogue: combine the two lane halves' normalisers, form O, RMSNorm, scale, store.
@@ -475,15 +422,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const int64_t BH = a.B * a.H;
   const int nqb = static_cast<int>((a.N + BR - 1) / BR);
   const int64_t nblk = BH * nqb;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
   const diffattn_saved& sv = a.saved;
-  hipLaunchKernelGGL(fwd_bf16_kernel, dim3(static_cast<unsigned>(nblk)), dim3(NT), LDS_BYTES, s,
+  hipLaunchKernelGGL(fwd_bf16_kernel, dim3(static_cast<unsigned>(nblk)), dim3(NT), 0, s,
                      static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
                      static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
                      static_cast<const bf16_t*>(a.v), a.lam, a.rms_weight,
