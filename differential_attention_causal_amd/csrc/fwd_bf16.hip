@@ -15,9 +15,10 @@
 // O = acc1 / l1 - lambda acc2 / l2 formed, normalised and scaled. That is exact in real
 // arithmetic; nothing is approximated.
 //
-// Work decomposition: one workgroup = 8 wavefronts = 256 query rows of one (b, h), two
-// wavefronts per SIMD so that one wave's softmax (vector ALU) overlaps the other's
-// matrix-core work.
+// Work decomposition: one workgroup = 4 wavefronts = 128 query rows of one (b, h); two
+// workgroups per CU, so each SIMD runs two wavefronts from different workgroups and one
+// wave's softmax (vector ALU) overlaps the other's matrix-core work without the two
+// being held in step by a shared barrier.
 //  * each wavefront owns 32 query rows and computes the transposed score tile
 //    S^T = K Q^T (32 keys x 32 queries) with v_mfma_f32_32x32x16_bf16, so each lane
 //    holds 16 scores of ONE query; the row max needs one exchange with lane ^ 32;
@@ -50,18 +51,31 @@ namespace fwdbf16 {
 
 constexpr int D = 64;
 constexpr int DV = 128;
-constexpr int NW = 8;         // wavefronts per workgroup
+#ifndef DIFFATTN_FWD_WAVES
+#define DIFFATTN_FWD_WAVES 4
+#endif
+// Wavefronts per workgroup. With 4, two workgroups share each CU (two waves per SIMD from
+// different workgroups, so their barriers do not keep them in step).
+constexpr int NW = DIFFATTN_FWD_WAVES;
 constexpr int NT = 64 * NW;   // threads per workgroup
 constexpr int BR = 32 * NW;   // query rows per workgroup
-constexpr int BC = 64;        // keys per tile
+#ifndef DIFFATTN_FWD_TILE
+#define DIFFATTN_FWD_TILE 64
+#endif
+constexpr int BC = DIFFATTN_FWD_TILE;  // keys per LDS tile (one barrier per tile)
 
-// LDS slot (bytes): K1 [64 keys][128 B] | K2 [64 keys][128 B] | V in 4 regions of 32
-// channels, [64 keys][64 B] each. Two slots.
+// LDS slot (bytes): K1 [BC keys][128 B] | K2 [BC keys][128 B] | V in 4 regions of 32
+// channels, [BC keys][64 B] each. Two slots.
+constexpr int KTILE = BC * 128;
+constexpr int VREG = BC * 64;
 constexpr int K1_OFF = 0;
-constexpr int K2_OFF = 8192;
-constexpr int V_OFF = 16384;
-constexpr int SLOT = 32768;
+constexpr int K2_OFF = KTILE;
+constexpr int V_OFF = 2 * KTILE;
+constexpr int SLOT = 2 * KTILE + 4 * VREG;
 constexpr int LDS_BYTES = 2 * SLOT;
+constexpr int KBLK = BC / (8 * NW);   // 1 KB K1 (and K2) blocks per wave per tile
+constexpr int VBLK = BC / (4 * NW);   // 1 KB V blocks per wave per tile
+static_assert(BC % 64 == 0, "tile of 64-key multiples");
 
 // K rows: 16-byte unit u stored at u ^ k_swz(row). Bits (b0 ^ b2, b1, b3): the 16 rows a
 // group of 16 operand lanes reads land in 16 different bank slots of 256 bytes, and any 8
@@ -81,25 +95,28 @@ __device__ __forceinline__ int perm_row(int m) {
 
 constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer, no swizzle
 
-// Per-thread DMA source offsets (bytes, for tile key 0) of the four 1 KB blocks a wave
-// moves per tile: K1 block w and K2 block w (8 key rows each); V blocks w and w + 8
-// (16 key rows of one 32-channel region each; V block i covers region i / 4, rows
-// 16 (i % 4) .. +15, so block w + 8 is the same rows two regions further).
+// Per-thread DMA source offsets (bytes, for tile key 0). K1 (and K2) block i holds key
+// rows 8i .. 8i+7; wave w moves blocks w + NW r. V block i holds rows 16 (i % (BC/16)) ..
+// +15 of region i / (BC/16); wave w moves blocks w + NW r. The swizzles depend only on
+// the low row bits, which the blocks of one wave share.
 struct DmaPlan {
-  int k;
-  int v;
+  int k[KBLK];
+  int v[VBLK];
 };
 
 __device__ __forceinline__ DmaPlan dma_plan(int wv, int lane) {
   DmaPlan p;
-  {
-    const int row = 8 * wv + (lane >> 3), pu = lane & 7;
-    p.k = row * (D * 2) + 16 * (pu ^ k_swz(row));
+#pragma unroll
+  for (int r = 0; r < KBLK; ++r) {
+    const int row = 8 * (wv + NW * r) + (lane >> 3), pu = lane & 7;
+    p.k[r] = row * (D * 2) + 16 * (pu ^ k_swz(row));
   }
-  {
-    const int region = wv >> 2;
-    const int row = 16 * (wv & 3) + (lane >> 2), pc = lane & 3;
-    p.v = row * (DV * 2) + 64 * region + 16 * (pc ^ v_swz(row));
+#pragma unroll
+  for (int r = 0; r < VBLK; ++r) {
+    const int i = wv + NW * r;
+    const int region = i / (BC / 16);
+    const int row = 16 * (i % (BC / 16)) + (lane >> 2), pc = lane & 3;
+    p.v[r] = row * (DV * 2) + 64 * region + 16 * (pc ^ v_swz(row));
   }
   return p;
 }
@@ -113,27 +130,65 @@ struct HeadRsrc {
 __device__ __forceinline__ void dma_tile(const HeadRsrc& rs, const DmaPlan& p, char* lds,
                                          int slot, int k0, int wv) {
   LDS_AS char* base = (LDS_AS char*)(lds) + slot * SLOT;
-  const int ko = p.k + k0 * (D * 2);
-  const int vo = p.v + k0 * (DV * 2);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k1, (LDS_AS void*)(base + K1_OFF + 1024 * wv), 16, ko, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k2, (LDS_AS void*)(base + K2_OFF + 1024 * wv), 16, ko, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (LDS_AS void*)(base + V_OFF + 1024 * wv), 16, vo, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (LDS_AS void*)(base + V_OFF + 1024 * (wv + 8)), 16,
-                                           vo + 128, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < KBLK; ++r) {
+    const int ko = p.k[r] + k0 * (D * 2);
+    LDS_AS char* dst = base + 1024 * (wv + NW * r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k1, (LDS_AS void*)(dst + K1_OFF), 16, ko, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k2, (LDS_AS void*)(dst + K2_OFF), 16, ko, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < VBLK; ++r) {
+    LDS_AS char* dst = base + V_OFF + 1024 * (wv + NW * r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (LDS_AS void*)(dst), 16, p.v[r] + k0 * (DV * 2), 0, 0, 0);
+  }
 }
 
 __device__ __forceinline__ bf16x8 lds_read8(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-// Keys e = 0..3 of the lane's 8 from the first read, e = 4..7 from rows 4 further.
-__device__ __forceinline__ bf16x8 lds_read_tr(const char* p) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * 64));
-  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
+// The V^T operand reads are issued as inline assembly: the compiler cannot tell that a
+// transposing LDS read does not overlap the tile being fetched into the other LDS slot,
+// and would otherwise wait for that fetch before every read. Their completion is awaited
+// explicitly (vt_wait) before the PV products, tied to the registers they fill.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16(int addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+
+// The 16 reads of one sub-tile: for region b and k-step t, keys e = 0..3 of the lane's 8
+// and (4 rows further) e = 4..7.
+struct VtRegs {
+  u32x2 r[4][2][2];
+};
+
+template <int B, int T>
+__device__ __forceinline__ void vt_issue_bt(VtRegs& v, int addr) {
+  v.r[B][T][0] = ds_read_tr16<V_OFF + VREG * B + 1024 * T>(addr);
+  v.r[B][T][1] = ds_read_tr16<V_OFF + VREG * B + 1024 * T + 4 * 64>(addr);
+}
+
+__device__ __forceinline__ void vt_issue(VtRegs& v, int addr) {
+  vt_issue_bt<0, 0>(v, addr); vt_issue_bt<0, 1>(v, addr);
+  vt_issue_bt<1, 0>(v, addr); vt_issue_bt<1, 1>(v, addr);
+  vt_issue_bt<2, 0>(v, addr); vt_issue_bt<2, 1>(v, addr);
+  vt_issue_bt<3, 0>(v, addr); vt_issue_bt<3, 1>(v, addr);
+}
+
+__device__ __forceinline__ void vt_wait(VtRegs& v) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v.r[0][0][0]), "+v"(v.r[0][0][1]), "+v"(v.r[0][1][0]), "+v"(v.r[0][1][1]),
+                 "+v"(v.r[1][0][0]), "+v"(v.r[1][0][1]), "+v"(v.r[1][1][0]), "+v"(v.r[1][1][1]),
+                 "+v"(v.r[2][0][0]), "+v"(v.r[2][0][1]), "+v"(v.r[2][1][0]), "+v"(v.r[2][1][1]),
+                 "+v"(v.r[3][0][0]), "+v"(v.r[3][0][1]), "+v"(v.r[3][1][0]), "+v"(v.r[3][1][1]));
+}
+
+__device__ __forceinline__ bf16x8 vt_operand(const VtRegs& v, int b, int t) {
+  const u32x4 x = {v.r[b][t][0][0], v.r[b][t][0][1], v.r[b][t][1][0], v.r[b][t][1][1]};
+  return __builtin_bit_cast(bf16x8, x);
 }
 
 // ---------------------------------------------------------------------------------
@@ -168,11 +223,19 @@ __device__ __forceinline__ float max16(const f32x16& s) {
   return a;
 }
 
+// max(x[l], x[l ^ 32]): v_permlane32_swap exchanges the upper half of its first operand
+// with the lower half of its second, so with x in both the two results hold x[l] and
+// x[l ^ 32] in every lane.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Row maxima of a score tile (scaled, log2 domain), merged across lane halves.
 __device__ __forceinline__ void tile_max(const Scores& S, float c, float& t1, float& t2) {
   float a = max16(S.s1), b = max16(S.s2);
-  a = fmaxf(a, __shfl_xor(a, 32));
-  b = fmaxf(b, __shfl_xor(b, 32));
+  a = max_halves(a);
+  b = max_halves(b);
   t1 = a * c;
   t2 = b * c;
 }
@@ -203,17 +266,14 @@ __device__ __forceinline__ void exp_tile(const f32x16& s, float c, float m, floa
   l = sa + sb;
 }
 
-// O^T += V^T P^T for both maps (16 MFMAs). vaddr: per-lane base of the transposing reads
-// (slot 0, region 0, sub-tile 0); voff: slot and sub-tile offset. Region b is 4096 bytes
-// further, k-step t 16 key rows (1024 bytes).
-__device__ __forceinline__ void pv_tile(f32x16* acc1, f32x16* acc2, const char* lds, int vaddr,
-                                        int voff, const bf16x8& p1a, const bf16x8& p1b,
+// O^T += V^T P^T for both maps (16 MFMAs), from the V^T operands already read.
+__device__ __forceinline__ void pv_tile(f32x16* acc1, f32x16* acc2, const VtRegs& vt,
+                                        const bf16x8& p1a, const bf16x8& p1b,
                                         const bf16x8& p2a, const bf16x8& p2b) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const char* p = lds + vaddr + voff + V_OFF + 4096 * b;
-    const bf16x8 va = lds_read_tr(p);
-    const bf16x8 vb = lds_read_tr(p + 1024);
+    const bf16x8 va = vt_operand(vt, b, 0);
+    const bf16x8 vb = vt_operand(vt, b, 1);
     acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1a, acc1[b], 0, 0, 0);
     acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p2a, acc2[b], 0, 0, 0);
     acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p1b, acc1[b], 0, 0, 0);
@@ -257,7 +317,7 @@ __device__ __forceinline__ void maybe_rescale(float t1, float t2, float& m1, flo
   }
 }
 
-__global__ void __launch_bounds__(NT) fwd_bf16_kernel(
+__global__ void __launch_bounds__(NT, 8 / NW) fwd_bf16_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
     const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
     const bf16_t* __restrict__ v, const diffattn_lambda_state* __restrict__ lamst,
@@ -318,6 +378,8 @@ __global__ void __launch_bounds__(NT) fwd_bf16_kernel(
     vaddr = row * 64 + 16 * (cp ^ v_swz(row)) + 8 * (a & 1);
   }
 
+  // LDS-relative byte address of the array, for the operands given to inline assembly.
+  const int lds_base = static_cast<int>(reinterpret_cast<uintptr_t>((LDS_AS char*)lds));
   const float c = kLog2e / 8.0f;  // log2(e) / sqrt(64)
   float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
   f32x16 acc1[4], acc2[4];
@@ -333,17 +395,23 @@ __global__ void __launch_bounds__(NT) fwd_bf16_kernel(
 
   // One loop over 32-key sub-tiles with a single copy of the body. The operand bases
   // follow the tile: sub-tile jt lives in slot (jt / 2) % 2 at half jt % 2.
-  const int n_sub = min(2 * n_tiles, diag + 1);
+  constexpr int SPT = BC / 32;  // sub-tiles per tile
+  const int n_sub = min(SPT * n_tiles, diag + 1);
   int koff = 0, voff = 0;
-  for (int jt = 0; jt < 2 * n_tiles; ++jt) {
-    const int t = jt >> 1;
-    if ((jt & 1) == 0) {
-      __syncthreads();  // tile t resident (each wave waited for its own loads); other slot free
+  for (int jt = 0; jt < SPT * n_tiles; ++jt) {
+    const int t = jt / SPT;
+    if (jt % SPT == 0) {
+      // Tile t resident: each wave waits for its own fetch, then all meet; the other slot
+      // is then free for tile t + 1.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
       if (t + 1 < n_tiles) dma_tile(rs, plan, lds, (t + 1) & 1, (t + 1) * BC, wv);
     }
     if (jt < n_sub) {
       Scores S;
       qk_tile(S, lds, kaddr, koff, qf1, qf2);
+      VtRegs vt;
+      vt_issue(vt, lds_base + vaddr + voff);
       if (jt == diag) mask_tile(S, 32 * jt, qrow, h);
       float t1, t2;
       tile_max(S, c, t1, t2);
@@ -351,12 +419,13 @@ __global__ void __launch_bounds__(NT) fwd_bf16_kernel(
       bf16x8 p1a, p1b, p2a, p2b;
       exp_tile(S.s1, c, m1, l1, p1a, p1b);
       exp_tile(S.s2, c, m2, l2, p2a, p2b);
-      pv_tile(acc1, acc2, lds, vaddr, voff, p1a, p1b, p2a, p2b);
+      vt_wait(vt);
+      pv_tile(acc1, acc2, vt, p1a, p1b, p2a, p2b);
     }
-    // next sub-tile: other half of this slot, or first half of the other slot
-    const int nt = (jt + 1) >> 1;
-    koff = (nt & 1) * SLOT + ((jt + 1) & 1) * (32 * 128);
-    voff = (nt & 1) * SLOT + ((jt + 1) & 1) * (32 * 64);
+    // next sub-tile: slot (jt + 1) / SPT % 2, position (jt + 1) % SPT within the tile
+    const int nt = (jt + 1) / SPT, ns = (jt + 1) % SPT;
+    koff = (nt & 1) * SLOT + ns * (32 * 128);
+    voff = (nt & 1) * SLOT + ns * (32 * 64);
   }
 
   // Epilogue: combine the two lane halves' normalisers, form O, RMSNorm, scale, store.
