@@ -11,13 +11,17 @@ Also reported in the same line:
             8192 tokens: HBM GB/s = (cache + query + output bytes) / step time.
   train   - forward (with saves) + backward on B8 H12 N4096 when the backward
             kernels are present: TFLOP/s under 12 d P + 20 d P per head.
+  copy    - a plain 2 GiB device-to-device copy: the HBM rate this machine reaches,
+            and the kernel the HBM byte counters are calibrated on.
   roofline - for the dominant kernel (the forward), achieved TFLOP/s from HIP
             events around each forward launch in the timed region, against the
-            bf16 dense MFMA peak of 2500 TFLOP/s.
+            bf16 dense MFMA peak of 2500 TFLOP/s; traffic = HBM bytes per launch
+            from profiles/hbm_traffic.md when it was measured on the current source.
   cpu_baseline - the float64 oracle on the host cores, on a bounded sample of the
-            forward workload (the last rows of head 0, ~10-30 s of CPU work).
+            forward workload (query rows from the last one down, head by head,
+            ~12 s of CPU work).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs fwd,decode,train]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs fwd,decode,train,copy]
                        [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -101,7 +105,8 @@ def leg_forward(steps, warmup):
         "ms_per_step": ms, "wall_ms_per_step": wall, "tflops": fl / (ms * 1e-3) / 1e12,
         "fwd_kernel_ms": kern_ms, "flops_per_launch": fl,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_from_profiles("fwd_bf16_kernel", "fwd_bf16.hip", w.name)},
         "formula_tflops_8dP": fl * 8.0 / 12.0 / (ms * 1e-3) / 1e12,
     }
 
@@ -133,7 +138,8 @@ def leg_decode(steps, warmup):
         "workload": w.name, "value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
         "ms_per_step": ms, "decode_ms": kern_ms, "bytes_per_step": nb,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+                     "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": traffic_from_profiles("decode_split_kernel", "decode.hip", w.name)},
     }
 
 
@@ -171,8 +177,58 @@ def leg_train(steps, warmup):
     }
 
 
+def leg_copy(steps, warmup):
+    """A plain 2 GiB device-to-device copy: the measured HBM reference, and the kernel the
+    FETCH_SIZE / WRITE_SIZE counters are calibrated on."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev:
+            ev[0].record()
+        b.copy_(a)
+        if ev:
+            ev[1].record()
+
+    ms, wall, inner = time_steps(step, steps, warmup, inner_events=True)
+    kern_ms = sum(inner) / len(inner)
+    return {"bytes_read": 2 * n, "bytes_written": 2 * n,
+            "GB_s": 4 * n / (kern_ms * 1e-3) / 1e9, "copy_ms": kern_ms}
+
+
+def source_hash(source: str) -> str:
+    """sha256 prefix over a kernel's source file and the two headers every kernel includes."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (source, "common.h", "launch.h"):
+        h.update(open(os.path.join(ROOT, "differential_attention_causal_amd", "csrc", f),
+                      "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, source: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from profiles/hbm_traffic.md, if that
+    row was measured on the current source of the kernel (see source_hash); else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    src = os.path.join(ROOT, "differential_attention_causal_amd", "csrc", source)
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    sha = source_hash(source)
+    for line in open(path):
+        cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 6 and cells[0] == kernel and cells[1] == sha and cells[2] == workload:
+            try:
+                return float(cells[5].replace(",", ""))
+            except ValueError:
+                return None
+    return None
+
+
 def cpu_baseline(budget_s: float = 12.0, cap_s: float = 30.0):
-    """The float64 oracle on the host: last rows of head 0 of the forward workload."""
+    """The float64 oracle on the host over a time-bounded sample of the forward workload."""
     import numpy as np
     import torch
     from differential_attention_causal_amd import synth
@@ -185,32 +241,36 @@ def cpu_baseline(budget_s: float = 12.0, cap_s: float = 30.0):
     w = synth.WORKLOADS[3]
     x = synth.make_inputs(w, "cuda:0")
     torch.cuda.synchronize()
-    h = {k: x[k][0, 0].float().cpu().double().numpy() for k in ("q1", "q2", "k1", "k2", "v")}
     lv = {k: x[k].cpu().double().numpy() for k in ("lq1", "lk1", "lq2", "lk2")}
-    del x
     ls = orc.lambda_scalar(lv["lq1"], lv["lk1"], lv["lq2"], lv["lk2"], w.layer)
     n = w.seqlen
-    done_pairs, rows_done, t0 = 0, 0, time.perf_counter()
-    chunk = 128
-    hi = n
-    while hi > 0:
-        lo = max(0, hi - chunk)
-        rows = list(range(lo, hi))
-        orc.forward_rows(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], rows, ls["lambda"],
-                         ls["lambda_init"])
-        done_pairs += sum(i + 1 for i in rows)
-        rows_done += len(rows)
-        hi = lo
-        el = time.perf_counter() - t0
-        if el >= budget_s or el >= cap_s:
+    done_pairs, rows_done, heads_done, t0 = 0, 0, 0, time.perf_counter()
+    chunk = 256
+    for hh in range(w.heads):
+        h = {k: x[k][0, hh].float().cpu().double().numpy() for k in ("q1", "q2", "k1", "k2", "v")}
+        hi = n
+        while hi > 0:
+            lo = max(0, hi - chunk)
+            rows = list(range(lo, hi))
+            orc.forward_rows(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], rows, ls["lambda"],
+                             ls["lambda_init"])
+            done_pairs += sum(i + 1 for i in rows)
+            rows_done += len(rows)
+            hi = lo
+            if time.perf_counter() - t0 >= min(budget_s, cap_s):
+                break
+        heads_done += 1
+        if time.perf_counter() - t0 >= min(budget_s, cap_s):
             break
+    del x
     el = time.perf_counter() - t0
     fl = 12.0 * w.head_dim * done_pairs
     cores = blas_threads or len(os.sched_getaffinity(0))
     return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 oracle forward_rows on the last {rows_done} query rows of head 0 "
-                      f"of B1 H16 N32768 d64 ({done_pairs} causal pairs, {el:.1f} s; "
-                      f"12 d P FLOP convention); host cpus {len(os.sched_getaffinity(0))}"}
+            "sample": f"float64 oracle forward_rows over {rows_done} query rows (heads 0.."
+                      f"{heads_done - 1}, from the last row down) of B1 H16 N32768 d64: "
+                      f"{done_pairs} causal pairs in {el:.1f} s, 12 d P FLOP convention; "
+                      f"host cpus {len(os.sched_getaffinity(0))}"}
 
 
 def main():
@@ -218,7 +278,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="fwd,decode,train")
+    ap.add_argument("--legs", default="fwd,decode,train,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -248,10 +308,9 @@ def main():
     if "decode" in legs:
         rec["decode"] = leg_decode(args.steps, args.warmup)
     if "train" in legs:
-        try:
-            rec["train"] = leg_train(max(1, args.steps // 2), args.warmup)
-        except Exception as e:  # backward not available in this build
-            rec["train"] = {"error": str(e)}
+        rec["train"] = leg_train(max(1, args.steps // 2), args.warmup)
+    if "copy" in legs:
+        rec["copy"] = leg_copy(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
     print(json.dumps(rec))
