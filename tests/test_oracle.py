@@ -355,3 +355,134 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     assert not pins_hold()
     monkeypatch.setattr(orc.math, "sqrt", good_sqrt)
     assert pins_hold()
+
+
+# ---------------------------------------------------------------- planted mistakes in copies
+def _planted_oracle(old, new):
+    """A copy of the whole oracle module with one source substring replaced."""
+    import inspect
+    import types
+    src = inspect.getsource(orc)
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("planted_oracle")
+    exec(compile(src.replace(old, new), "planted_oracle", "exec"), mod.__dict__)
+    return mod
+
+
+def _pin_failures(m):
+    """Runs the independent pins against oracle module `m`; returns the names that fail."""
+    fails = []
+    golden = json.load(open(os.path.join(GOLDEN, "lambda_init_endpoints.json")))
+    r = rng(77)
+    # lambda_init at the page's endpoint, its limit, and the gap to it shrinking by e^-0.3
+    if abs(m.lambda_init(1) - golden["layer_1"]) > 1e-15:
+        fails.append("lambda_init(1)")
+    if abs(m.lambda_init(200) - golden["limit_deep_layers"]) > 1e-15:
+        fails.append("lambda_init limit")
+    gaps = [golden["limit_deep_layers"] - m.lambda_init(l) for l in (3, 4)]
+    if abs(gaps[1] - math.exp(-0.3) * gaps[0]) > 1e-15:
+        fails.append("lambda_init decay")
+    # lambda closed form: a = ln 2 (e^a = 2), b = 0 (e^b = 1) -> lambda = 1 + lambda_init
+    d = 8
+    lq1 = np.zeros(d); lk1 = np.zeros(d); lq1[0] = math.log(2.0); lk1[0] = 1.0
+    st = m.lambda_scalar(lq1, lk1, np.zeros(d), np.zeros(d), 5)
+    if abs(st["lambda"] - (1.0 + m.lambda_init(5))) > 1e-14:
+        fails.append("lambda closed form")
+    # forward: two-map composition of torch's causal attention, on one head
+    n, d = 12, 4
+    q1, q2, k1, k2 = (rand(r, 1, 1, n, d) for _ in range(4))
+    v = rand(r, 1, 1, n, 2 * d)
+    lam, li = 0.37, 0.25
+    y, sv = m.forward(q1, q2, k1, k2, v, lam, li, want_saved=True)
+    ref_o = sdpa_causal(q1, k1, v) - lam * sdpa_causal(q2, k2, v)
+    if not np.allclose(sv["o"], ref_o, rtol=1e-10, atol=1e-12):
+        fails.append("two-map composition")
+    # RMSNorm and scale against torch's rms_norm, at a magnitude where eps matters
+    t = torch.from_numpy(ref_o[0, 0]).double()
+    ref_y = (1 - li) * torch.nn.functional.rms_norm(t, (2 * d,), eps=1e-5).numpy()
+    if not np.allclose(y[0, 0], ref_y, rtol=1e-10, atol=1e-12):
+        fails.append("norm and scale")
+    small = 1e-3 * ref_o[0, 0]
+    ys, _ = m.rms_norm_rows(small)
+    ref_s = torch.nn.functional.rms_norm(torch.from_numpy(small), (2 * d,), eps=1e-5).numpy()
+    if not np.allclose(ys, ref_s, rtol=1e-10, atol=1e-12):
+        fails.append("rmsnorm eps")
+    # row 0 closed form: Y[0] = (1 - li)(1 - lam) V0 / sqrt((1 - lam)^2 mean(V0^2) + eps)
+    v0 = v[0, 0, 0]
+    y0 = (1 - li) * (1 - lam) * v0 / math.sqrt((1 - lam) ** 2 * np.mean(v0 * v0) + 1e-5)
+    if not np.allclose(y[0, 0, 0], y0, rtol=1e-12, atol=1e-14):
+        fails.append("row 0")
+    # lse is the log of the row normaliser
+    s = 1.0 / math.sqrt(d)
+    i = n - 1
+    if abs(sv["lse2"][0, 0, i] - np.log(np.sum(np.exp(s * (k2[0, 0] @ q2[0, 0, i]))))) > 1e-12:
+        fails.append("lse")
+    # decode equals the last row of the prefill over the first len tokens
+    ln = 7
+    yd = m.decode(q1[:, :, ln - 1], q2[:, :, ln - 1], k1, k2, v, np.array([ln]), lam, li)
+    yp = m.forward(q1[:, :, :ln], q2[:, :, :ln], k1[:, :, :ln], k2[:, :, :ln], v[:, :, :ln],
+                   lam, li)
+    if not np.allclose(yd[0, 0], yp[0, 0, ln - 1], rtol=1e-12, atol=1e-14):
+        fails.append("decode")
+    # backward: central finite differences of the module's own forward
+    n, d, H = 5, 3, 2
+    p = {k: rand(r, 1, H, n, d) for k in ("q1", "q2", "k1", "k2")}
+    p["v"] = rand(r, 1, H, n, 2 * d)
+    for k in ("lq1", "lk1", "lq2", "lk2"):
+        p[k] = rand(r, d, scale=0.3)
+    dy = rand(r, 1, H, n, 2 * d)
+    g = m.backward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"], dy, p["lq1"], p["lk1"],
+                   p["lq2"], p["lk2"], 3)
+
+    def loss():
+        st = m.lambda_scalar(p["lq1"], p["lk1"], p["lq2"], p["lk2"], 3)
+        return float(np.sum(m.forward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"],
+                                      st["lambda"], st["lambda_init"]) * dy))
+    h = 1e-6
+    for name in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2"):
+        flat = p[name].reshape(-1)
+        fd = np.empty(flat.size)
+        for j in range(flat.size):
+            old = flat[j]
+            flat[j] = old + h; lp = loss()
+            flat[j] = old - h; lm = loss()
+            flat[j] = old
+            fd[j] = (lp - lm) / (2 * h)
+        an = g["d" + name].reshape(-1)
+        if np.max(np.abs(an - fd)) > 1e-5 * max(np.max(np.abs(fd)), 1e-9):
+            fails.append("fd " + name)
+    return fails
+
+
+def test_pins_hold_on_the_oracle():
+    assert _pin_failures(orc) == []
+
+
+PLANTS = [
+    ("lambda sign", "lam = (ea - eb) + li", "lam = (eb - ea) + li"),
+    ("lambda_init form", "return 0.8 - 0.6 * e", "return 0.8 - 0.6 / e"),
+    ("DiffAttn sign", "o[r0:r1] = (a1 - lam * a2) @ v[:kend]",
+     "o[r0:r1] = (a1 + lam * a2) @ v[:kend]"),
+    ("second map uses K1", "s2 = s * (q2[r0:r1] @ k2[:kend].T)",
+     "s2 = s * (q2[r0:r1] @ k1[:kend].T)"),
+    ("transposed scores", "s1 = s * (q1[r0:r1] @ k1[:kend].T)",
+     "s1 = s * (k1[:kend] @ q1[r0:r1].T)"),
+    ("eps outside the root", "np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)\n    y = o",
+     "(np.sqrt(np.mean(o * o, axis=-1, keepdims=True)) + eps)\n    y = o"),
+    ("scale by lambda_init", "    y = (1.0 - lam_init) * y\n    if want_saved:",
+     "    y = lam_init * y\n    if want_saved:"),
+    ("lse sign", "saved[name][r0:r1] = m + np.log(", "saved[name][r0:r1] = m - np.log("),
+    ("decode length off by one", "n = L if cache_len is None else int(cache_len[b])",
+     "n = L if cache_len is None else int(cache_len[b]) - 1"),
+    ("norm gradient sign", "G = r * g - o * r ** 3", "G = r * g + o * r ** 3"),
+    ("dK transposed", '"dk1": s * ds1.T @ q1', '"dk1": s * ds1 @ q1'),
+    ("dS2 uses A1", "ds2 = a2 * (da2 - np.sum(a2 * da2", "ds2 = a2 * (da2 - np.sum(a1 * da2"),
+    ("dlq2 sign", 'out["dlq2"] = -dlam * st["exp_b"] * lk2', 'out["dlq2"] = dlam * st["exp_b"] * lk2'),
+    ("dlam sign", '"dlam": float(-np.sum(a2 * gv))', '"dlam": float(np.sum(a2 * gv))'),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PLANTS, ids=[p[0] for p in PLANTS])
+def test_planted_mistake_fails_a_pin(name, old, new):
+    m = _planted_oracle(old, new)
+    assert _pin_failures(m), name
