@@ -58,6 +58,10 @@ bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
   return false;
 }
 
+// Longest bf16 sequence of the forward and backward kernels: they address one head's K
+// and V rows through 32-bit buffer offsets (N * 256 bytes for V).
+constexpr int64_t kMaxSeqBf16 = int64_t(1) << 22;
+
 size_t elem_bytes(diffattn_dtype t) { return t == DIFFATTN_FP32 ? 4 : 2; }
 
 // Validates the problem descriptor. Sets *empty when there is nothing to compute.
@@ -108,7 +112,10 @@ size_t diffattn_workspace_bytes(diffattn_op op, const diffattn_problem* p) {
   bool empty = false;
   if (check_problem(p, &empty) != DIFFATTN_OK || empty) return 0;
   switch (op) {
-    case DIFFATTN_OP_FWD: return 0;
+    case DIFFATTN_OP_FWD:
+      return p->dtype == DIFFATTN_BF16
+                 ? diffattn::fwd_bf16_workspace_bytes(p->batch, p->heads, p->seqlen)
+                 : 0;
     case DIFFATTN_OP_DECODE: return decode_ws_bytes(p);
     case DIFFATTN_OP_BWD:
       return diffattn::bwd_workspace_floats(p->batch, p->heads, p->seqlen, p->head_dim) *
@@ -139,8 +146,6 @@ diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const vo
                              const diffattn_lambda_state* lam, const float* rms_weight,
                              void* out, const diffattn_saved* saved, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   bool empty = false;
   diffattn_status st = check_problem(p, &empty);
   if (st != DIFFATTN_OK) return st;
@@ -151,9 +156,13 @@ diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const vo
     if (p->batch * p->heads > 65535) return DIFFATTN_E_UNSUPPORTED;
   } else {
     if (d != 64) return DIFFATTN_E_UNSUPPORTED;
+    if (p->seqlen > kMaxSeqBf16) return DIFFATTN_E_UNSUPPORTED;
   }
   if (empty) return DIFFATTN_OK;
   if (!q1 || !q2 || !k1 || !k2 || !v || !lam || !out) return DIFFATTN_E_ARG;
+  const size_t need = diffattn_workspace_bytes(DIFFATTN_OP_FWD, p);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DIFFATTN_E_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return DIFFATTN_E_ARG;
   const void* ptrs[6] = {q1, q2, k1, k2, v, out};
   for (const void* x : ptrs)
     if (!aligned(x, 16)) return DIFFATTN_E_ARG;
@@ -173,15 +182,16 @@ diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const vo
         !aligned(s.o1, 16) || !aligned(s.o2, 16))
       return DIFFATTN_E_ARG;
     const size_t rb = rows * sizeof(float), ob = rows * 2 * d * sizeof(float);
-    const Span outs[6] = {{out, vb}, {s.lse1, rb}, {s.lse2, rb}, {s.o1, ob}, {s.o2, ob},
-                          {s.rstd, rb}};
-    if (any_overlap(outs, 6, in, 7)) return DIFFATTN_E_ARG;
+    const Span outs[7] = {{out, vb}, {s.lse1, rb}, {s.lse2, rb}, {s.o1, ob}, {s.o2, ob},
+                          {s.rstd, rb}, {workspace, need}};
+    if (any_overlap(outs, 7, in, 7)) return DIFFATTN_E_ARG;
     a.saved = s;
     a.training = true;
   } else {
-    const Span outs[1] = {{out, vb}};
-    if (any_overlap(outs, 1, in, 7)) return DIFFATTN_E_ARG;
+    const Span outs[2] = {{out, vb}, {workspace, need}};
+    if (any_overlap(outs, 2, in, 7)) return DIFFATTN_E_ARG;
   }
+  a.workspace = need > 0 ? workspace : nullptr;
   a.q1 = q1; a.q2 = q2; a.k1 = k1; a.k2 = k2; a.v = v;
   a.lam = lam;
   a.rms_weight = rms_weight;
@@ -252,6 +262,7 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
   diffattn_status st = check_problem(p, &empty);
   if (st != DIFFATTN_OK) return st;
   if (p->dtype != DIFFATTN_BF16 || p->head_dim != 64) return DIFFATTN_E_UNSUPPORTED;
+  if (p->seqlen > kMaxSeqBf16) return DIFFATTN_E_UNSUPPORTED;
   const int d = p->head_dim;
   // The lambda-vector gradients exist even for an empty problem (they are then zero).
   if (!lq1 || !lk1 || !lq2 || !lk2 || !lam || !dlq1 || !dlk1 || !dlq2 || !dlk2)

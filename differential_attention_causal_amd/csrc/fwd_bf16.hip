@@ -15,32 +15,40 @@
 // O = acc1 / l1 - lambda acc2 / l2 formed, normalised and scaled. That is exact in real
 // arithmetic; nothing is approximated.
 //
-// Work decomposition: one workgroup = 4 wavefronts = 128 query rows of one (b, h); two
-// workgroups per CU, so each SIMD runs two wavefronts from different workgroups and one
-// wave's softmax (vector ALU) overlaps the other's matrix-core work without the two
-// being held in step by a shared barrier.
-//  * each wavefront owns 32 query rows and computes the transposed score tile
-//    S^T = K Q^T (32 keys x 32 queries) with v_mfma_f32_32x32x16_bf16, so each lane
-//    holds 16 scores of ONE query; the row max needs one exchange with lane ^ 32;
-//  * the key rows fed to the MFMA are permuted (bits 2 and 3 of the row swapped) so that
-//    the score registers are directly the B operand of O^T += V^T P^T;
+// Work decomposition: one workgroup = 4 wavefronts = 256 query rows of one (b, h), one
+// workgroup per CU and one wavefront per SIMD. A wavefront owns 64 query rows as two
+// groups of 32; its four accumulators (2 maps x 2 groups, 128 x 32 fp32 each) live in
+// the accumulation registers, everything else in the vector registers.
+//  * Transposed score tiles S^T = K Q^T (32 keys x 32 queries per group) with
+//    v_mfma_f32_32x32x16_bf16: each lane holds 16 scores of one query of each group, and
+//    the key rows fed to the MFMA are permuted (bits 2 and 3 swapped) so that the score
+//    registers, packed to bf16, are directly the B operand of O^T += V^T P^T. The two
+//    groups share every K and V^T operand read from LDS.
+//  * Software pipeline over 32-key sub-tiles j, in two half-steps whose matrix work and
+//    vector work are independent, so the wavefront issues one map's softmax between the
+//    other map's MFMAs:
+//      X(j): MFMA  S2(j) = K2 Q2^T,  acc2 += V^T(j-1) P2(j-1)^T
+//            VALU  softmax of S1(j) -> P1(j)
+//      Y(j): MFMA  S1(j+1) = K1 Q1^T, acc1 += V^T(j) P1(j)^T
+//            VALU  softmax of S2(j) -> P2(j)
+//    A map's rescale (when its running max moved) happens between its half-steps, after
+//    the last product into that accumulator and before the next.
+//  * Query rows are dealt to lanes with stride 8 (row 8 m + 2 w + g of the workgroup's
+//    256 for lane column m, wavefront w, group g), so every wavefront and group sees the
+//    same key range: sub-tiles below the workgroup's first row run without mask code and
+//    the 8 sub-tiles of the diagonal block apply the integer predicate key <= query.
 //  * K1, K2 and V tiles of 64 keys go from HBM straight into LDS (buffer loads with the
-//    LDS as destination, double buffered, one barrier per tile). Rows at or beyond N read
-//    as zero. The V^T operand comes out of the row-major V tile with the transposing LDS
-//    read ds_read_b64_tr_b16: in each group of 16 lanes, lane 4a+b receives element b of
-//    the 8 bytes that lanes 4j+a (j = 0..3) addressed; so lane 4j+a of group G points at
-//    key 8(G/2)+j, channels 32 blk + 16(G%2) + 4a .. +3, and every MFMA lane ends up with
-//    8 consecutive keys of one channel;
-//  * LDS swizzles keep every operand read free of bank conflicts; operand addresses are a
-//    per-lane base plus compile-time offsets;
-//  * the running max moves lazily (see maybe_rescale), so the accumulators are rescaled
-//    only a handful of times per row;
-//  * sub-tiles wholly below a wave's rows run without mask code; the diagonal sub-tile
-//    applies the causal predicate key <= query as an integer compare; later ones are
-//    skipped;
-//  * workgroups run longest-first (the last query tiles have the most keys), and
-//    consecutive workgroup ids take different heads so that the tiles of one head land on
-//    the same XCD (ids are dealt to the 8 XCDs round-robin) and share its L2.
+//    LDS as destination) in a ring of 4 slots, two tiles ahead, one barrier per tile.
+//    Rows at or beyond N read as zero. V^T comes out of the row-major V tile with the
+//    transposing read ds_read_b64_tr_b16; LDS swizzles keep every operand read free of
+//    bank conflicts.
+//  * No row maximum on the fast path: weights use the row's current reference m, and a
+//    row only takes the slow path (exact maximum, rescale) when its partial sum leaves
+//    the bound (see kThr); the decision is per row, so every row's result depends on its
+//    own scores only.
+//  * Workgroups run longest-first, and consecutive workgroup ids take different heads so
+//    that the tiles of one head land on the same XCD (ids are dealt to the 8 XCDs
+//    round-robin) and share its L2.
 #include "common.h"
 #include "launch.h"
 
@@ -51,31 +59,25 @@ namespace fwdbf16 {
 
 constexpr int D = 64;
 constexpr int DV = 128;
-#ifndef DIFFATTN_FWD_WAVES
-#define DIFFATTN_FWD_WAVES 4
-#endif
-// Wavefronts per workgroup. With 4, two workgroups share each CU (two waves per SIMD from
-// different workgroups, so their barriers do not keep them in step).
-constexpr int NW = DIFFATTN_FWD_WAVES;
-constexpr int NT = 64 * NW;   // threads per workgroup
-constexpr int BR = 32 * NW;   // query rows per workgroup
-#ifndef DIFFATTN_FWD_TILE
-#define DIFFATTN_FWD_TILE 64
-#endif
-constexpr int BC = DIFFATTN_FWD_TILE;  // keys per LDS tile (one barrier per tile)
+constexpr int NW = 4;          // wavefronts per workgroup (one per SIMD)
+constexpr int NT = 64 * NW;    // threads per workgroup
+constexpr int BR = 64 * NW;    // query rows per workgroup
+constexpr int BC = 64;         // keys per LDS tile
+constexpr int NSLOT = 4;       // LDS ring depth (tiles)
 
 // LDS slot (bytes): K1 [BC keys][128 B] | K2 [BC keys][128 B] | V in 4 regions of 32
-// channels, [BC keys][64 B] each. Two slots.
+// channels, [BC keys][64 B] each.
 constexpr int KTILE = BC * 128;
 constexpr int VREG = BC * 64;
 constexpr int K1_OFF = 0;
 constexpr int K2_OFF = KTILE;
 constexpr int V_OFF = 2 * KTILE;
 constexpr int SLOT = 2 * KTILE + 4 * VREG;
-constexpr int LDS_BYTES = 2 * SLOT;
+constexpr int LDS_BYTES = NSLOT * SLOT;
 constexpr int KBLK = BC / (8 * NW);   // 1 KB K1 (and K2) blocks per wave per tile
 constexpr int VBLK = BC / (4 * NW);   // 1 KB V blocks per wave per tile
-static_assert(BC % 64 == 0, "tile of 64-key multiples");
+constexpr int DMA_PER_TILE = 2 * KBLK + VBLK;   // buffer loads per wave per tile
+static_assert(DMA_PER_TILE == 8, "vmcnt immediates below assume 8 loads per tile");
 
 // K rows: 16-byte unit u stored at u ^ k_swz(row). Bits (b0 ^ b2, b1, b3): the 16 rows a
 // group of 16 operand lanes reads land in 16 different bank slots of 256 bytes, and any 8
@@ -95,63 +97,59 @@ __device__ __forceinline__ int perm_row(int m) {
 
 constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer, no swizzle
 
-// Per-thread DMA source offsets (bytes, for tile key 0). K1 (and K2) block i holds key
-// rows 8i .. 8i+7; wave w moves blocks w + NW r. V block i holds rows 16 (i % (BC/16)) ..
-// +15 of region i / (BC/16); wave w moves blocks w + NW r. The swizzles depend only on
-// the low row bits, which the blocks of one wave share.
-struct DmaPlan {
-  int k[KBLK];
-  int v[VBLK];
-};
-
-__device__ __forceinline__ DmaPlan dma_plan(int wv, int lane) {
-  DmaPlan p;
-#pragma unroll
-  for (int r = 0; r < KBLK; ++r) {
-    const int row = 8 * (wv + NW * r) + (lane >> 3), pu = lane & 7;
-    p.k[r] = row * (D * 2) + 16 * (pu ^ k_swz(row));
-  }
-#pragma unroll
-  for (int r = 0; r < VBLK; ++r) {
-    const int i = wv + NW * r;
-    const int region = i / (BC / 16);
-    const int row = 16 * (i % (BC / 16)) + (lane >> 2), pc = lane & 3;
-    p.v[r] = row * (DV * 2) + 64 * region + 16 * (pc ^ v_swz(row));
-  }
-  return p;
-}
-
+// Issues this wave's share of tile `t` (keys t BC ..) into its ring slot; lane l's 16
+// bytes land at block base + 16 l. K1 (and K2) block i holds key rows 8i .. 8i+7, V
+// block i rows 16 (i % (BC/16)) .. +15 of region i / (BC/16); wave w moves blocks
+// w + NW r. The source offsets are recomputed per tile (they would otherwise hold six
+// vector registers through the loop).
 struct HeadRsrc {
   __amdgpu_buffer_rsrc_t k1, k2, v;
 };
 
-// Issues this wave's share of tile k0 into LDS slot `slot` (lane l's 16 bytes land at
-// block base + 16 l).
-__device__ __forceinline__ void dma_tile(const HeadRsrc& rs, const DmaPlan& p, char* lds,
-                                         int slot, int k0, int wv) {
-  LDS_AS char* base = (LDS_AS char*)(lds) + slot * SLOT;
+__device__ __forceinline__ void dma_tile(const HeadRsrc& rs, char* lds, int t, int wv, int lane) {
+  LDS_AS char* base = (LDS_AS char*)(lds) + (t % NSLOT) * SLOT;
+  const int k0 = t * BC;
 #pragma unroll
   for (int r = 0; r < KBLK; ++r) {
-    const int ko = p.k[r] + k0 * (D * 2);
+    const int row = 8 * (wv + NW * r) + (lane >> 3), pu = lane & 7;
+    const int ko = (k0 + row) * (D * 2) + 16 * (pu ^ k_swz(row));
     LDS_AS char* dst = base + 1024 * (wv + NW * r);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k1, (LDS_AS void*)(dst + K1_OFF), 16, ko, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k2, (LDS_AS void*)(dst + K2_OFF), 16, ko, 0, 0, 0);
   }
 #pragma unroll
   for (int r = 0; r < VBLK; ++r) {
-    LDS_AS char* dst = base + V_OFF + 1024 * (wv + NW * r);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (LDS_AS void*)(dst), 16, p.v[r] + k0 * (DV * 2), 0, 0, 0);
+    const int i = wv + NW * r;
+    const int region = i / (BC / 16);
+    const int row = 16 * (i % (BC / 16)) + (lane >> 2), pc = lane & 3;
+    const int vo = (k0 + row) * (DV * 2) + 64 * region + 16 * (pc ^ v_swz(row));
+    LDS_AS char* dst = base + V_OFF + 1024 * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (LDS_AS void*)(dst), 16, vo, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ bf16x8 lds_read8(const char* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+// Tile t resident in LDS for every wave: this wave's own loads of tile t are complete
+// (only tile t + 1's, issued later, may still be in flight), then all waves meet.
+__device__ __forceinline__ void tile_barrier(bool next_in_flight) {
+  if (next_in_flight) {
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __builtin_amdgcn_s_barrier();
 }
 
-// The V^T operand reads are issued as inline assembly: the compiler cannot tell that a
-// transposing LDS read does not overlap the tile being fetched into the other LDS slot,
-// and would otherwise wait for that fetch before every read. Their completion is awaited
-// explicitly (vt_wait) before the PV products, tied to the registers they fill.
+// ---------------------------------------------------------------------------------
+// LDS operand reads. They are issued as inline assembly and awaited explicitly: the
+// compiler cannot tell that they do not overlap the tiles being fetched into other ring
+// slots and would otherwise wait for those fetches first. Each wait is tied to the
+// registers it completes, so no consumer can be scheduled above it.
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_b128(int addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
 template <int OFF>
 __device__ __forceinline__ u32x2 ds_read_tr16(int addr) {
   u32x2 r;
@@ -159,62 +157,85 @@ __device__ __forceinline__ u32x2 ds_read_tr16(int addr) {
   return r;
 }
 
-// The 16 reads of one sub-tile: for region b and k-step t, keys e = 0..3 of the lane's 8
-// and (4 rows further) e = 4..7.
-struct VtRegs {
-  u32x2 r[4][2][2];
+// K operand of one map for one 32-key sub-tile: 4 channel blocks of 16.
+struct KOps {
+  u32x4 r[4];
 };
+template <int MAP_OFF>
+__device__ __forceinline__ void k_issue(KOps& k, const int* kaddr, int off) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) k.r[kb] = ds_read_b128<MAP_OFF>(kaddr[kb] + off);
+}
+__device__ __forceinline__ bf16x8 k_operand(const KOps& k, int kb) {
+  return __builtin_bit_cast(bf16x8, k.r[kb]);
+}
 
+// V^T operand of one k-step (16 keys) of a sub-tile: for region b, keys e = 0..3 of the
+// lane's 8 and (4 rows further) e = 4..7.
+struct VtHalf {
+  u32x2 r[4][2];
+};
 template <int B, int T>
-__device__ __forceinline__ void vt_issue_bt(VtRegs& v, int addr) {
-  v.r[B][T][0] = ds_read_tr16<V_OFF + VREG * B + 1024 * T>(addr);
-  v.r[B][T][1] = ds_read_tr16<V_OFF + VREG * B + 1024 * T + 4 * 64>(addr);
+__device__ __forceinline__ void vt_issue_b(VtHalf& v, int addr) {
+  v.r[B][0] = ds_read_tr16<V_OFF + VREG * B + 1024 * T>(addr);
+  v.r[B][1] = ds_read_tr16<V_OFF + VREG * B + 1024 * T + 4 * 64>(addr);
 }
-
-__device__ __forceinline__ void vt_issue(VtRegs& v, int addr) {
-  vt_issue_bt<0, 0>(v, addr); vt_issue_bt<0, 1>(v, addr);
-  vt_issue_bt<1, 0>(v, addr); vt_issue_bt<1, 1>(v, addr);
-  vt_issue_bt<2, 0>(v, addr); vt_issue_bt<2, 1>(v, addr);
-  vt_issue_bt<3, 0>(v, addr); vt_issue_bt<3, 1>(v, addr);
+template <int T>
+__device__ __forceinline__ void vt_issue(VtHalf& v, int addr) {
+  vt_issue_b<0, T>(v, addr); vt_issue_b<1, T>(v, addr);
+  vt_issue_b<2, T>(v, addr); vt_issue_b<3, T>(v, addr);
 }
-
-__device__ __forceinline__ void vt_wait(VtRegs& v) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(v.r[0][0][0]), "+v"(v.r[0][0][1]), "+v"(v.r[0][1][0]), "+v"(v.r[0][1][1]),
-                 "+v"(v.r[1][0][0]), "+v"(v.r[1][0][1]), "+v"(v.r[1][1][0]), "+v"(v.r[1][1][1]),
-                 "+v"(v.r[2][0][0]), "+v"(v.r[2][0][1]), "+v"(v.r[2][1][0]), "+v"(v.r[2][1][1]),
-                 "+v"(v.r[3][0][0]), "+v"(v.r[3][0][1]), "+v"(v.r[3][1][0]), "+v"(v.r[3][1][1]));
-}
-
-__device__ __forceinline__ bf16x8 vt_operand(const VtRegs& v, int b, int t) {
-  const u32x4 x = {v.r[b][t][0][0], v.r[b][t][0][1], v.r[b][t][1][0], v.r[b][t][1][1]};
+__device__ __forceinline__ bf16x8 vt_operand(const VtHalf& v, int b) {
+  const u32x4 x = {v.r[b][0][0], v.r[b][0][1], v.r[b][1][0], v.r[b][1][1]};
   return __builtin_bit_cast(bf16x8, x);
 }
 
-// ---------------------------------------------------------------------------------
-// The softmax uses a lazily updated row maximum: m only moves when a new score exceeds
-// it by more than kTau (in log2 units), so the accumulators are rescaled rarely; until
-// then p = exp2(s c - m) <= 2^kTau. The final O = acc / l and the log-sum-exp
-// m + log2(l) do not depend on which m was used.
-constexpr float kTau = 8.0f;
-
-struct Scores {
-  f32x16 s1, s2;
-};
-
-// S^T = K Q^T for both maps (8 MFMAs). kaddr: per-lane LDS byte addresses of the K1
-// operand rows for the 4 channel blocks (slot 0, sub-tile 0); koff: slot and sub-tile.
-__device__ __forceinline__ void qk_tile(Scores& S, const char* lds, const int* kaddr, int koff,
-                                        const bf16x8* qf1, const bf16x8* qf2) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) S.s1[j] = S.s2[j] = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const char* p = lds + kaddr[kb] + koff;
-    S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(p + K1_OFF), qf1[kb], S.s1, 0, 0, 0);
-    S.s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read8(p + K2_OFF), qf2[kb], S.s2, 0, 0, 0);
-  }
+// Waits. Order of issue: V^T k-steps 0 and 1 of a half-step (8 reads each, prefetched
+// during the previous one), then, after the first products, the K rows of the next score
+// tile (4).
+__device__ __forceinline__ void wait_v0(VtHalf& v) {
+  asm volatile("s_waitcnt lgkmcnt(8)"
+               : "+v"(v.r[0][0]), "+v"(v.r[0][1]), "+v"(v.r[1][0]), "+v"(v.r[1][1]),
+                 "+v"(v.r[2][0]), "+v"(v.r[2][1]), "+v"(v.r[3][0]), "+v"(v.r[3][1]));
 }
+__device__ __forceinline__ void wait_v1(VtHalf& v) {
+  asm volatile("s_waitcnt lgkmcnt(4)"
+               : "+v"(v.r[0][0]), "+v"(v.r[0][1]), "+v"(v.r[1][0]), "+v"(v.r[1][1]),
+                 "+v"(v.r[2][0]), "+v"(v.r[2][1]), "+v"(v.r[3][0]), "+v"(v.r[3][1]));
+}
+__device__ __forceinline__ void wait_vt_all(VtHalf (&v)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0].r[0][0]), "+v"(v[0].r[0][1]), "+v"(v[0].r[1][0]), "+v"(v[0].r[1][1]),
+                 "+v"(v[0].r[2][0]), "+v"(v[0].r[2][1]), "+v"(v[0].r[3][0]), "+v"(v[0].r[3][1]),
+                 "+v"(v[1].r[0][0]), "+v"(v[1].r[0][1]), "+v"(v[1].r[1][0]), "+v"(v[1].r[1][1]),
+                 "+v"(v[1].r[2][0]), "+v"(v[1].r[2][1]), "+v"(v[1].r[3][0]), "+v"(v[1].r[3][1]));
+}
+__device__ __forceinline__ void wait_k(KOps& k) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(k.r[0]), "+v"(k.r[1]), "+v"(k.r[2]), "+v"(k.r[3]));
+}
+
+// ---------------------------------------------------------------------------------
+// Softmax with a lazily moved reference m per row (scaled log2 domain): the weights of a
+// sub-tile are p = exp2(s c - m) with the m the row already has, and the row's partial
+// sum of them (its lane's 16 keys) is checked afterwards. Only when that partial exceeds
+// kThr (always on the row's first sub-tile, while m is still kMInit) does the row take
+// the slow path: m moves to the row's exact maximum if that is larger, the row's weights
+// are recomputed, and its accumulator and normaliser are rescaled. Otherwise every
+// weight is at most kThr. The decision and its effect are per row, so each row's result
+// depends on its own scores only; the final O = acc / l and the log-sum-exp m + log2(l)
+// do not depend on which m was used.
+constexpr float kThr = 256.0f;
+// Initial reference: finite, so that the first sub-tile's weights are +inf for visible
+// keys (forcing the slow path) and exactly 0 for masked ones, and no NaN ever arises (the
+// library is built assuming no NaNs, so the threshold test could not see one).
+constexpr float kMInit = -1e30f;
+
+// Per map and group: reference m, this lane's normaliser l (its 16 keys of each sub-tile)
+// and the sub-tile's partial sum lp (added to l once the sub-tile is settled).
+struct RowState {
+  float m, l, lp;
+};
 
 __device__ __forceinline__ float max16(const f32x16& s) {
   float a = fmaxf(s[0], s[1]);
@@ -231,21 +252,17 @@ __device__ __forceinline__ float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Row maxima of a score tile (scaled, log2 domain), merged across lane halves.
-__device__ __forceinline__ void tile_max(const Scores& S, float c, float& t1, float& t2) {
-  float a = max16(S.s1), b = max16(S.s2);
-  a = max_halves(a);
-  b = max_halves(b);
-  t1 = a * c;
-  t2 = b * c;
+// Causal predicate on a sub-tile starting at key ks for query q: key > query -> -inf.
+__device__ __forceinline__ void mask_scores(f32x16& s, int ks, int q, int h) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (ks + key_of(j, h) > q) s[j] = -INFINITY;
+  }
 }
 
-// p = exp2(s c - m) for 16 scores; returns the bf16 operands of the two PV k-steps and
-// adds their sum to l. The sum is taken over the bf16-rounded weights, the same values
-// the PV product multiplies, two per v_dot2 against (1, 1).
-__device__ __forceinline__ void exp_tile(const f32x16& s, float c, float m, float& l,
-                                         bf16x8& pa, bf16x8& pb) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// p = exp2(s c - m) for the 16 scores, packed to the bf16 operands of the two PV k-steps.
+__device__ __forceinline__ void exp_pack(const f32x16& s, float c, float m, bf16x8& pa,
+                                         bf16x8& pb) {
   f32x8 x, y;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -254,8 +271,13 @@ __device__ __forceinline__ void exp_tile(const f32x16& s, float c, float m, floa
   }
   pa = __builtin_convertvector(x, bf16x8);
   pb = __builtin_convertvector(y, bf16x8);
+}
+// Sum of the 16 weights over their bf16-rounded values (the ones the PV product
+// multiplies), two per v_dot2 against (1, 1).
+__device__ __forceinline__ float psum(const bf16x8& pa, const bf16x8& pb) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  float sa = l, sb = 0.f;
+  float sa = 0.f, sb = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const bf16x2 a2 = {pa[2 * e], pa[2 * e + 1]};
@@ -263,68 +285,157 @@ __device__ __forceinline__ void exp_tile(const f32x16& s, float c, float m, floa
     sa = __builtin_amdgcn_fdot2_f32_bf16(a2, one, sa, false);
     sb = __builtin_amdgcn_fdot2_f32_bf16(b2, one, sb, false);
   }
-  l = sa + sb;
+  return sa + sb;
 }
 
-// O^T += V^T P^T for both maps (16 MFMAs), from the V^T operands already read.
-__device__ __forceinline__ void pv_tile(f32x16* acc1, f32x16* acc2, const VtRegs& vt,
-                                        const bf16x8& p1a, const bf16x8& p1b,
-                                        const bf16x8& p2a, const bf16x8& p2b) {
+__device__ __forceinline__ bool over(float lp) { return !(lp <= kThr); }
+
+// Fast path bound: a row keeps the reference m of its first sub-tile, and its weights may
+// grow up to 2^32 (the products and sums stay far inside float range). A partial sum
+// above kBad (including +inf) flags the row for the fixup pass.
+constexpr float kBad = 4294967296.0f;
+__device__ __forceinline__ bool over_bad(float lp) { return lp > kBad; }
+
+// Accumulator registers pass through one vector register to be scaled (read, multiply,
+// write back), so the rare slow path needs almost no vector registers of its own.
+__device__ __forceinline__ float scale_acc(float x, float a) {
+  float t;
+  asm volatile("v_accvgpr_read_b32 %1, %0\n\t"
+               "v_mul_f32 %1, %1, %2\n\t"
+               "v_accvgpr_write_b32 %0, %1"
+               : "+a"(x), "=&v"(t)
+               : "v"(a));
+  return x;
+}
+
+// Slow path for one group (see above): rows whose partial sum is over the threshold
+// move m to their exact maximum when it is larger, recompute their weights and partial
+// sum, and rescale their accumulator column and normaliser. Other rows keep everything
+// (a = 1, their weights unchanged).
+__device__ __forceinline__ void settle_row(const f32x16& s, float c, RowState& st, bf16x8& pa,
+                                           bf16x8& pb, f32x16 (&acc)[4]) {
+  const auto tr = __builtin_amdgcn_permlane32_swap(over(st.lp), over(st.lp), false, false);
+  const bool trig = (tr[0] | tr[1]) != 0;
+  const float t = max_halves(max16(s)) * c;
+  const float mn = (trig && t > st.m) ? t : st.m;
+  const float a = (mn == st.m) ? 1.0f : fast_exp2(st.m - mn);
+  bf16x8 na, nb;
+  exp_pack(s, c, mn, na, nb);
+  const float nlp = psum(na, nb);
+  if (trig) {
+    pa = na;
+    pb = nb;
+    st.lp = nlp;
+  }
+  st.m = mn;
+  st.l *= a;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const bf16x8 va = vt_operand(vt, b, 0);
-    const bf16x8 vb = vt_operand(vt, b, 1);
-    acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1a, acc1[b], 0, 0, 0);
-    acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p2a, acc2[b], 0, 0, 0);
-    acc1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p1b, acc1[b], 0, 0, 0);
-    acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p2b, acc2[b], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[b][j] = scale_acc(acc[b][j], a);
   }
 }
 
-// Causal predicate on a sub-tile starting at key ks: key > query -> -inf.
-__device__ __forceinline__ void mask_tile(Scores& S, int ks, int q, int h) {
+// S^T = K Q^T for one map and both groups (8 MFMAs sharing the K operands). The score
+// products are written as assembly so that their results stay in vector registers while
+// the accumulator products (compiler-visible, below) keep theirs in the accumulation
+// registers. Their consumers are fenced by s_guard. Destinations are early-clobber
+// outputs: a product may not overwrite its own operands.
+__device__ __forceinline__ void qk(f32x16 (&S)[2], const KOps& k, const bf16x8 (&q)[2][4]) {
+  const bf16x8 a0 = k_operand(k, 0);
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S[0]) : "v"(a0), "v"(q[0][0]));
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S[1]) : "v"(a0), "v"(q[1][0]));
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (ks + key_of(j, h) > q) {
-      S.s1[j] = -INFINITY;
-      S.s2[j] = -INFINITY;
-    }
+  for (int kb = 1; kb < 4; ++kb) {
+    const bf16x8 a = k_operand(k, kb);
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S[0]) : "v"(a), "v"(q[0][kb]));
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S[1]) : "v"(a), "v"(q[1][kb]));
+  }
+}
+// One score product; FIRST starts the accumulation from zero. The destination must not
+// share registers with the operands (early clobber): the product writes it while the
+// operands are still being read.
+__device__ __forceinline__ void qk_one(f32x16& S, const bf16x8& a, const bf16x8& q, bool first) {
+  if (first) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S) : "v"(a), "v"(q));
+  } else {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(a), "v"(q));
+  }
+}
+// Wait states between the last score product and any vector access to the scores (more
+// than the 8-pass MFMA's result latency); every consumer depends on this statement.
+__device__ __forceinline__ void s_guard(f32x16 (&S)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 4" : "+v"(S[0]), "+v"(S[1]));
+}
+
+// O^T += V^T P^T for one map, both groups and one k-step (8 MFMAs sharing the V^T
+// operands).
+__device__ __forceinline__ void pv(f32x16 (&acc)[2][4], const VtHalf& vt,
+                                   const bf16x8 (&p)[2][2], int t) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const bf16x8 va = vt_operand(vt, b);
+    acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[0][t], acc[0][b], 0, 0, 0);
+    acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[1][t], acc[1][b], 0, 0, 0);
+  }
+}
+// Keeps the accumulators in the accumulation registers across the loop.
+__device__ __forceinline__ void acc_pin(f32x16 (&acc)[2][4]) {
+  asm volatile(""
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                 "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
+}
+// The softmax results are complete here (keeps them from being sunk past the rescale).
+__device__ __forceinline__ void p_anchor(bf16x8 (&P)[2][2]) {
+  asm volatile("" : "+v"(P[0][0]), "+v"(P[0][1]), "+v"(P[1][0]), "+v"(P[1][1]));
+}
+// MFMA / vector-ALU interleave for the 16 accumulator products of a half-step: each is
+// followed by a few softmax instructions.
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
   }
 }
 
-// Lazy max update. The branch is taken when some row of the wave grew by more than
-// kTau, but each row moves its own maximum only on its own trigger (the others multiply
-// by exactly 1), so every row's result depends on its own scores only.
-__device__ __forceinline__ void maybe_rescale(float t1, float t2, float& m1, float& m2,
-                                              float& l1, float& l2, f32x16* acc1,
-                                              f32x16* acc2) {
-  const bool n1 = t1 > m1 + kTau, n2 = t2 > m2 + kTau;
-  if (__builtin_expect(__any(n1 || n2), 0)) {
-    const float a1 = n1 ? fast_exp2(m1 - t1) : 1.0f;
-    const float a2 = n2 ? fast_exp2(m2 - t2) : 1.0f;
-    m1 = n1 ? t1 : m1;
-    m2 = n2 ? t2 : m2;
-    l1 *= a1;
-    l2 *= a2;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        acc1[b][j] *= a1;
-        acc2[b][j] *= a2;
-      }
-    }
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
+// Calls f(Int<I>{}) for I = A .. B-1, in order, each with a compile-time index.
+template <int A, int B, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (A < B) {
+    f(Int<A>{});
+    static_for<A + 1, B>(f);
   }
 }
 
-__global__ void __launch_bounds__(NT, 8 / NW) fwd_bf16_kernel(
+// LDS byte offsets of sub-tile j's K rows and V rows relative to slot 0, sub-tile 0.
+__device__ __forceinline__ int k_off(int j) { return ((j >> 1) % NSLOT) * SLOT + (j & 1) * (32 * 128); }
+__device__ __forceinline__ int v_off(int j) { return ((j >> 1) % NSLOT) * SLOT + (j & 1) * (32 * 64); }
+
+// SAFE = false: the fast pass (every row block). SAFE = true: the fixup pass, which
+// returns at once unless the fast pass flagged a row of its block in `flags` (8 words per
+// block, block (b h, qb) at words 8 (bh nqb + qb) ..: bit m of word 2 w + g is row
+// 8 m + 2 w + g of the block), and then redoes the block on the checked path and rewrites
+// exactly the flagged rows.
+template <bool SAFE>
+__global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
     const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
     const bf16_t* __restrict__ v, const diffattn_lambda_state* __restrict__ lamst,
     const float* __restrict__ rms_w, bf16_t* __restrict__ out, float* __restrict__ sv_lse1,
     float* __restrict__ sv_lse2, float* __restrict__ sv_o1, float* __restrict__ sv_o2,
-    float* __restrict__ sv_rstd, int BH, int H, int N, int nqb, float eps) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+    float* __restrict__ sv_rstd, uint32_t* __restrict__ flags, int BH, int H, int N, int nqb,
+    float eps) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -332,155 +443,351 @@ __global__ void __launch_bounds__(NT, 8 / NW) fwd_bf16_kernel(
   const int m = lane & 31;
   const int h = lane >> 5;
 
-  // Longest-first over query tiles; consecutive ids walk the heads.
+  // Longest-first over query blocks; consecutive ids walk the heads.
   const int bid = blockIdx.x;
   const int bh = bid % BH;
   const int qb = nqb - 1 - bid / BH;
   const int q0 = qb * BR;
-  const int q0w = q0 + 32 * wv;
   const int64_t hoff = static_cast<int64_t>(bh) * N;
 
-  const bf16_t* Q1 = q1 + hoff * D;
-  const bf16_t* Q2 = q2 + hoff * D;
   HeadRsrc rs;
   rs.k1 = __builtin_amdgcn_make_buffer_rsrc((void*)(k1 + hoff * D), 0, N * D * 2, kBufFlags);
   rs.k2 = __builtin_amdgcn_make_buffer_rsrc((void*)(k2 + hoff * D), 0, N * D * 2, kBufFlags);
   rs.v = __builtin_amdgcn_make_buffer_rsrc((void*)(v + hoff * DV), 0, N * DV * 2, kBufFlags);
-  const DmaPlan plan = dma_plan(wv, lane);
 
-  const int kend = min(N, q0 + BR);
-  const int n_tiles = (kend + BC - 1) / BC;
-  dma_tile(rs, plan, lds, 0, 0, wv);
+  // Every wave walks the same sub-tiles: keys 0 .. q0 + BR - 1 (rows beyond N are
+  // zero-filled and masked). The first jd are wholly below the block's first row.
+  const int n_sub = (q0 + BR) / 32;
+  const int n_tiles = n_sub / 2;
+  const int jd = q0 / 32;
 
-  // Q^T operand: lane holds query q0w + m, channels 16 kb + 8 h .. + 7.
-  bf16x8 qf1[4], qf2[4];
-  {
-    const int q = min(q0w + m, N - 1);
+  // Queries of this lane: group g holds workgroup row 8 m + 2 wv + g.
+  bf16x8 qf1[2][4], qf2[2][4];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int q = min(q0 + 8 * m + 2 * wv + g, N - 1);
+    const bf16_t* Q1 = q1 + (hoff + q) * D;
+    const bf16_t* Q2 = q2 + (hoff + q) * D;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      qf1[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Q1 + q * D + 16 * kb + 8 * h));
-      qf2[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Q2 + q * D + 16 * kb + 8 * h));
+      qf1[g][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Q1 + 16 * kb + 8 * h));
+      qf2[g][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Q2 + 16 * kb + 8 * h));
     }
   }
-  // Per-lane LDS operand addresses (bytes, slot 0, sub-tile 0).
-  int kaddr[4];
+
+  // LDS-relative byte addresses of the operands (slot 0, sub-tile 0).
+  const int lds_base = static_cast<int>(reinterpret_cast<uintptr_t>((LDS_AS char*)lds));
+  int ka[4];
   {
     const int kr = perm_row(m);
     const int ks = k_swz(kr);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) kaddr[kb] = kr * 128 + 16 * ((2 * kb + h) ^ ks);
+    for (int kb = 0; kb < 4; ++kb) ka[kb] = lds_base + kr * 128 + 16 * ((2 * kb + h) ^ ks);
   }
-  int vaddr;
+  int va;
   {
     const int G = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
-    const int row = 8 * (G >> 1) + j;                 // + 32 sb + 16 t + 4 (second read)
+    const int row = 8 * (G >> 1) + j;
     const int cp = 2 * (G & 1) + (a >> 1);
-    vaddr = row * 64 + 16 * (cp ^ v_swz(row)) + 8 * (a & 1);
+    va = lds_base + row * 64 + 16 * (cp ^ v_swz(row)) + 8 * (a & 1);
   }
 
-  // LDS-relative byte address of the array, for the operands given to inline assembly.
-  const int lds_base = static_cast<int>(reinterpret_cast<uintptr_t>((LDS_AS char*)lds));
   const float c = kLog2e / 8.0f;  // log2(e) / sqrt(64)
-  float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
-  f32x16 acc1[4], acc2[4];
+  RowState st1[2], st2[2];
+  f32x16 acc1[2][4], acc2[2][4];
+  f32x16 S1[2], S2[2];
+  bf16x8 P1[2][2], P2[2][2];
+  // V^T operands of the sub-tile the next PV products use.
+  VtHalf vt[2];
+  // Per group: this lane's row left the fast path's bound on some sub-tile (fast pass),
+  // or was flagged by it (fixup pass).
+  uint32_t bad[2] = {0u, 0u};
+  if constexpr (SAFE) {
+    const uint32_t* f = flags + 8 * (static_cast<int64_t>(bh) * nqb + qb);
+    uint32_t any = 0;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+    for (int i = 0; i < 8; ++i) any |= f[i];
+    if (__builtin_amdgcn_readfirstlane(any) == 0) return;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc1[b][j] = acc2[b][j] = 0.f;
-  }
-  const int qrow = q0w + m;
-  // Sub-tiles (32 keys) below this wave's rows need no mask; sub-tile `diag` holds the
-  // diagonal; later ones are skipped.
-  const int diag = q0w / 32;
-
-  // One loop over 32-key sub-tiles with a single copy of the body. The operand bases
-  // follow the tile: sub-tile jt lives in slot (jt / 2) % 2 at half jt % 2.
-  constexpr int SPT = BC / 32;  // sub-tiles per tile
-  const int n_sub = min(SPT * n_tiles, diag + 1);
-  int koff = 0, voff = 0;
-  for (int jt = 0; jt < SPT * n_tiles; ++jt) {
-    const int t = jt / SPT;
-    if (jt % SPT == 0) {
-      // Tile t resident: each wave waits for its own fetch, then all meet; the other slot
-      // is then free for tile t + 1.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (t + 1 < n_tiles) dma_tile(rs, plan, lds, (t + 1) & 1, (t + 1) * BC, wv);
-    }
-    if (jt < n_sub) {
-      Scores S;
-      qk_tile(S, lds, kaddr, koff, qf1, qf2);
-      VtRegs vt;
-      vt_issue(vt, lds_base + vaddr + voff);
-      if (jt == diag) mask_tile(S, 32 * jt, qrow, h);
-      float t1, t2;
-      tile_max(S, c, t1, t2);
-      maybe_rescale(t1, t2, m1, m2, l1, l2, acc1, acc2);
-      bf16x8 p1a, p1b, p2a, p2b;
-      exp_tile(S.s1, c, m1, l1, p1a, p1b);
-      exp_tile(S.s2, c, m2, l2, p2a, p2b);
-      vt_wait(vt);
-      pv_tile(acc1, acc2, vt, p1a, p1b, p2a, p2b);
-    }
-    // next sub-tile: slot (jt + 1) / SPT % 2, position (jt + 1) % SPT within the tile
-    const int nt = (jt + 1) / SPT, ns = (jt + 1) % SPT;
-    koff = (nt & 1) * SLOT + ns * (32 * 128);
-    voff = (nt & 1) * SLOT + ns * (32 * 64);
+    for (int g = 0; g < 2; ++g) bad[g] = (f[2 * wv + g] >> m) & 1u;
   }
 
-  // Epilogue: combine the two lane halves' normalisers, form O, RMSNorm, scale, store.
-  l1 += __shfl_xor(l1, 32);
-  l2 += __shfl_xor(l2, 32);
-  const float lam = lamst->lambda_f;
-  const float g = lamst->one_minus_init_f;
-  const float il1 = 1.0f / l1, il2 = 1.0f / l2;
-  float ss = 0.f;
+  // One half-step, in a fixed order: 24 products (16 accumulator products acc += V^T P^T,
+  // then 8 score products S_next = K Q^T), each followed by a slice of the softmax of
+  // S_cur (sub-tile j, for accumulator acc_cur), software-pipelined over pairs of scores:
+  // fma (scale, subtract m), exp2, pack to bf16, row-sum dot product. The matrix core
+  // thus always has a product queued while the vector unit works. CHECK (fixup pass):
+  // the row sums are tested against kThr and the rare slow path may follow; otherwise
+  // (fast pass) a row's partial sum over kBad only sets its flag, and the loop has no
+  // branch at all. IS_X: the X half-step, which
+  // also prefetches V^T(j) (used by Y(j) and again by X(j + 1)); the Y half-step of an
+  // odd sub-tile holds the tile barrier.
+  auto half = [&](auto masked, auto is_x, auto check, int j, f32x16 (&acc)[2][4],
+                  const bf16x8 (&Pin)[2][2], f32x16 (&S_next)[2], const bf16x8 (&qf)[2][4],
+                  int k_sub, f32x16 (&S_cur)[2], const bf16x8 (&qf_cur)[2][4],
+                  RowState (&st)[2], bf16x8 (&Pout)[2][2], f32x16 (&acc_cur)[2][4])
+      __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    constexpr bool IS_X = decltype(is_x)::value;
+    constexpr bool CHECK = decltype(check)::value;
+    constexpr int KN_OFF = IS_X ? K2_OFF : K1_OFF;   // map of S_next
+    constexpr int KC_OFF = IS_X ? K1_OFF : K2_OFF;   // map of S_cur
+    if (!IS_X) wait_vt_all(vt);
+    KOps kop;
+    float y[32];
+    // Packed weights as separate 32-bit words: kept in a u32x4 and updated element by
+    // element, the dot products below were compiled to read element 0 each time.
+    uint32_t pw[2][2][4];
+    float ssum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    bool slow = false;
+    auto slot = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      // ---- the k-th product
+      if constexpr (k < 16) {
+        constexpr int t = k >> 3, b = (k & 7) >> 1, g = k & 1;
+        acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_operand(vt[t], b), Pin[g][t],
+                                                             acc[g][b], 0, 0, 0);
+      } else {
+        constexpr int kb = (k - 16) >> 1, g = k & 1;
+        qk_one(S_next[g], k_operand(kop, kb), qf[g][kb], kb == 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- work placed behind it
+      if constexpr (k == 0) s_guard(S_cur);
+      if constexpr (k == 2) k_issue<KN_OFF>(kop, ka, k_off(k_sub));
+      static_for<0, 16>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int pr = decltype(pc)::value;
+        constexpr int sa = 2 + pr;
+        constexpr int g = pr >> 3, e = 2 * (pr & 7);
+        if constexpr (k == sa) {          // scale and subtract the reference
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float o1 = acc1[b][j] * il1;
-      const float o2 = acc2[b][j] * il2;
-      acc1[b][j] = o1;
-      acc2[b][j] = o2;
-      const float o = o1 - lam * o2;
-      ss = fmaf(o, o, ss);
-    }
-  }
-  ss += __shfl_xor(ss, 32);
-  const float rstd = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
-  if (qrow < N) {
-    const int hh = bh % H;
-    bf16_t* Y = out + (hoff + qrow) * DV;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int col = 32 * b + 8 * jg + 4 * h;
-        f32x4 w = {1.f, 1.f, 1.f, 1.f};
-        if (rms_w) w = *reinterpret_cast<const f32x4*>(rms_w + hh * DV + col);
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float o = acc1[b][4 * jg + e] - lam * acc2[b][4 * jg + e];
-          y[e] = g * (w[e] * (o * rstd));
+          for (int i = 0; i < 2; ++i) {
+            float sv = S_cur[g][e + i];
+            if (MASKED && 32 * j + key_of(e + i, h) > q0 + 8 * m + 2 * wv + g) sv = -INFINITY;
+            y[16 * g + e + i] = fmaf(sv, c, -st[g].m);
+          }
         }
-        u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-        *reinterpret_cast<u32x2*>(Y + col) = pk;
-        if (sv_o1) {
-          f32x4 a = {acc1[b][4 * jg], acc1[b][4 * jg + 1], acc1[b][4 * jg + 2], acc1[b][4 * jg + 3]};
-          f32x4 bb = {acc2[b][4 * jg], acc2[b][4 * jg + 1], acc2[b][4 * jg + 2], acc2[b][4 * jg + 3]};
-          *reinterpret_cast<f32x4*>(sv_o1 + (hoff + qrow) * DV + col) = a;
-          *reinterpret_cast<f32x4*>(sv_o2 + (hoff + qrow) * DV + col) = bb;
+        if constexpr (k == sa + 1) {      // exp2
+          y[16 * g + e] = fast_exp2(y[16 * g + e]);
+          y[16 * g + e + 1] = fast_exp2(y[16 * g + e + 1]);
+        }
+        if constexpr (k == sa + 2) {      // pack to bf16
+          pw[g][e >> 3][(e & 7) >> 1] = pack_bf16x2(y[16 * g + e], y[16 * g + e + 1]);
+        }
+        if constexpr (k == sa + 3) {      // row-sum dot product
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+          ssum[g][e >> 3] = __builtin_amdgcn_fdot2_f32_bf16(
+              __builtin_bit_cast(bf16x2, pw[g][e >> 3][(e & 7) >> 1]), one, ssum[g][e >> 3], false);
+        }
+      });
+      if constexpr (k == 15) wait_k(kop);
+      if constexpr (k == 21) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) st[g].lp = ssum[g][0] + ssum[g][1];
+      }
+      if constexpr (k == 22) {
+        if constexpr (CHECK) {
+          slow = __any(over(st[0].lp) || over(st[1].lp));
+        } else {
+          bad[0] |= static_cast<uint32_t>(over_bad(st[0].lp));
+          bad[1] |= static_cast<uint32_t>(over_bad(st[1].lp));
+        }
+      }
+      if constexpr (IS_X && k == 16) vt_issue<0>(vt[0], va + v_off(j));
+      if constexpr (IS_X && k == 17) vt_issue<1>(vt[1], va + v_off(j));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    slot(Int<0>{});
+    slot(Int<1>{});
+    if (!IS_X && (j & 1) && ((j + 1) >> 1) < n_tiles) {
+      // tile of sub-tile j + 1 resident before its K1 rows are read (slot 2)
+      const int u = (j + 1) >> 1;
+      tile_barrier(u + 1 < n_tiles);
+      if (u + 2 < n_tiles) dma_tile(rs, lds, u + 2, wv, lane);
+    }
+    static_for<2, 24>(slot);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x4 w4 = {pw[g][hf][0], pw[g][hf][1], pw[g][hf][2], pw[g][hf][3]};
+        Pout[g][hf] = __builtin_bit_cast(bf16x8, w4);
+      }
+    }
+    if constexpr (CHECK) {
+      if (__builtin_expect(slow, 0)) {
+        // Slow path: S_cur again from its K rows (still resident) and Q.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        KOps kc;
+        k_issue<KC_OFF>(kc, ka, k_off(j));
+        wait_k(kc);
+        f32x16 Sr[2];
+        qk(Sr, kc, qf_cur);
+        s_guard(Sr);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          if (MASKED) mask_scores(Sr[g], 32 * j, q0 + 8 * m + 2 * wv + g, h);
+          settle_row(Sr[g], c, st[g], Pout[g][0], Pout[g][1], acc_cur[g]);
         }
       }
     }
-    if (sv_lse1 && h == 0) {
-      // lse_k = ln(sum_j exp(S_kj)) = (m_k + log2 l_k) * ln 2, m_k in the scaled log2 domain.
-      sv_lse1[hoff + qrow] = (m1 + __log2f(l1)) * kLn2;
-      sv_lse2[hoff + qrow] = (m2 + __log2f(l2)) * kLn2;
-      sv_rstd[hoff + qrow] = rstd;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) st[g].l += st[g].lp;
+  };
+
+  auto step = [&](int j, auto masked, auto check) __attribute__((always_inline)) {
+    // X(j): acc2 += V^T(j-1) P2(j-1); S2(j); softmax of S1(j) -> P1.
+    half(masked, Flag<true>{}, check, j, acc2, P2, S2, qf2, j, S1, qf1, st1, P1, acc1);
+    // Y(j): acc1 += V^T(j) P1(j); S1(j+1); softmax of S2(j) -> P2.
+    half(masked, Flag<false>{}, check, j, acc1, P1, S1, qf1, j + 1, S2, qf2, st2, P2, acc2);
+  };
+
+  // The key loop over every sub-tile, from loading tile 0 to the last product. The fast
+  // pass takes each row's reference m from the exact maximum of its first sub-tile (both
+  // maps' first score tiles are formed here once for that) and never branches; the fixup
+  // pass checks every sub-tile.
+  auto run = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      st1[g] = RowState{kMInit, 0.f, 0.f};
+      st2[g] = RowState{kMInit, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc1[g][b][j] = acc2[g][b][j] = 0.f;
+      }
     }
+    acc_pin(acc1);
+    acc_pin(acc2);
+    // Tiles 0 and 1 on their way, tile 0 resident, tile 2 on its way; S1(0).
+    dma_tile(rs, lds, 0, wv, lane);
+    if (n_tiles > 1) dma_tile(rs, lds, 1, wv, lane);
+    tile_barrier(n_tiles > 1);
+    if (n_tiles > 2) dma_tile(rs, lds, 2, wv, lane);
+    {
+      KOps kop;
+      k_issue<K1_OFF>(kop, ka, k_off(0));
+      wait_k(kop);
+      qk(S1, kop, qf1);
+    }
+    if constexpr (!SAFE) {
+      // Reference m of both maps: exact row maxima of sub-tile 0 (masked where the block
+      // starts at key 0).
+      KOps kop;
+      k_issue<K2_OFF>(kop, ka, k_off(0));
+      wait_k(kop);
+      f32x16 T2[2];
+      qk(T2, kop, qf2);
+      s_guard(S1);
+      s_guard(T2);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        f32x16 a = S1[g], b = T2[g];
+        if (jd == 0) {
+          mask_scores(a, 0, q0 + 8 * m + 2 * wv + g, h);
+          mask_scores(b, 0, q0 + 8 * m + 2 * wv + g, h);
+        }
+        st1[g].m = max_halves(max16(a)) * c;
+        st2[g].m = max_halves(max16(b)) * c;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) P2[g][0] = P2[g][1] = bf16x8{};
+    // X(0) multiplies tile 0's V (finite) by P2 = 0.
+    vt_issue<0>(vt[0], va + v_off(0));
+    vt_issue<1>(vt[1], va + v_off(0));
+    wait_vt_all(vt);
+    for (int j = 0; j < jd; ++j) step(j, Flag<false>{}, Flag<SAFE>{});
+    for (int j = jd; j < n_sub; ++j) step(j, Flag<true>{}, Flag<SAFE>{});
+    // Drain: acc2 += V^T(last) P2(last); vt holds V^T(last).
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          acc2[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_operand(vt[t], b), P2[g][t],
+                                                               acc2[g][b], 0, 0, 0);
+      }
+    }
+  };
+
+  // Epilogue per group: combine the lane halves' normalisers, form O, RMSNorm, scale,
+  // store. ONLY_BAD: only rows whose flag is set (after the safe re-run).
+  const float lam = lamst->lambda_f;
+  const float gsc = lamst->one_minus_init_f;
+  const int hh = bh % H;
+  auto epilogue = [&](auto only_bad) __attribute__((always_inline)) {
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const bool row_bad = (bad[g] | static_cast<uint32_t>(__shfl_xor(static_cast<int>(bad[g]), 32))) != 0;
+    float l1 = st1[g].l + __shfl_xor(st1[g].l, 32);
+    float l2 = st2[g].l + __shfl_xor(st2[g].l, 32);
+    const float il1 = 1.0f / l1, il2 = 1.0f / l2;
+    float ss = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float o1 = acc1[g][b][j] * il1;
+        const float o2 = acc2[g][b][j] * il2;
+        acc1[g][b][j] = o1;
+        acc2[g][b][j] = o2;
+        const float o = o1 - lam * o2;
+        ss = fmaf(o, o, ss);
+      }
+    }
+    ss += __shfl_xor(ss, 32);
+    const float rstd = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
+    const int qr = q0 + 8 * m + 2 * wv + g;
+    if (qr < N && (!decltype(only_bad)::value || row_bad)) {
+      bf16_t* Y = out + (hoff + qr) * DV;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int col = 32 * b + 8 * jg + 4 * h;
+          f32x4 w = {1.f, 1.f, 1.f, 1.f};
+          if (rms_w) w = *reinterpret_cast<const f32x4*>(rms_w + hh * DV + col);
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float o = acc1[g][b][4 * jg + e] - lam * acc2[g][b][4 * jg + e];
+            y[e] = gsc * (w[e] * (o * rstd));
+          }
+          u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+          *reinterpret_cast<u32x2*>(Y + col) = pk;
+          if (sv_o1) {
+            f32x4 a = {acc1[g][b][4 * jg], acc1[g][b][4 * jg + 1], acc1[g][b][4 * jg + 2], acc1[g][b][4 * jg + 3]};
+            f32x4 bb = {acc2[g][b][4 * jg], acc2[g][b][4 * jg + 1], acc2[g][b][4 * jg + 2], acc2[g][b][4 * jg + 3]};
+            *reinterpret_cast<f32x4*>(sv_o1 + (hoff + qr) * DV + col) = a;
+            *reinterpret_cast<f32x4*>(sv_o2 + (hoff + qr) * DV + col) = bb;
+          }
+        }
+      }
+      if (sv_lse1 && h == 0) {
+        // lse_k = ln(sum_j exp(S_kj)) = (m_k + log2 l_k) * ln 2, m_k in the scaled log2 domain.
+        sv_lse1[hoff + qr] = (st1[g].m + __log2f(l1)) * kLn2;
+        sv_lse2[hoff + qr] = (st2[g].m + __log2f(l2)) * kLn2;
+        sv_rstd[hoff + qr] = rstd;
+      }
+    }
+  }
+  };
+
+  run();
+  if constexpr (!SAFE) {
+    epilogue(Flag<false>{});
+    // Row flags of this block: bit m of word 2 wv + g for row 8 m + 2 wv + g.
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint64_t bal = __ballot(bad[g] != 0);
+      const uint32_t mask = static_cast<uint32_t>(bal) | static_cast<uint32_t>(bal >> 32);
+      if (lane == 0) flags[8 * (static_cast<int64_t>(bh) * nqb + qb) + 2 * wv + g] = mask;
+    }
+  } else {
+    epilogue(Flag<true>{});
   }
 }
 
@@ -488,20 +795,41 @@ __global__ void __launch_bounds__(NT, 8 / NW) fwd_bf16_kernel(
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   using namespace fwdbf16;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   const int64_t BH = a.B * a.H;
   const int nqb = static_cast<int>((a.N + BR - 1) / BR);
   const int64_t nblk = BH * nqb;
   const diffattn_saved& sv = a.saved;
-  hipLaunchKernelGGL(fwd_bf16_kernel, dim3(static_cast<unsigned>(nblk)), dim3(NT), 0, s,
-                     static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
-                     static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
-                     static_cast<const bf16_t*>(a.v), a.lam, a.rms_weight,
-                     static_cast<bf16_t*>(a.out), a.training ? sv.lse1 : nullptr,
-                     a.training ? sv.lse2 : nullptr, a.training ? sv.o1 : nullptr,
-                     a.training ? sv.o2 : nullptr, a.training ? sv.rstd : nullptr,
-                     static_cast<int>(BH), static_cast<int>(a.H), static_cast<int>(a.N), nqb,
-                     a.eps);
-  return hipGetLastError();
+  uint32_t* flags = static_cast<uint32_t*>(a.workspace);
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nblk)), dim3(NT), LDS_BYTES, s,
+                       static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
+                       static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
+                       static_cast<const bf16_t*>(a.v), a.lam, a.rms_weight,
+                       static_cast<bf16_t*>(a.out), a.training ? sv.lse1 : nullptr,
+                       a.training ? sv.lse2 : nullptr, a.training ? sv.o1 : nullptr,
+                       a.training ? sv.o2 : nullptr, a.training ? sv.rstd : nullptr, flags,
+                       static_cast<int>(BH), static_cast<int>(a.H), static_cast<int>(a.N), nqb,
+                       a.eps);
+    return hipGetLastError();
+  };
+  hipError_t e = launch(fwd_bf16_kernel<false>);
+  if (e != hipSuccess) return e;
+  return launch(fwd_bf16_kernel<true>);
+}
+
+size_t fwd_bf16_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+  const int64_t nqb = (N + fwdbf16::BR - 1) / fwdbf16::BR;
+  return static_cast<size_t>(B * H * nqb) * 8 * sizeof(uint32_t);
 }
 
 }  // namespace diffattn

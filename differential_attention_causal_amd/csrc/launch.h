@@ -17,6 +17,7 @@ struct FwdArgs {
   void* out;
   diffattn_saved saved;      // all-null fields = inference
   bool training;
+  void* workspace;           // bf16: per row block, 8 words of row flags
   int64_t B, H, N;
   int d;
   float eps;
@@ -54,6 +55,7 @@ hipError_t launch_lambda(int dim, int layer, const float* lq1, const float* lk1,
                          hipStream_t s);
 hipError_t launch_fwd_fp32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+size_t fwd_bf16_workspace_bytes(int64_t B, int64_t H, int64_t N);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 

@@ -170,13 +170,15 @@ def _saved_struct(sv: Optional[Dict[str, torch.Tensor]]):
 
 
 def forward(q1, q2, k1, k2, v, lam_state, rms_weight=None, eps: float = 1e-5,
-            out: Optional[torch.Tensor] = None, saved: Optional[Dict[str, torch.Tensor]] = None):
+            out: Optional[torch.Tensor] = None, saved: Optional[Dict[str, torch.Tensor]] = None,
+            workspace: Optional[torch.Tensor] = None):
     """Causal DiffAttn forward. Q/K [B,H,N,d], V [B,H,N,2d] (float32 or bfloat16).
 
     Returns Y [B,H,N,2d].  ``saved`` (from ``alloc_saved``) requests the training
-    saves.
+    saves.  ``workspace``: a uint8 device tensor of at least
+    ``workspace_bytes(OP_FWD, ...)`` bytes (allocated here when omitted).
     """
-    _need_cuda(q1, q2, k1, k2, v, lam_state, rms_weight, out)
+    _need_cuda(q1, q2, k1, k2, v, lam_state, rms_weight, out, workspace)
     B, H, N, d = q1.shape
     for t in (q2, k1, k2):
         if tuple(t.shape) != (B, H, N, d) or t.dtype != q1.dtype:
@@ -187,10 +189,13 @@ def forward(q1, q2, k1, k2, v, lam_state, rms_weight=None, eps: float = 1e-5,
         out = torch.empty_like(v)
     p = problem(B, H, N, d, _dtype_code(q1), eps)
     svs = _saved_struct(saved)
+    need = workspace_bytes(OP_FWD, p)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
     _check("diffattn_fwd", _lib().diffattn_fwd(
         ctypes.byref(p), _ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), _ptr(lam_state),
-        _ptr(rms_weight), _ptr(out), ctypes.byref(svs) if svs is not None else None, None, 0,
-        _stream(q1.device)))
+        _ptr(rms_weight), _ptr(out), ctypes.byref(svs) if svs is not None else None,
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q1.device)))
     return out
 
 

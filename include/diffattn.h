@@ -38,8 +38,9 @@
  *   - Outputs must not overlap inputs (DIFFATTN_E_ARG).
  *   - A problem with batch, heads or seqlen equal to 0 is valid and does nothing.
  *   - Supported: DIFFATTN_FP32 forward with d in {16, 32, 64}; DIFFATTN_BF16 forward,
- *     decode and backward with d = 64. Accumulation is float32 everywhere. Other
- *     combinations return DIFFATTN_E_UNSUPPORTED.
+ *     decode and backward with d = 64, forward and backward with seqlen <= 2^22.
+ *     Accumulation is float32 everywhere. Other combinations return
+ *     DIFFATTN_E_UNSUPPORTED.
  */
 #ifndef DIFFATTN_H
 #define DIFFATTN_H
@@ -124,7 +125,12 @@ diffattn_status diffattn_lambda(int32_t dim, int32_t layer_idx, const float* lq1
  *   out             [B, H, N, 2d] of p->dtype (output Y)
  *   saved           host pointer to a struct of device pointers, or NULL (inference).
  *                   Non-NULL: every field must be a valid device buffer (bf16 only).
- *   workspace       may be NULL when diffattn_workspace_bytes(OP_FWD) is 0
+ *   workspace       device buffer of at least diffattn_workspace_bytes(OP_FWD) bytes
+ *                   (bf16: 32 bytes per block of 256 query rows, B * H * ceil(N / 256)
+ *                   blocks; it holds the row flags that pass the fast pass's result to a
+ *                   fixup pass; contents are scratch, nothing needs to be cleared). May
+ *                   be NULL when that size is 0 (float32). Too small or NULL when needed:
+ *                   DIFFATTN_E_WORKSPACE. It must not overlap any other argument.
  * Pointers must be 16-byte aligned. */
 diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const void* q2,
                              const void* k1, const void* k2, const void* v,

@@ -48,9 +48,12 @@ def test_status_strings():
     assert lib.diffattn_last_hip_error() == 0
 
 
-def fwd(p, ptrs=None, saved=None):
+WS = addr(40)            # a fake workspace far from the other fake buffers
+
+
+def fwd(p, ptrs=None, saved=None, ws=WS, ws_bytes=1 << 20):
     ptrs = ptrs or [addr(i) for i in range(8)]
-    return da.lib().diffattn_fwd(ctypes.byref(p), *ptrs, saved, None, 0, None)
+    return da.lib().diffattn_fwd(ctypes.byref(p), *ptrs, saved, ws, ws_bytes, None)
 
 
 def test_forward_argument_checks():
@@ -95,6 +98,17 @@ def test_forward_argument_checks():
     assert fwd(da.problem(1, 2, 64, 16, da.FP32), saved=ctypes.byref(sv)) == da.E_UNSUPPORTED
     # overflow of the element count
     assert fwd(bf(batch=1 << 40, heads=1 << 20)) == da.E_ARG
+    # bf16 sequences beyond the kernels' 32-bit per-head buffer offsets
+    assert fwd(bf(batch=1, heads=1, seqlen=(1 << 22) + 1)) == da.E_UNSUPPORTED
+    # bf16 needs its workspace: missing, too small, misaligned, overlapping the output
+    need = da.workspace_bytes(da.OP_FWD, bf())
+    assert need == 2 * 1 * 32
+    assert fwd(bf(), ws=None, ws_bytes=0) == da.E_WORKSPACE
+    assert fwd(bf(), ws_bytes=need - 1) == da.E_WORKSPACE
+    assert fwd(bf(), ws=ctypes.c_void_p(A * 41 + 8), ws_bytes=need) == da.E_ARG
+    assert fwd(bf(), ws=addr(7), ws_bytes=need) == da.E_ARG
+    # float32 needs none
+    assert da.workspace_bytes(da.OP_FWD, da.problem(1, 2, 64, 16, da.FP32)) == 0
 
 
 def test_empty_problems_are_noops():
@@ -162,10 +176,15 @@ def test_backward_argument_checks():
     assert call(p, bad, ctypes.byref(sv), ws, need) == da.E_ARG
     bad = list(ptrs); bad[5] = None         # lq1
     assert call(p, bad, ctypes.byref(sv), ws, need) == da.E_ARG
+    long = da.problem(1, 1, (1 << 22) + 1, 64, da.BF16)
+    assert call(long, ptrs, ctypes.byref(sv), ws, need) == da.E_UNSUPPORTED
 
 
 def test_workspace_queries():
-    assert da.workspace_bytes(da.OP_FWD, da.problem(4, 8, 2048, 64, da.BF16)) == 0
+    # forward: 8 words of row flags per block of 256 query rows
+    assert da.workspace_bytes(da.OP_FWD, da.problem(4, 8, 2048, 64, da.BF16)) == 4 * 8 * 8 * 32
+    assert da.workspace_bytes(da.OP_FWD, da.problem(1, 1, 257, 64, da.BF16)) == 2 * 32
+    assert da.workspace_bytes(da.OP_FWD, da.problem(4, 8, 2048, 64, da.FP32)) == 0
     p = da.problem(64, 16, 8192, 64, da.BF16)
     # per (b, h, split): 2 maps x (m, l, 128 accumulators) float32
     n = da.workspace_bytes(da.OP_DECODE, p)

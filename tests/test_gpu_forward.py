@@ -211,3 +211,28 @@ def test_unsupported_head_dim_raises():
     st = da.lambda_state_tensor(0.5, 0.2, DEV)
     with pytest.raises(da.DiffAttnError):
         da.forward(q, q.clone(), q.clone(), q.clone(), v, st)
+
+
+def test_bf16_fixup_pass_for_large_score_jump():
+    """A key whose score exceeds a row's first-sub-tile maximum by ~2^40 in weight: the
+    fast pass flags that row (bit 18 of word 0 of row block 1: row 400 = 256 + 8*18) and
+    the fixup pass recomputes it; every row must still match the oracle."""
+    w = synth.custom("fwd", 1, 2, 600, 64, 5, "bf16", number=470)
+    x, h, st, ls, _ = _run_fwd(w)
+    x = {k: t.clone() for k, t in x.items()}
+    x["q1"][0, 0, 400] = 2.0
+    x["k1"][0, 0, 350] = 2.0
+    x["q2"][0, 1, 400] = 2.0
+    x["k2"][0, 1, 350] = 2.0
+    p = da.problem(1, 2, 600, 64, da.BF16)
+    ws = torch.zeros(da.workspace_bytes(da.OP_FWD, p), dtype=torch.uint8, device=DEV)
+    y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, workspace=ws)
+    y2 = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
+    torch.cuda.synchronize()
+    flags = ws.view(torch.int32).cpu().numpy().reshape(2, 3, 8)   # [head, row block, word]
+    assert flags[0, 1, 0] & (1 << 18) and flags[1, 1, 0] & (1 << 18)
+    assert torch.equal(y, y2)
+    hh = {k: np64(t) for k, t in x.items()}
+    ref = orc.forward(hh["q1"], hh["q2"], hh["k1"], hh["k2"], hh["v"], ls["lambda"],
+                      ls["lambda_init"])
+    assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
