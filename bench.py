@@ -87,13 +87,15 @@ def leg_forward(steps, warmup):
     w = synth.WORKLOADS[3]
     x = synth.make_inputs(w, "cuda:0")
     out = torch.empty_like(x["v"])
+    p = da.problem(w.batch, w.heads, w.seqlen, w.head_dim, da.BF16)
+    ws = torch.empty(da.workspace_bytes(da.OP_FWD, p), dtype=torch.uint8, device="cuda:0")
     torch.cuda.synchronize()
 
     def step(ev):
         st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
         if ev:
             ev[0].record()
-        da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, out=out)
+        da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, out=out, workspace=ws)
         if ev:
             ev[1].record()
 
@@ -106,7 +108,7 @@ def leg_forward(steps, warmup):
         "fwd_kernel_ms": kern_ms, "flops_per_launch": fl,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_from_profiles("fwd_bf16_kernel", "fwd_bf16.hip", w.name)},
+                     "traffic": traffic_from_profiles("fwd_bf16_kernel<false>", "fwd_bf16.hip", w.name)},
         "formula_tflops_8dP": fl * 8.0 / 12.0 / (ms * 1e-3) / 1e12,
     }
 
@@ -154,11 +156,13 @@ def leg_train(steps, warmup):
     p = da.problem(w.batch, w.heads, w.seqlen, w.head_dim, da.BF16)
     ws = torch.empty(max(16, da.workspace_bytes(da.OP_BWD, p)), dtype=torch.uint8,
                      device="cuda:0")
+    wsf = torch.empty(da.workspace_bytes(da.OP_FWD, p), dtype=torch.uint8, device="cuda:0")
     torch.cuda.synchronize()
 
     def step(ev):
         st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
-        da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, out=out, saved=sv)
+        da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, out=out, saved=sv,
+                   workspace=wsf)
         if ev:
             ev[0].record()
         da.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lq1"], x["lk1"], x["lq2"],

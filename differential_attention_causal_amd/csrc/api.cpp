@@ -58,8 +58,8 @@ bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
   return false;
 }
 
-// Longest bf16 sequence of the forward and backward kernels: they address one head's K
-// and V rows through 32-bit buffer offsets (N * 256 bytes for V).
+// Longest bf16 sequence (forward, backward) or cache (decode): the kernels address one
+// head's K and V rows through 32-bit buffer offsets (N * 256 bytes for V).
 constexpr int64_t kMaxSeqBf16 = int64_t(1) << 22;
 
 size_t elem_bytes(diffattn_dtype t) { return t == DIFFATTN_FP32 ? 4 : 2; }
@@ -213,8 +213,7 @@ diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const
   diffattn_status st = check_problem(p, &empty);
   if (st != DIFFATTN_OK) return st;
   if (p->dtype != DIFFATTN_BF16 || p->head_dim != 64) return DIFFATTN_E_UNSUPPORTED;
-  if (p->batch * p->heads > 65535 || p->seqlen > (static_cast<int64_t>(1) << 31))
-    return DIFFATTN_E_UNSUPPORTED;
+  if (p->batch * p->heads > 65535 || p->seqlen > kMaxSeqBf16) return DIFFATTN_E_UNSUPPORTED;
   if (empty) return DIFFATTN_OK;
   if (!q1 || !q2 || !k1c || !k2c || !vc || !lam || !out) return DIFFATTN_E_ARG;
   const void* ptrs[6] = {q1, q2, k1c, k2c, vc, out};

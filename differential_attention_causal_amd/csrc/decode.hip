@@ -5,13 +5,14 @@
 // maps of the DiffAttn equation (pt.news.hada.io "Como a atencao diferencial funciona").
 // Generating a token re-reads the whole K1/K2/V cache from HBM (priorstack.com, "The
 // Memory Wall: Why the KV Cache Constrains LLM Serving"), so the kernel is a streaming
-// read: every cache byte is loaded exactly once, with 16-byte loads, and no LDS staging.
+// read: every cache byte is loaded exactly once, with 16-byte buffer loads, and no LDS
+// staging.
 //
 // Pass 1 (decode_split_kernel), grid = splits x (B*H): a workgroup of 4 wavefronts takes
 // one split of the cache; each wavefront walks 64-key rounds of its share:
 //   * scores: 8 lanes per key, each lane a 16-byte slice of the K1 and K2 rows, so one
-//     wave instruction reads 8 whole rows (1 KiB contiguous); the 8 partial dot products
-//     are summed across the lanes;
+//     wave instruction reads 8 whole rows (1 KiB contiguous); each lane's slice is dotted
+//     with the query by v_dot2_f32_bf16 and the 8 partial sums are added across lanes;
 //   * per map: running max m, normaliser l, and p_j = exp2(s_j log2(e)/sqrt(d) - m);
 //   * values: 16 lanes per V row (16 bytes each), 4 rows per instruction; each lane keeps
 //     8 output channels of both accumulators.
@@ -29,9 +30,11 @@ constexpr int D = 64;
 constexpr int DV = 128;
 constexpr int NT = 256;
 constexpr int KEYS_PER_ROUND = 64;          // per wavefront
+constexpr int SG = KEYS_PER_ROUND / 8;      // score groups of 8 keys (8 lanes per key)
+constexpr int VI = KEYS_PER_ROUND / 4;      // value loads (16 lanes per row, 4 rows each)
 constexpr int PART = 2 + DV;                // m, l, acc[DV]
 
-__global__ void __launch_bounds__(NT) decode_split_kernel(
+__global__ void __launch_bounds__(NT, 2) decode_split_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
     const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cache_len,
@@ -49,26 +52,29 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
   const int64_t s0 = static_cast<int64_t>(split) * split_len;
   if (s0 >= len) return;  // the combine pass reads only splits that start below len
 
-  const bf16_t* K1 = k1 + bh * L * D;
-  const bf16_t* K2 = k2 + bh * L * D;
-  const bf16_t* V = v + bh * L * DV;
+  // Cache rows through buffer resources bounded at len rows: keys at or beyond len read
+  // as zero, and each load needs only a 32-bit lane offset plus the round's scalar offset.
+  constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer, no swizzle
+  const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(k1 + bh * L * D), 0, static_cast<int>(len * D * 2), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(k2 + bh * L * D), 0, static_cast<int>(len * D * 2), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(v + bh * L * DV), 0, static_cast<int>(len * DV * 2), kBufFlags);
 
   // Score lanes: key r = lane / 8 of each group of 8, channel slice c = lane % 8.
   const int r = lane >> 3, c = lane & 7;
-  float qa[8], qb[8];
-  {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(q1 + bh * D + 8 * c);
-    const u32x4 y = *reinterpret_cast<const u32x4*>(q2 + bh * D + 8 * c);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      qa[2 * t] = __uint_as_float(x[t] << 16);
-      qa[2 * t + 1] = __uint_as_float(x[t] & 0xffff0000u);
-      qb[2 * t] = __uint_as_float(y[t] << 16);
-      qb[2 * t + 1] = __uint_as_float(y[t] & 0xffff0000u);
-    }
-  }
+  // This lane's 8 query channels of each map, as bf16 pairs for v_dot2 (each product of
+  // two bf16 values is exact in float32; the sums are float32).
+  // (Pairs are built element by element from bf16x8 vectors: bit-casting 32-bit lanes of
+  // a u32x4 to bf16x2 here was compiled to feed the same pair to every dot product.)
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q1 + bh * D + 8 * c));
+  const bf16x8 qb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q2 + bh * D + 8 * c));
   // Value lanes: channel slice e = lane % 16 (channels 8e..8e+7), key phase f = lane / 16.
   const int e = lane & 15, f = lane >> 4;
+  const int ko = r * D * 2 + 16 * c;    // byte offset of this lane's K slice in a round
+  const int vo = f * DV * 2 + 16 * e;   // byte offset of this lane's V slice in a round
 
   const float cs = kLog2e / 8.0f;  // log2(e) / sqrt(64)
   float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
@@ -76,35 +82,33 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc1[t] = acc2[t] = 0.f;
 
+#pragma clang loop unroll(disable)
   for (int rd = 0; rd < rounds; ++rd) {
     const int64_t kb = s0 + (static_cast<int64_t>(wv) * rounds + rd) * KEYS_PER_ROUND;
     if (kb >= len) break;
-    // ---- scores of the 64 keys kb + 8 g + r
-    u32x4 kx[8], ky[8];
+    const int kbs = __builtin_amdgcn_readfirstlane(static_cast<int>(kb));
+    // ---- scores of the keys kb + 8 g + r
+    u32x4 kx[SG], ky[SG];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int64_t key = kb + 8 * g + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kx[g] = key < len ? *reinterpret_cast<const u32x4*>(K1 + key * D + 8 * c) : z;
-      ky[g] = key < len ? *reinterpret_cast<const u32x4*>(K2 + key * D + 8 * c) : z;
+    for (int g = 0; g < SG; ++g) {
+      kx[g] = __builtin_amdgcn_raw_buffer_load_b128(rk1, ko + g * 8 * D * 2, kbs * D * 2, 0);
+      ky[g] = __builtin_amdgcn_raw_buffer_load_b128(rk2, ko + g * 8 * D * 2, kbs * D * 2, 0);
     }
-    u32x4 vv[16];
+    u32x4 vv[VI];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t key = kb + 4 * i + f;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      vv[i] = key < len ? *reinterpret_cast<const u32x4*>(V + key * DV + 8 * e) : z;
-    }
-    float s1[8], s2[8];
+    for (int i = 0; i < VI; ++i)
+      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * 4 * DV * 2, kbs * DV * 2, 0);
+    float s1[SG], s2[SG];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = 0; g < SG; ++g) {
       float d1 = 0.f, d2 = 0.f;
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, kx[g]), kc = __builtin_bit_cast(bf16x8, ky[g]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        d1 = fmaf(qa[2 * t], __uint_as_float(kx[g][t] << 16), d1);
-        d1 = fmaf(qa[2 * t + 1], __uint_as_float(kx[g][t] & 0xffff0000u), d1);
-        d2 = fmaf(qb[2 * t], __uint_as_float(ky[g][t] << 16), d2);
-        d2 = fmaf(qb[2 * t + 1], __uint_as_float(ky[g][t] & 0xffff0000u), d2);
+        const bf16x2 q1p = {qa[2 * t], qa[2 * t + 1]}, k1p = {ka[2 * t], ka[2 * t + 1]};
+        const bf16x2 q2p = {qb[2 * t], qb[2 * t + 1]}, k2p = {kc[2 * t], kc[2 * t + 1]};
+        d1 = __builtin_amdgcn_fdot2_f32_bf16(q1p, k1p, d1, false);
+        d2 = __builtin_amdgcn_fdot2_f32_bf16(q2p, k2p, d2, false);
       }
 #pragma unroll
       for (int o = 1; o < 8; o <<= 1) {
@@ -117,7 +121,7 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     }
     float mx1 = s1[0], mx2 = s2[0];
 #pragma unroll
-    for (int g = 1; g < 8; ++g) {
+    for (int g = 1; g < SG; ++g) {
       mx1 = fmaxf(mx1, s1[g]);
       mx2 = fmaxf(mx2, s2[g]);
     }
@@ -128,9 +132,9 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     }
     const float mn1 = fmaxf(m1, mx1), mn2 = fmaxf(m2, mx2);
     const float al1 = fast_exp2(m1 - mn1), al2 = fast_exp2(m2 - mn2);
-    float p1[8], p2[8], sum1 = 0.f, sum2 = 0.f;
+    float p1[SG], p2[SG], sum1 = 0.f, sum2 = 0.f;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = 0; g < SG; ++g) {
       p1[g] = fast_exp2(s1[g] - mn1);
       p2[g] = fast_exp2(s2[g] - mn2);
       sum1 += p1[g];
@@ -152,7 +156,7 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(
     }
     // ---- values: key 4 i + f, whose weight sits in register i/2 of lanes 8 * (key % 8)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < VI; ++i) {
       const int src = 32 * (i & 1) + 8 * f;
       const float w1 = __shfl(p1[i >> 1], src);
       const float w2 = __shfl(p2[i >> 1], src);
@@ -253,9 +257,10 @@ __global__ void __launch_bounds__(DV) decode_combine_kernel(
 }  // namespace dec
 
 void decode_split_geometry(int64_t B, int64_t H, int64_t L, int* n_split, int* split_len) {
-  // Rounds of 64 keys per wavefront: as many as keep >= 4096 workgroups in flight.
+  // Rounds of 64 keys per wavefront, at most 2 per wavefront: many small workgroups, so
+  // that the last partial wave of workgroups leaves little of the chip idle.
   const int64_t BH = B * H;
-  int rounds = 8;
+  int rounds = 2;
   while (rounds > 1) {
     const int64_t sl = static_cast<int64_t>(dec::KEYS_PER_ROUND) * 4 * rounds;
     if (BH * ((L + sl - 1) / sl) >= 4096) break;

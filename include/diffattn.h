@@ -38,7 +38,7 @@
  *   - Outputs must not overlap inputs (DIFFATTN_E_ARG).
  *   - A problem with batch, heads or seqlen equal to 0 is valid and does nothing.
  *   - Supported: DIFFATTN_FP32 forward with d in {16, 32, 64}; DIFFATTN_BF16 forward,
- *     decode and backward with d = 64, forward and backward with seqlen <= 2^22.
+ *     decode and backward with d = 64, seqlen (or cache capacity) <= 2^22.
  *     Accumulation is float32 everywhere. Other combinations return
  *     DIFFATTN_E_UNSUPPORTED.
  */

@@ -154,6 +154,9 @@ def test_decode_argument_checks():
     assert call(p, bad, ws, need) == da.E_ARG
     bad = list(ptrs); bad[5] = ctypes.c_void_p(A * 5 * 64 + 2)   # misaligned cache_len
     assert call(p, bad, ws, need) == da.E_ARG
+    # caches beyond the kernel's 32-bit per-head buffer offsets
+    long = da.problem(1, 1, (1 << 22) + 1, 64, da.BF16)
+    assert call(long, ptrs, ws, need) == da.E_UNSUPPORTED
 
 
 def test_backward_argument_checks():
