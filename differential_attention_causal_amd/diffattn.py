@@ -96,6 +96,11 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _nbytes(t) -> int:
+    """Size in bytes of a workspace tensor (any dtype), 0 for None."""
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -195,7 +200,7 @@ def forward(q1, q2, k1, k2, v, lam_state, rms_weight=None, eps: float = 1e-5,
     _check("diffattn_fwd", _lib().diffattn_fwd(
         ctypes.byref(p), _ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), _ptr(lam_state),
         _ptr(rms_weight), _ptr(out), ctypes.byref(svs) if svs is not None else None,
-        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q1.device)))
+        _ptr(workspace), _nbytes(workspace), _stream(q1.device)))
     return out
 
 
@@ -213,7 +218,7 @@ def decode(q1, q2, k1c, k2c, vc, lam_state, cache_len=None, rms_weight=None, eps
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=vc.device)
     _check("diffattn_decode", _lib().diffattn_decode(
         ctypes.byref(p), _ptr(q1), _ptr(q2), _ptr(k1c), _ptr(k2c), _ptr(vc), _ptr(cache_len),
-        _ptr(lam_state), _ptr(rms_weight), _ptr(out), _ptr(workspace), workspace.numel(),
+        _ptr(lam_state), _ptr(rms_weight), _ptr(out), _ptr(workspace), _nbytes(workspace),
         _stream(vc.device)))
     return out
 
@@ -240,5 +245,5 @@ def backward(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, lam_state, saved, dout, rms_
         ctypes.byref(svs) if svs is not None else None, _ptr(dout),
         _ptr(g["dq1"]), _ptr(g["dq2"]), _ptr(g["dk1"]), _ptr(g["dk2"]), _ptr(g["dv"]),
         _ptr(g["d_attn"]), _ptr(g["dlq1"]), _ptr(g["dlk1"]), _ptr(g["dlq2"]), _ptr(g["dlk2"]),
-        _ptr(workspace), workspace.numel(), _stream(q1.device)))
+        _ptr(workspace), _nbytes(workspace), _stream(q1.device)))
     return g
