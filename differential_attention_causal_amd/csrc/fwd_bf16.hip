@@ -95,7 +95,6 @@ __device__ __forceinline__ int perm_row(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer, no swizzle
 
 // Issues this wave's share of tile `t` (keys t BC ..) into its ring slot; lane l's 16
 // bytes land at block base + 16 l. K1 (and K2) block i holds key rows 8i .. 8i+7, V
@@ -103,19 +102,35 @@ constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer, no swizzle
 // w + NW r. The source offsets are recomputed per tile (they would otherwise hold six
 // vector registers through the loop).
 struct HeadRsrc {
-  __amdgpu_buffer_rsrc_t k1, k2, v;
+  u32x4 k1, k2, v;
 };
+// Buffer resource words (raw 32-bit buffer, no swizzle) for `bytes` bytes at `base`.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const u32x4 r = {static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes,
+                   0x00020000u};
+  return r;
+}
+// 16 bytes per lane from the buffer (offset voff) into LDS at m0 + 16 lane. Issued as
+// assembly: the compiler would otherwise make every later LDS read wait for it. (m0 is
+// reserved by the compiler and used by nothing else in this kernel.)
+__device__ __forceinline__ void dma16(const u32x4& rs, uint32_t m0, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rs));
+}
 
 __device__ __forceinline__ void dma_tile(const HeadRsrc& rs, char* lds, int t, int wv, int lane) {
-  LDS_AS char* base = (LDS_AS char*)(lds) + (t % NSLOT) * SLOT;
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)lds)) +
+                        (t % NSLOT) * SLOT;
   const int k0 = t * BC;
 #pragma unroll
   for (int r = 0; r < KBLK; ++r) {
     const int row = 8 * (wv + NW * r) + (lane >> 3), pu = lane & 7;
     const int ko = (k0 + row) * (D * 2) + 16 * (pu ^ k_swz(row));
-    LDS_AS char* dst = base + 1024 * (wv + NW * r);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k1, (LDS_AS void*)(dst + K1_OFF), 16, ko, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k2, (LDS_AS void*)(dst + K2_OFF), 16, ko, 0, 0, 0);
+    const uint32_t dst = base + 1024 * (wv + NW * r);
+    dma16(rs.k1, dst + K1_OFF, ko);
+    dma16(rs.k2, dst + K2_OFF, ko);
   }
 #pragma unroll
   for (int r = 0; r < VBLK; ++r) {
@@ -123,8 +138,7 @@ __device__ __forceinline__ void dma_tile(const HeadRsrc& rs, char* lds, int t, i
     const int region = i / (BC / 16);
     const int row = 16 * (i % (BC / 16)) + (lane >> 2), pc = lane & 3;
     const int vo = (k0 + row) * (DV * 2) + 64 * region + 16 * (pc ^ v_swz(row));
-    LDS_AS char* dst = base + V_OFF + 1024 * i;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (LDS_AS void*)(dst), 16, vo, 0, 0, 0);
+    dma16(rs.v, base + V_OFF + 1024 * i, vo);
   }
 }
 
@@ -136,25 +150,25 @@ __device__ __forceinline__ void tile_barrier(bool next_in_flight) {
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  __builtin_amdgcn_s_barrier();
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------------
-// LDS operand reads. They are issued as inline assembly and awaited explicitly: the
-// compiler cannot tell that they do not overlap the tiles being fetched into other ring
-// slots and would otherwise wait for those fetches first. Each wait is tied to the
-// registers it completes, so no consumer can be scheduled above it.
+// LDS operand reads are ordinary loads: the compiler tracks their completion and places
+// the waits (reads issued as assembly would complete after the compiler believes their
+// registers hold the data, and it may copy or reuse those registers meanwhile). The
+// tile fills are assembly (dma16), so the compiler does not order these reads behind
+// them; the tile barrier orders them instead.
 template <int OFF>
 __device__ __forceinline__ u32x4 ds_read_b128(int addr) {
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
-  return r;
+  return *reinterpret_cast<const LDS_AS u32x4*>((LDS_AS char*)nullptr + addr + OFF);
 }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 template <int OFF>
 __device__ __forceinline__ u32x2 ds_read_tr16(int addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
-  return r;
+  const s16x4 v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)((LDS_AS char*)nullptr + addr + OFF));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // K operand of one map for one 32-key sub-tile: 4 channel blocks of 16.
@@ -188,31 +202,6 @@ __device__ __forceinline__ void vt_issue(VtHalf& v, int addr) {
 __device__ __forceinline__ bf16x8 vt_operand(const VtHalf& v, int b) {
   const u32x4 x = {v.r[b][0][0], v.r[b][0][1], v.r[b][1][0], v.r[b][1][1]};
   return __builtin_bit_cast(bf16x8, x);
-}
-
-// Waits. Order of issue: V^T k-steps 0 and 1 of a half-step (8 reads each, prefetched
-// during the previous one), then, after the first products, the K rows of the next score
-// tile (4).
-__device__ __forceinline__ void wait_v0(VtHalf& v) {
-  asm volatile("s_waitcnt lgkmcnt(8)"
-               : "+v"(v.r[0][0]), "+v"(v.r[0][1]), "+v"(v.r[1][0]), "+v"(v.r[1][1]),
-                 "+v"(v.r[2][0]), "+v"(v.r[2][1]), "+v"(v.r[3][0]), "+v"(v.r[3][1]));
-}
-__device__ __forceinline__ void wait_v1(VtHalf& v) {
-  asm volatile("s_waitcnt lgkmcnt(4)"
-               : "+v"(v.r[0][0]), "+v"(v.r[0][1]), "+v"(v.r[1][0]), "+v"(v.r[1][1]),
-                 "+v"(v.r[2][0]), "+v"(v.r[2][1]), "+v"(v.r[3][0]), "+v"(v.r[3][1]));
-}
-__device__ __forceinline__ void wait_vt_all(VtHalf (&v)[2]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(v[0].r[0][0]), "+v"(v[0].r[0][1]), "+v"(v[0].r[1][0]), "+v"(v[0].r[1][1]),
-                 "+v"(v[0].r[2][0]), "+v"(v[0].r[2][1]), "+v"(v[0].r[3][0]), "+v"(v[0].r[3][1]),
-                 "+v"(v[1].r[0][0]), "+v"(v[1].r[0][1]), "+v"(v[1].r[1][0]), "+v"(v[1].r[1][1]),
-                 "+v"(v[1].r[2][0]), "+v"(v[1].r[2][1]), "+v"(v[1].r[3][0]), "+v"(v[1].r[3][1]));
-}
-__device__ __forceinline__ void wait_k(KOps& k) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(k.r[0]), "+v"(k.r[1]), "+v"(k.r[2]), "+v"(k.r[3]));
 }
 
 // ---------------------------------------------------------------------------------
@@ -451,9 +440,9 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   const int64_t hoff = static_cast<int64_t>(bh) * N;
 
   HeadRsrc rs;
-  rs.k1 = __builtin_amdgcn_make_buffer_rsrc((void*)(k1 + hoff * D), 0, N * D * 2, kBufFlags);
-  rs.k2 = __builtin_amdgcn_make_buffer_rsrc((void*)(k2 + hoff * D), 0, N * D * 2, kBufFlags);
-  rs.v = __builtin_amdgcn_make_buffer_rsrc((void*)(v + hoff * DV), 0, N * DV * 2, kBufFlags);
+  rs.k1 = rsrc_words(k1 + hoff * D, N * D * 2);
+  rs.k2 = rsrc_words(k2 + hoff * D, N * D * 2);
+  rs.v = rsrc_words(v + hoff * DV, N * DV * 2);
 
   // Every wave walks the same sub-tiles: keys 0 .. q0 + BR - 1 (rows beyond N are
   // zero-filled and masked). The first jd are wholly below the block's first row.
@@ -532,7 +521,6 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     constexpr bool CHECK = decltype(check)::value;
     constexpr int KN_OFF = IS_X ? K2_OFF : K1_OFF;   // map of S_next
     constexpr int KC_OFF = IS_X ? K1_OFF : K2_OFF;   // map of S_cur
-    if (!IS_X) wait_vt_all(vt);
     KOps kop;
     float y[32];
     // Packed weights as separate 32-bit words: kept in a u32x4 and updated element by
@@ -581,7 +569,6 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
               __builtin_bit_cast(bf16x2, pw[g][e >> 3][(e & 7) >> 1]), one, ssum[g][e >> 3], false);
         }
       });
-      if constexpr (k == 15) wait_k(kop);
       if constexpr (k == 21) {
 #pragma unroll
         for (int g = 0; g < 2; ++g) st[g].lp = ssum[g][0] + ssum[g][1];
@@ -621,7 +608,6 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         KOps kc;
         k_issue<KC_OFF>(kc, ka, k_off(j));
-        wait_k(kc);
         f32x16 Sr[2];
         qk(Sr, kc, qf_cur);
         s_guard(Sr);
@@ -668,7 +654,6 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     {
       KOps kop;
       k_issue<K1_OFF>(kop, ka, k_off(0));
-      wait_k(kop);
       qk(S1, kop, qf1);
     }
     if constexpr (!SAFE) {
@@ -676,7 +661,6 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
       // starts at key 0).
       KOps kop;
       k_issue<K2_OFF>(kop, ka, k_off(0));
-      wait_k(kop);
       f32x16 T2[2];
       qk(T2, kop, qf2);
       s_guard(S1);
@@ -697,7 +681,6 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     // X(0) multiplies tile 0's V (finite) by P2 = 0.
     vt_issue<0>(vt[0], va + v_off(0));
     vt_issue<1>(vt[1], va + v_off(0));
-    wait_vt_all(vt);
     for (int j = 0; j < jd; ++j) step(j, Flag<false>{}, Flag<SAFE>{});
     for (int j = jd; j < n_sub; ++j) step(j, Flag<true>{}, Flag<SAFE>{});
     // Drain: acc2 += V^T(last) P2(last); vt holds V^T(last).
