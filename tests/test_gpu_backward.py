@@ -81,8 +81,8 @@ def compare(g, ref, heads, h=None, layer=None, weight=None):
                                    atol=1e-6 * abs(dlam_gpu) * np.max(np.abs(f)))
 
 
-@pytest.mark.parametrize("b,hh,n", [(1, 1, 1), (1, 1, 32), (1, 2, 33), (2, 1, 64), (1, 2, 200),
-                                    (1, 1, 300)])
+@pytest.mark.parametrize("b,hh,n", [(1, 1, 1), (1, 1, 32), (1, 2, 33), (2, 1, 64), (1, 2, 129),
+                                    (1, 2, 200), (1, 1, 300), (1, 2, 1000)])
 def test_backward_small(b, hh, n):
     w = synth.custom("train", b, hh, n, 64, 6, "bf16", number=700 + n)
     x, h = draw(w)
