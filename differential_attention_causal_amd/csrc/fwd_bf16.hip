@@ -249,32 +249,27 @@ __device__ __forceinline__ void mask_scores(f32x16& s, int ks, int q, int h) {
   }
 }
 
-// p = exp2(s c - m) for the 16 scores, packed to the bf16 operands of the two PV k-steps.
-__device__ __forceinline__ void exp_pack(const f32x16& s, float c, float m, bf16x8& pa,
-                                         bf16x8& pb) {
+// p = exp2(s c - m) for the 16 scores, packed to the bf16 operands of the two PV k-steps;
+// returns their float32 sum (the row's partial normaliser, summed as in the fast loop).
+__device__ __forceinline__ float exp_pack(const f32x16& s, float c, float m, bf16x8& pa,
+                                          bf16x8& pb) {
   f32x8 x, y;
+  float sum = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < 8; e += 2) {
     x[e] = fast_exp2(fmaf(s[e], c, -m));
+    x[e + 1] = fast_exp2(fmaf(s[e + 1], c, -m));
+    sum += x[e] + x[e + 1];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
     y[e] = fast_exp2(fmaf(s[8 + e], c, -m));
+    y[e + 1] = fast_exp2(fmaf(s[9 + e], c, -m));
+    sum += y[e] + y[e + 1];
   }
   pa = __builtin_convertvector(x, bf16x8);
   pb = __builtin_convertvector(y, bf16x8);
-}
-// Sum of the 16 weights over their bf16-rounded values (the ones the PV product
-// multiplies), two per v_dot2 against (1, 1).
-__device__ __forceinline__ float psum(const bf16x8& pa, const bf16x8& pb) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  float sa = 0.f, sb = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const bf16x2 a2 = {pa[2 * e], pa[2 * e + 1]};
-    const bf16x2 b2 = {pb[2 * e], pb[2 * e + 1]};
-    sa = __builtin_amdgcn_fdot2_f32_bf16(a2, one, sa, false);
-    sb = __builtin_amdgcn_fdot2_f32_bf16(b2, one, sb, false);
-  }
-  return sa + sb;
+  return sum;
 }
 
 __device__ __forceinline__ bool over(float lp) { return !(lp <= kThr); }
@@ -309,8 +304,7 @@ __device__ __forceinline__ void settle_row(const f32x16& s, float c, RowState& s
   const float mn = (trig && t > st.m) ? t : st.m;
   const float a = (mn == st.m) ? 1.0f : fast_exp2(st.m - mn);
   bf16x8 na, nb;
-  exp_pack(s, c, mn, na, nb);
-  const float nlp = psum(na, nb);
+  const float nlp = exp_pack(s, c, mn, na, nb);
   if (trig) {
     pa = na;
     pb = nb;
@@ -503,8 +497,11 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
 
   // One half-step, in a fixed order: 24 products (16 accumulator products acc += V^T P^T,
   // then 8 score products S_next = K Q^T), each followed by a slice of the softmax of
-  // S_cur (sub-tile j, for accumulator acc_cur), software-pipelined over pairs of scores:
-  // fma (scale, subtract m), exp2, pack to bf16, row-sum dot product. The matrix core
+  // S_cur (sub-tile j, for accumulator acc_cur), software-pipelined over pairs of scores
+  // started every 1.25 slots: fma (scale, subtract m), one exp2, the other exp2, pack to
+  // bf16, row sum. At most two transcendentals fall behind one product, and no v_dot2
+  // (which does not co-execute with the matrix core); each step's results are anchored
+  // so the compiler cannot gather the steps of many slots in one place. The matrix core
   // thus always has a product queued while the vector unit works. CHECK (fixup pass):
   // the row sums are tested against kThr and the rare slow path may follow; otherwise
   // (fast pass) a row's partial sum over kBad only sets its flag, and the loop has no
@@ -545,7 +542,7 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
       if constexpr (k == 2) k_issue<KN_OFF>(kop, ka, k_off(k_sub));
       static_for<0, 16>([&](auto pc) __attribute__((always_inline)) {
         constexpr int pr = decltype(pc)::value;
-        constexpr int sa = 2 + pr;
+        constexpr int sa = (pr * 5) / 4;   // 16 pairs over slots 0 .. 22
         constexpr int g = pr >> 3, e = 2 * (pr & 7);
         if constexpr (k == sa) {          // scale and subtract the reference
 #pragma unroll
@@ -554,33 +551,25 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
             if (MASKED && 32 * j + key_of(e + i, h) > q0 + 8 * m + 2 * wv + g) sv = -INFINITY;
             y[16 * g + e + i] = fmaf(sv, c, -st[g].m);
           }
+          asm volatile("" : "+v"(y[16 * g + e]), "+v"(y[16 * g + e + 1]));
         }
-        if constexpr (k == sa + 1) {      // exp2
+        if constexpr (k == sa + 1) {      // exp2 of the first
           y[16 * g + e] = fast_exp2(y[16 * g + e]);
+          asm volatile("" : "+v"(y[16 * g + e]));
+        }
+        if constexpr (k == sa + 2) {      // exp2 of the second
           y[16 * g + e + 1] = fast_exp2(y[16 * g + e + 1]);
+          asm volatile("" : "+v"(y[16 * g + e + 1]));
         }
-        if constexpr (k == sa + 2) {      // pack to bf16
+        if constexpr (k == sa + 3) {      // pack to bf16
           pw[g][e >> 3][(e & 7) >> 1] = pack_bf16x2(y[16 * g + e], y[16 * g + e + 1]);
+          asm volatile("" : "+v"(pw[g][e >> 3][(e & 7) >> 1]));
         }
-        if constexpr (k == sa + 3) {      // row-sum dot product
-          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-          const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-          ssum[g][e >> 3] = __builtin_amdgcn_fdot2_f32_bf16(
-              __builtin_bit_cast(bf16x2, pw[g][e >> 3][(e & 7) >> 1]), one, ssum[g][e >> 3], false);
+        if constexpr (k == sa + 4) {      // row sum
+          ssum[g][e >> 3] += y[16 * g + e] + y[16 * g + e + 1];
+          asm volatile("" : "+v"(ssum[g][e >> 3]));
         }
       });
-      if constexpr (k == 21) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) st[g].lp = ssum[g][0] + ssum[g][1];
-      }
-      if constexpr (k == 22) {
-        if constexpr (CHECK) {
-          slow = __any(over(st[0].lp) || over(st[1].lp));
-        } else {
-          bad[0] |= static_cast<uint32_t>(over_bad(st[0].lp));
-          bad[1] |= static_cast<uint32_t>(over_bad(st[1].lp));
-        }
-      }
       if constexpr (IS_X && k == 16) vt_issue<0>(vt[0], va + v_off(j));
       if constexpr (IS_X && k == 17) vt_issue<1>(vt[1], va + v_off(j));
       __builtin_amdgcn_sched_barrier(0);
@@ -594,6 +583,14 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
       if (u + 2 < n_tiles) dma_tile(rs, lds, u + 2, wv, lane);
     }
     static_for<2, 24>(slot);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) st[g].lp = ssum[g][0] + ssum[g][1];
+    if constexpr (CHECK) {
+      slow = __any(over(st[0].lp) || over(st[1].lp));
+    } else {
+      bad[0] |= static_cast<uint32_t>(over_bad(st[0].lp));
+      bad[1] |= static_cast<uint32_t>(over_bad(st[1].lp));
+    }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
 #pragma unroll
