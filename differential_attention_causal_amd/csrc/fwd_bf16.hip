@@ -570,8 +570,12 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
           asm volatile("" : "+v"(ssum[g][e >> 3]));
         }
       });
-      if constexpr (IS_X && k == 16) vt_issue<0>(vt[0], va + v_off(j));
-      if constexpr (IS_X && k == 17) vt_issue<1>(vt[1], va + v_off(j));
+      // V^T(j) for Y(j) and X(j + 1): two transposing reads per slot (they do not overlap
+      // the matrix core well when bunched).
+      if constexpr (IS_X && k >= 16) {
+        constexpr int t = (k - 16) >> 2, b = (k - 16) & 3;
+        vt_issue_b<b, t>(vt[t], va + v_off(j));
+      }
       __builtin_amdgcn_sched_barrier(0);
     };
     slot(Int<0>{});
