@@ -136,12 +136,32 @@ def leg_decode(steps, warmup):
     nb = decode_bytes(w)
     kern_ms = sum(inner) / len(inner)
     gbs = nb / (kern_ms * 1e-3) / 1e9
+
+    # The write half of a serving step: append one token per sequence to the caches
+    # (each call starts from caches one row short of full, so every call writes).
+    new = {k: x[k][:, :, 0].contiguous() for k in ("k1", "k2", "v")}
+    full = torch.full((w.batch,), w.seqlen - 1, dtype=torch.int32, device="cuda:0")
+    cl = full.clone()
+
+    def append_step(ev):
+        cl.copy_(full)
+        if ev:
+            ev[0].record()
+        da.cache_append(new["k1"], new["k2"], new["v"], x["k1"], x["k2"], x["v"], cl)
+        if ev:
+            ev[1].record()
+
+    _, _, app = time_steps(append_step, steps, warmup, inner_events=True)
+    app_ms = sum(app) / len(app)
+    app_bytes = 2 * w.batch * w.heads * (4 * w.head_dim) * 2   # rows read + rows written
     return {
         "workload": w.name, "value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
         "ms_per_step": ms, "decode_ms": kern_ms, "bytes_per_step": nb,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS,
                      "traffic": traffic_from_profiles("decode_split_kernel", "decode.hip", w.name)},
+        "append": {"us_per_call": app_ms * 1e3, "bytes": app_bytes,
+                   "GB_s": app_bytes / (app_ms * 1e-3) / 1e9, "bound": "launch latency"},
     }
 
 

@@ -249,6 +249,37 @@ diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const
   return hip_status(diffattn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)), "decode");
 }
 
+diffattn_status diffattn_cache_append(const diffattn_problem* p, const void* k1_new,
+                                      const void* k2_new, const void* v_new, void* k1c,
+                                      void* k2c, void* vc, int32_t* cache_len, void* stream) {
+  bool empty = false;
+  diffattn_status st = check_problem(p, &empty);
+  if (st != DIFFATTN_OK) return st;
+  if (p->dtype != DIFFATTN_BF16 || p->head_dim != 64) return DIFFATTN_E_UNSUPPORTED;
+  if (p->seqlen > kMaxSeqBf16) return DIFFATTN_E_UNSUPPORTED;
+  if (empty) return DIFFATTN_OK;
+  if (!k1_new || !k2_new || !v_new || !k1c || !k2c || !vc || !cache_len) return DIFFATTN_E_ARG;
+  const void* ptrs[6] = {k1_new, k2_new, v_new, k1c, k2c, vc};
+  for (const void* x : ptrs)
+    if (!aligned(x, 16)) return DIFFATTN_E_ARG;
+  if (!aligned(cache_len, 4)) return DIFFATTN_E_ARG;
+  const int d = p->head_dim;
+  const size_t bh = static_cast<size_t>(p->batch) * p->heads;
+  const size_t kr = bh * d * 2, vr = bh * 2 * d * 2;
+  const size_t kc = kr * p->seqlen, vcb = vr * p->seqlen;
+  const Span in[3] = {{k1_new, kr}, {k2_new, kr}, {v_new, vr}};
+  const Span outs[4] = {{k1c, kc}, {k2c, kc}, {vc, vcb},
+                        {cache_len, static_cast<size_t>(p->batch) * 4}};
+  if (any_overlap(outs, 4, in, 3)) return DIFFATTN_E_ARG;
+  diffattn::AppendArgs a;
+  a.k1n = k1_new; a.k2n = k2_new; a.vn = v_new;
+  a.k1c = k1c; a.k2c = k2c; a.vc = vc;
+  a.cache_len = cache_len;
+  a.B = p->batch; a.H = p->heads; a.L = p->seqlen;
+  return hip_status(diffattn::launch_cache_append_bf16(a, static_cast<hipStream_t>(stream)),
+                    "cache_append");
+}
+
 diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const void* q2,
                              const void* k1, const void* k2, const void* v, const float* lq1,
                              const float* lk1, const float* lq2, const float* lk2,

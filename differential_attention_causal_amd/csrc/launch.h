@@ -50,6 +50,13 @@ struct BwdArgs {
   int d;
 };
 
+struct AppendArgs {
+  const void *k1n, *k2n, *vn;  // new rows [B, H, d] / [B, H, 2d]
+  void *k1c, *k2c, *vc;        // caches [B, H, L, d] / [B, H, L, 2d]
+  int32_t* cache_len;          // [B], updated in place
+  int64_t B, H, L;
+};
+
 hipError_t launch_lambda(int dim, int layer, const float* lq1, const float* lk1,
                          const float* lq2, const float* lk2, diffattn_lambda_state* out,
                          hipStream_t s);
@@ -58,6 +65,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 size_t fwd_bf16_workspace_bytes(int64_t B, int64_t H, int64_t N);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_cache_append_bf16(const AppendArgs& a, hipStream_t s);
 
 // Decode split geometry shared by the workspace query and the launcher.
 void decode_split_geometry(int64_t B, int64_t H, int64_t L, int* n_split, int* split_len);

@@ -22,8 +22,9 @@ FP32, BF16 = 0, 1
 OP_FWD, OP_DECODE, OP_BWD = 0, 1, 2
 
 # Every symbol declared in include/diffattn.h.
-EXPORTS = ("diffattn_lambda", "diffattn_fwd", "diffattn_decode", "diffattn_bwd",
-           "diffattn_workspace_bytes", "diffattn_status_string", "diffattn_last_hip_error")
+EXPORTS = ("diffattn_lambda", "diffattn_fwd", "diffattn_decode", "diffattn_cache_append",
+           "diffattn_bwd", "diffattn_workspace_bytes", "diffattn_status_string",
+           "diffattn_last_hip_error")
 
 
 class Problem(ctypes.Structure):
@@ -74,6 +75,8 @@ def _lib():
         lib.diffattn_decode.restype = ctypes.c_int
         lib.diffattn_decode.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
                                         ctypes.c_size_t, P]
+        lib.diffattn_cache_append.restype = ctypes.c_int
+        lib.diffattn_cache_append.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P]
         lib.diffattn_bwd.restype = ctypes.c_int
         lib.diffattn_bwd.argtypes = ([ctypes.POINTER(Problem)] + [P] * 11 +
                                      [ctypes.POINTER(Saved)] + [P] * 12 +
@@ -221,6 +224,18 @@ def decode(q1, q2, k1c, k2c, vc, lam_state, cache_len=None, rms_weight=None, eps
         _ptr(lam_state), _ptr(rms_weight), _ptr(out), _ptr(workspace), _nbytes(workspace),
         _stream(vc.device)))
     return out
+
+
+# ------------------------------------------------------------------ cache append
+def cache_append(k1_new, k2_new, v_new, k1c, k2c, vc, cache_len):
+    """Appends one token per sequence in place: rows [B,H,d]/[B,H,2d] go to cache row
+    cache_len[b] (if below L), and cache_len [B] int32 is incremented on the device."""
+    _need_cuda(k1_new, k2_new, v_new, k1c, k2c, vc, cache_len)
+    B, H, L, d = k1c.shape
+    p = problem(B, H, L, d, _dtype_code(k1c))
+    _check("diffattn_cache_append", _lib().diffattn_cache_append(
+        ctypes.byref(p), _ptr(k1_new), _ptr(k2_new), _ptr(v_new), _ptr(k1c), _ptr(k2c),
+        _ptr(vc), _ptr(cache_len), _stream(k1c.device)))
 
 
 # ------------------------------------------------------------------ backward

@@ -160,6 +160,26 @@ diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const
                                 const float* rms_weight, void* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* Appends one generated token per sequence to its K1/K2/V cache, in place: the write half
+ * of an autoregressive serving step, before the decode call that reads the cache whole
+ * (priorstack.com, "Multi-Head Latent Attention: Scaling LLM Serving Throughput via
+ * Low-Rank KV Compression", section "The Memory Wall: Why the KV Cache Constrains LLM
+ * Serving": the cache grows by one token per generated token).
+ * For every sequence b with n = cache_len[b] (a negative value counts as 0) below L, the
+ * rows k1_new[b, h], k2_new[b, h] and v_new[b, h] of every head h are copied to cache row
+ * n, and cache_len[b] becomes n + 1 on the device, so a following diffattn_decode sees the
+ * new token at position len - 1. A sequence whose cache is full (n >= L) is left unchanged,
+ * its length included; the caller detects that from cache_len.
+ *   k1_new, k2_new [B, H, d];  v_new [B, H, 2d]           (inputs)
+ *   k1c, k2c [B, H, L, d]; vc [B, H, L, 2d] (p->seqlen = L) (updated in place)
+ *   cache_len  device int32 [B], required                  (updated in place)
+ * bf16 only, d = 64, 16-byte aligned rows and caches, 4-byte aligned cache_len; the new
+ * rows must not overlap the caches or cache_len, nor the caches each other (E_ARG).
+ * The caller owns every buffer; no workspace. */
+diffattn_status diffattn_cache_append(const diffattn_problem* p, const void* k1_new,
+                                      const void* k2_new, const void* v_new, void* k1c,
+                                      void* k2c, void* vc, int32_t* cache_len, void* stream);
+
 /* Backward of the forward above for the loss sum(Y * dout), recomputing A1 and A2 from
  * the saved log-sum-exps. The pages print no gradient formulas; these follow from the
  * forward by the chain rule:

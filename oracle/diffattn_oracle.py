@@ -22,6 +22,10 @@ Sources (page title, then section / equation):
            Into Attention Calculations" (causal mask) and "Differential Attention
            With Multiple Heads" (lambda shared per layer, per-head RMSNorm,
            scale by 1 - lambda_init).
+  [MLA]    "Multi-Head Latent Attention: Scaling LLM Serving Throughput via
+           Low-Rank KV Compression" (priorstack.com, same tag page), section
+           "The Memory Wall: Why the KV Cache Constrains LLM Serving" (the decode
+           step reads the whole cache, which grows by one token per step).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
@@ -38,7 +42,8 @@ lambda vectors, lambda = 0 against torch's float64 causal scaled-dot-product
 attention, Q2 = Q1 and K2 = K1 giving (1 - lambda) times softmax attention,
 rows of each map summing to one, row 0 attending only to V row 0, mask
 perturbation invariance, RMSNorm against torch's rms_norm, a scalar brute-force
-twin on tiny shapes, decode equal to the last prefill row, and central finite
+twin on tiny shapes, decode equal to the last prefill row, append-then-decode
+equal to the prefill row of the extended sequence, and central finite
 differences of the forward for every gradient.
 """
 from __future__ import annotations
@@ -289,6 +294,31 @@ def decode(q1, q2, k1c, k2c, vc, cache_len, lam: float, lam_init: float,
             yy, _ = rms_norm_rows(o[None, :], eps, w)
             y[b, h] = (1.0 - lam_init) * yy[0]
     return y
+
+
+def cache_append(k1_new, k2_new, v_new, k1c, k2c, vc, cache_len):
+    """One generated token appended to each sequence's cache: the write half of an
+    autoregressive serving step, before the decode that reads the cache whole ([MLA],
+    "The Memory Wall: Why the KV Cache Constrains LLM Serving": the cache grows by one
+    token per generated token).
+
+    For sequence b with n = max(cache_len[b], 0) < L, row n of every head receives
+    k1_new[b, h], k2_new[b, h], v_new[b, h] and the length becomes n + 1; a full cache
+    (n >= L) is left as it is.  Returns new arrays (k1c, k2c, vc, cache_len); the
+    caches keep their dtype (the copy is exact).
+    """
+    k1c, k2c, vc = np.array(k1c), np.array(k2c), np.array(vc)
+    lens = np.array(cache_len, dtype=np.int64)
+    L = k1c.shape[2]
+    for b in range(k1c.shape[0]):
+        n = max(int(lens[b]), 0)
+        if n >= L:
+            continue
+        k1c[b, :, n] = k1_new[b]
+        k2c[b, :, n] = k2_new[b]
+        vc[b, :, n] = v_new[b]
+        lens[b] = n + 1
+    return k1c, k2c, vc, lens
 
 
 # --------------------------------------------------------------------------

@@ -159,6 +159,31 @@ def test_decode_argument_checks():
     assert call(long, ptrs, ws, need) == da.E_UNSUPPORTED
 
 
+def test_cache_append_argument_checks():
+    lib = da.lib()
+    p = da.problem(4, 2, 128, 64, da.BF16)
+    ptrs = [addr(i * 64) for i in range(7)]   # k1n k2n vn k1c k2c vc len
+    call = lambda p, ptrs: lib.diffattn_cache_append(ctypes.byref(p), *ptrs, None)
+    assert call(da.problem(4, 2, 128, 64, da.FP32), ptrs) == da.E_UNSUPPORTED
+    assert call(da.problem(4, 2, 128, 32, da.BF16), ptrs) == da.E_UNSUPPORTED
+    assert call(da.problem(1, 1, (1 << 22) + 1, 64, da.BF16), ptrs) == da.E_UNSUPPORTED
+    for i in range(7):
+        bad = list(ptrs); bad[i] = None
+        assert call(p, bad) == da.E_ARG, i
+    bad = list(ptrs); bad[1] = ctypes.c_void_p(A * 65 + 8)      # misaligned row
+    assert call(p, bad) == da.E_ARG
+    bad = list(ptrs); bad[6] = ctypes.c_void_p(A * 64 * 7 + 2)  # misaligned cache_len
+    assert call(p, bad) == da.E_ARG
+    bad = list(ptrs); bad[2] = ptrs[5]                          # new V row inside the V cache
+    assert call(p, bad) == da.E_ARG
+    bad = list(ptrs); bad[4] = ptrs[3]                          # K2 cache aliases K1 cache
+    assert call(p, bad) == da.E_ARG
+    bad = list(ptrs); bad[6] = ctypes.c_void_p(A * 193 + 16)     # length inside the K1 cache
+    assert call(p, bad) == da.E_ARG
+    # nothing to append: valid, no pointer needed
+    assert call(da.problem(0, 2, 128, 64, da.BF16), [None] * 7) == da.OK
+
+
 def test_backward_argument_checks():
     lib = da.lib()
     p = da.problem(2, 2, 128, 64, da.BF16)

@@ -88,3 +88,68 @@ def test_decode_lengths_clamped():
     ref = orc.decode(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], [1, 100], ls["lambda"],
                      ls["lambda_init"])
     assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
+
+
+def _append_case(w, lens, seed):
+    """Caches drawn for workload w, plus new rows from a second draw of the same shape."""
+    x, h = draw(w)
+    y, g = draw(w, seed=seed)
+    new = {k: y[k][:, :, 0].contiguous() for k in ("k1", "k2", "v")}
+    cl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    return x, h, new, cl
+
+
+def test_cache_append_bitwise():
+    """Every byte of the caches and lengths after an append equals the oracle's copy:
+    lengths 0, inside, last free row, full, negative."""
+    w = synth.custom("decode", 5, 3, 40, 64, 3, "bf16", number=660)
+    lens = [0, 7, 39, 40, -2]
+    x, h, new, cl = _append_case(w, lens, seed=4660)
+    k1, k2, v = x["k1"].clone(), x["k2"].clone(), x["v"].clone()
+    da.cache_append(new["k1"], new["k2"], new["v"], k1, k2, v, cl)
+    torch.cuda.synchronize()
+    i16 = lambda t: t.cpu().view(torch.int16).numpy()      # the copy moves bit patterns
+    r1, r2, rv, rl = orc.cache_append(i16(new["k1"]), i16(new["k2"]), i16(new["v"]),
+                                      i16(x["k1"]), i16(x["k2"]), i16(x["v"]), lens)
+    assert cl.cpu().tolist() == list(rl) == [1, 8, 40, 40, 1]
+    for got, ref in ((k1, r1), (k2, r2), (v, rv)):
+        assert np.array_equal(i16(got), ref)
+
+
+def test_cache_append_then_decode():
+    """Append then decode equals the oracle's decode over its own appended caches, and
+    twice in a row keeps growing the sequences."""
+    w = synth.custom("decode", 3, 2, 300, 64, 5, "bf16", number=670)
+    lens = [120, 299, 1]
+    x, h, new, cl = _append_case(w, lens, seed=4670)
+    st, ls = lam_pair(x, h, w.layer)
+    k1, k2, v = x["k1"].clone(), x["k2"].clone(), x["v"].clone()
+    hk = [h["k1"], h["k2"], h["v"]]
+    hl = lens
+    for step in range(2):
+        da.cache_append(new["k1"], new["k2"], new["v"], k1, k2, v, cl)
+        y = da.decode(x["q1"], x["q2"], k1, k2, v, st, cache_len=cl)
+        torch.cuda.synchronize()
+        *hk, hl = orc.cache_append(np64(new["k1"]), np64(new["k2"]), np64(new["v"]), *hk, hl)
+        assert cl.cpu().tolist() == list(hl)
+        ref = orc.decode(h["q1"], h["q2"], *hk, hl, ls["lambda"], ls["lambda_init"])
+        assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL, step
+
+
+def test_cache_append_decode_workload():
+    """64 sequences x 16 heads, L = 8192, every cache one row from full: after the append
+    every length is L and the new rows are in place (sampled), bitwise."""
+    w = synth.WORKLOADS[4]
+    x = synth.make_inputs(w, DEV)
+    gen = torch.Generator(device=DEV).manual_seed(4680)
+    new = {k: torch.randn(x[k][:, :, 0].shape, generator=gen, device=DEV).to(torch.bfloat16)
+           for k in ("k1", "k2", "v")}
+    cl = torch.full((w.batch,), w.seqlen - 1, dtype=torch.int32, device=DEV)
+    before = x["k1"][5, 3, w.seqlen - 2].clone()
+    da.cache_append(new["k1"], new["k2"], new["v"], x["k1"], x["k2"], x["v"], cl)
+    torch.cuda.synchronize()
+    assert (cl == w.seqlen).all().item()
+    for b, hh in ((0, 0), (5, 3), (63, 15)):
+        for k in ("k1", "k2", "v"):
+            assert torch.equal(x[k][b, hh, w.seqlen - 1], new[k][b, hh]), (b, hh, k)
+    assert torch.equal(x["k1"][5, 3, w.seqlen - 2], before)

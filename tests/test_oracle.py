@@ -235,6 +235,34 @@ def test_decode_equals_last_prefill_row():
     np.testing.assert_allclose(yfull, y[:, :, -1], rtol=1e-12, atol=1e-13)
 
 
+def test_cache_append_then_decode_equals_prefill_row():
+    """Appending token n to caches that hold tokens 0 .. n-1 (arbitrary values beyond)
+    and decoding gives row n of the prefill over the extended sequence; a full cache and
+    its length stay as they are, and a negative length counts as 0."""
+    r = rng(21)
+    B, H, L, d = 4, 2, 19, 8
+    q1, q2, k1, k2 = (rand(r, B, H, L, d) for _ in range(4))
+    v = rand(r, B, H, L, 2 * d)
+    lam, li = 0.31, 0.6
+    y = orc.forward(q1, q2, k1, k2, v, lam, li)
+    lens = np.array([5, 0, L, -3])
+    pos = np.array([5, 0, L - 1, 0])          # row each new token belongs to
+    tok = lambda a: np.stack([a[b, :, pos[b]] for b in range(B)])
+    junk = [rand(r, B, H, L, d), rand(r, B, H, L, d), rand(r, B, H, L, 2 * d)]
+    caches = []
+    for a, jk in zip((k1, k2, v), junk):
+        c = jk.copy()
+        for b in range(B):
+            c[b, :, :max(lens[b], 0)] = a[b, :, :max(lens[b], 0)]
+        caches.append(c)
+    c1, c2, cv, nl = orc.cache_append(tok(k1), tok(k2), tok(v), *caches, lens)
+    assert list(nl) == [6, 1, L, 1]
+    np.testing.assert_array_equal(c1[2], caches[0][2])     # full: untouched
+    yd = orc.decode(tok(q1), tok(q2), c1, c2, cv, nl, lam, li)
+    for b in (0, 1, 3):
+        np.testing.assert_allclose(yd[b], y[b, :, pos[b]], rtol=1e-12, atol=1e-13)
+
+
 def test_saved_lse_is_log_normaliser():
     r = rng(13)
     n, d = 30, 8
@@ -424,6 +452,18 @@ def _pin_failures(m):
                    lam, li)
     if not np.allclose(yd[0, 0], yp[0, 0, ln - 1], rtol=1e-12, atol=1e-14):
         fails.append("decode")
+    # append token ln - 1 to a cache holding tokens 0 .. ln - 2 (garbage beyond), then
+    # decode: equal to the same prefill row; a full cache is left unchanged
+    junk = lambda a: np.concatenate([a[:, :, :ln - 1], rand(r, *a[:, :, ln - 1:].shape)], 2)
+    c1, c2, cv, lens = m.cache_append(k1[:, :, ln - 1], k2[:, :, ln - 1], v[:, :, ln - 1],
+                                      junk(k1), junk(k2), junk(v), np.array([ln - 1]))
+    ya = m.decode(q1[:, :, ln - 1], q2[:, :, ln - 1], c1, c2, cv, lens, lam, li)
+    if lens[0] != ln or not np.allclose(ya[0, 0], yp[0, 0, ln - 1], rtol=1e-12, atol=1e-14):
+        fails.append("append then decode")
+    f1, _, _, flen = m.cache_append(k1[:, :, 0], k2[:, :, 0], v[:, :, 0], k1, k2, v,
+                                    np.array([n]))
+    if flen[0] != n or not np.array_equal(f1, k1):
+        fails.append("append to a full cache")
     # backward: central finite differences of the module's own forward
     n, d, H = 5, 3, 2
     p = {k: rand(r, 1, H, n, d) for k in ("q1", "q2", "k1", "k2")}
@@ -474,6 +514,8 @@ PLANTS = [
     ("lse sign", "saved[name][r0:r1] = m + np.log(", "saved[name][r0:r1] = m - np.log("),
     ("decode length off by one", "n = L if cache_len is None else int(cache_len[b])",
      "n = L if cache_len is None else int(cache_len[b]) - 1"),
+    ("append keeps the length", "        lens[b] = n + 1", "        lens[b] = n"),
+    ("append writes V one row early", "vc[b, :, n] = v_new[b]", "vc[b, :, n - 1] = v_new[b]"),
     ("norm gradient sign", "G = r * g - o * r ** 3", "G = r * g + o * r ** 3"),
     ("dK transposed", '"dk1": s * ds1.T @ q1', '"dk1": s * ds1 @ q1'),
     ("dS2 uses A1", "ds2 = a2 * (da2 - np.sum(a2 * da2", "ds2 = a2 * (da2 - np.sum(a1 * da2"),
