@@ -25,13 +25,16 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed float32 ops (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # no NaN inputs are supported, so max/min need no canonicalisation of MFMA results
-    "-fno-honor-nans",
     "-Wall", "-Wno-unused-function",
 ]
 
-# Per-file extra flags (none at present).
-FILE_FLAGS = {}
+# Kernel sources: no NaN inputs are supported, so max/min need no canonicalisation of
+# MFMA results. The host-side argument checks (api.cpp) keep IEEE NaN semantics so that
+# their finiteness tests are not folded away.
+KERNEL_FLAGS = ["-fno-honor-nans"]
+
+# Per-file extra flags.
+FILE_FLAGS = {s: KERNEL_FLAGS for s in SOURCES if s.endswith(".hip")}
 
 
 def hipcc() -> str:

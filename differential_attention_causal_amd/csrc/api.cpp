@@ -141,6 +141,32 @@ diffattn_status diffattn_lambda(int32_t dim, int32_t layer_idx, const float* lq1
                     "lambda");
 }
 
+diffattn_status diffattn_lambda_layers(int32_t dim, int32_t n_layers, int32_t first_layer,
+                                       int32_t fixed_init, float lambda_init,
+                                       const float* lq1, const float* lk1, const float* lq2,
+                                       const float* lk2, diffattn_lambda_state* states_out,
+                                       void* stream) {
+  if (dim < 1 || dim > 1024 || n_layers < 0 || n_layers > 65535 || first_layer < 1)
+    return DIFFATTN_E_ARG;
+  if (first_layer > INT32_MAX - n_layers) return DIFFATTN_E_ARG;
+  if (fixed_init != 0 && fixed_init != 1) return DIFFATTN_E_ARG;
+  if (fixed_init && !std::isfinite(lambda_init)) return DIFFATTN_E_ARG;
+  if (n_layers == 0) return DIFFATTN_OK;
+  if (!lq1 || !lk1 || !lq2 || !lk2 || !states_out) return DIFFATTN_E_ARG;
+  if (!aligned(lq1, 4) || !aligned(lk1, 4) || !aligned(lq2, 4) || !aligned(lk2, 4) ||
+      !aligned(states_out, 8))
+    return DIFFATTN_E_ARG;
+  const size_t vb = static_cast<size_t>(dim) * n_layers * sizeof(float);
+  const Span out[1] = {{states_out, sizeof(diffattn_lambda_state) * n_layers}};
+  const Span in[4] = {{lq1, vb}, {lk1, vb}, {lq2, vb}, {lk2, vb}};
+  if (any_overlap(out, 1, in, 4)) return DIFFATTN_E_ARG;
+  const double init = fixed_init ? static_cast<double>(lambda_init) : 0.0;
+  return hip_status(diffattn::launch_lambda_layers(dim, n_layers, first_layer, fixed_init != 0,
+                                                   init, lq1, lk1, lq2, lk2, states_out,
+                                                   static_cast<hipStream_t>(stream)),
+                    "lambda_layers");
+}
+
 diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const void* q2,
                              const void* k1, const void* k2, const void* v,
                              const diffattn_lambda_state* lam, const float* rms_weight,

@@ -60,6 +60,9 @@ struct AppendArgs {
 hipError_t launch_lambda(int dim, int layer, const float* lq1, const float* lk1,
                          const float* lq2, const float* lk2, diffattn_lambda_state* out,
                          hipStream_t s);
+hipError_t launch_lambda_layers(int dim, int n_layers, int first, bool fixed, double init_value,
+                                const float* lq1, const float* lk1, const float* lq2,
+                                const float* lk2, diffattn_lambda_state* out, hipStream_t s);
 hipError_t launch_fwd_fp32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 size_t fwd_bf16_workspace_bytes(int64_t B, int64_t H, int64_t N);

@@ -22,7 +22,7 @@ FP32, BF16 = 0, 1
 OP_FWD, OP_DECODE, OP_BWD = 0, 1, 2
 
 # Every symbol declared in include/diffattn.h.
-EXPORTS = ("diffattn_lambda", "diffattn_fwd", "diffattn_decode", "diffattn_cache_append",
+EXPORTS = ("diffattn_lambda", "diffattn_lambda_layers", "diffattn_fwd", "diffattn_decode", "diffattn_cache_append",
            "diffattn_bwd", "diffattn_workspace_bytes", "diffattn_status_string",
            "diffattn_last_hip_error")
 
@@ -69,6 +69,10 @@ def _lib():
         lib.diffattn_workspace_bytes.argtypes = [ctypes.c_int, ctypes.POINTER(Problem)]
         lib.diffattn_lambda.restype = ctypes.c_int
         lib.diffattn_lambda.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P]
+        lib.diffattn_lambda_layers.restype = ctypes.c_int
+        lib.diffattn_lambda_layers.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_float, P, P, P, P, P,
+                                               P]
         lib.diffattn_fwd.restype = ctypes.c_int
         lib.diffattn_fwd.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P,
                                      ctypes.POINTER(Saved), P, ctypes.c_size_t, P]
@@ -145,6 +149,27 @@ def lambda_(lq1, lk1, lq2, lk2, layer: int) -> torch.Tensor:
     _check("diffattn_lambda", _lib().diffattn_lambda(
         lq1.numel(), int(layer), _ptr(lq1), _ptr(lk1), _ptr(lq2), _ptr(lk2), _ptr(st),
         _stream(lq1.device)))
+    return st
+
+
+def lambda_layers(lq1s, lk1s, lq2s, lk2s, first_layer: int,
+                  lambda_init: Optional[float] = None) -> torch.Tensor:
+    """Device lambda states for layers first_layer .. first_layer + n - 1 (uint8 tensor
+    [n, 48]); the vectors are float32 [n, d]. lambda_init None: the per-layer schedule;
+    a number: that lambda_init for every layer."""
+    _need_cuda(lq1s, lk1s, lq2s, lk2s)
+    for t in (lq1s, lk1s, lq2s, lk2s):
+        if (t.dtype != torch.float32 or t.dim() != 2 or t.shape != lq1s.shape
+                or not t.is_contiguous()):
+            raise ValueError("lambda vectors must be contiguous float32 [n_layers, d] of "
+                             "equal shape")
+    n, d = lq1s.shape
+    st = torch.empty(n, LAMBDA_STATE_BYTES, dtype=torch.uint8, device=lq1s.device)
+    fixed = 0 if lambda_init is None else 1
+    init = 0.0 if lambda_init is None else float(lambda_init)
+    _check("diffattn_lambda_layers", _lib().diffattn_lambda_layers(
+        d, n, int(first_layer), fixed, init, _ptr(lq1s), _ptr(lk1s), _ptr(lq2s), _ptr(lk2s),
+        _ptr(st), _stream(lq1s.device)))
     return st
 
 

@@ -124,3 +124,14 @@ def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
     if with_dout if with_dout is not None else (w.kind == "train"):
         out["dout"] = _cast(_normal(gen, (B, H, N, dv), device), 1.0, dt)
     return out
+
+
+def make_lambda_layers(n_layers: int, head_dim: int, device="cpu", seed: int = 0,
+                       std: float = 0.1) -> Dict[str, torch.Tensor]:
+    """The four lambda vectors of n_layers layers, each float32 [n_layers, head_dim]
+    (row k belongs to the k-th layer), normal with standard deviation ``std``."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return {name: _normal(gen, (n_layers, head_dim), device).mul_(std)
+            for name in ("lq1", "lk1", "lq2", "lk2")}

@@ -114,6 +114,30 @@ diffattn_status diffattn_lambda(int32_t dim, int32_t layer_idx, const float* lq1
                                 const float* lk1, const float* lq2, const float* lk2,
                                 diffattn_lambda_state* state_out, void* stream);
 
+/* lambda for n_layers consecutive layers in one call, optionally with one fixed
+ * lambda_init for all of them. Besides the schedule above, the same lambda_init in every
+ * layer (0.8 is the example given) was also tried, with results reported as fairly robust
+ * to the choice (pt.news.hada.io, "Como a atencao diferencial funciona", the note after
+ * the lambda_init equation).
+ *   dim           length of each lambda vector, 1 <= dim <= 1024
+ *   n_layers      number of layers, 0 <= n_layers <= 65535 (0: nothing to do, OK, and no
+ *                 pointer is read)
+ *   first_layer   layer index l of the first layer (>= 1); layer k uses l = first_layer + k
+ *   fixed_init    0: lambda_init follows the per-layer schedule (lambda_init is ignored);
+ *                 1: lambda_init, which must be finite, for every layer (first_layer then
+ *                 only labels the layers)
+ *   lq1..lk2      device float32 [n_layers, dim], layer k at offset k * dim (4-byte aligned)
+ *   states_out    device diffattn_lambda_state [n_layers] (8-byte aligned), written
+ * One launch, one workgroup per layer; each state is computed exactly as diffattn_lambda
+ * computes it (bitwise equal under the schedule). Errors: E_ARG for NULL or misaligned
+ * pointers, values out of range, a non-finite fixed lambda_init, or states overlapping
+ * the vectors. */
+diffattn_status diffattn_lambda_layers(int32_t dim, int32_t n_layers, int32_t first_layer,
+                                       int32_t fixed_init, float lambda_init,
+                                       const float* lq1, const float* lk1, const float* lq2,
+                                       const float* lk2, diffattn_lambda_state* states_out,
+                                       void* stream);
+
 /* Causal DiffAttn forward with the per-head RMSNorm and (1 - lambda_init) scale fused in.
  * Source: the DiffAttn equation (pt.news.hada.io "Como a atencao diferencial funciona";
  * priorstack.com "Cancelling Context Noise Through Attention Map Subtraction"), causal

@@ -49,7 +49,7 @@ differences of the forward for every gradient.
 from __future__ import annotations
 
 import math
-from typing import Dict, Optional
+from typing import Dict, List, Optional
 
 import numpy as np
 
@@ -77,7 +77,8 @@ def lambda_init(layer: int) -> float:
     return 0.8 - 0.6 * e
 
 
-def lambda_scalar(lq1, lk1, lq2, lk2, layer: int) -> Dict[str, float]:
+def lambda_scalar(lq1, lk1, lq2, lk2, layer: int,
+                  fixed_init: Optional[float] = None) -> Dict[str, float]:
     """lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init.
 
     [HADA] "Como a atencao diferencial funciona", lambda equation; [PRIOR],
@@ -87,6 +88,11 @@ def lambda_scalar(lq1, lk1, lq2, lk2, layer: int) -> Dict[str, float]:
     The dot products are summed in index order in float64 (each product of
     two float32 values is exact in float64).  The result is returned in float64
     and rounded once to float32 (the value the kernels consume).
+
+    fixed_init None: lambda_init follows the layer schedule; otherwise it is
+    fixed_init for every layer (the pages also try one constant lambda_init,
+    for example 0.8, in all layers: [HADA], the note after the lambda_init
+    equation).
     """
     lq1, lk1, lq2, lk2 = (_f64(v).reshape(-1) for v in (lq1, lk1, lq2, lk2))
     if not (lq1.shape == lk1.shape == lq2.shape == lk2.shape):
@@ -99,7 +105,7 @@ def lambda_scalar(lq1, lk1, lq2, lk2, layer: int) -> Dict[str, float]:
         b = b + x * y
     ea = math.exp(a)
     eb = math.exp(b)
-    li = lambda_init(layer)
+    li = lambda_init(layer) if fixed_init is None else float(fixed_init)
     lam = (ea - eb) + li
     return {
         "lambda": lam, "lambda_init": li, "exp_a": ea, "exp_b": eb,
@@ -107,6 +113,19 @@ def lambda_scalar(lq1, lk1, lq2, lk2, layer: int) -> Dict[str, float]:
         "lambda_init_f32": float(np.float32(li)),
         "one_minus_init_f32": float(np.float32(1.0 - li)),
     }
+
+
+def lambda_layers(lq1s, lk1s, lq2s, lk2s, first_layer: int,
+                  fixed_init: Optional[float] = None) -> List[Dict[str, float]]:
+    """lambda of n consecutive layers: row k of each [n, d] array belongs to
+    layer first_layer + k, and each is lambda_scalar of that row ([HADA]: one
+    lambda per layer, lambda_init from the layer index or fixed)."""
+    rows = [_f64(v) for v in (lq1s, lk1s, lq2s, lk2s)]
+    if rows[0].ndim != 2 or any(r.shape != rows[0].shape for r in rows):
+        raise ValueError("lambda vectors must be [n_layers, d] of equal shape")
+    return [lambda_scalar(rows[0][k], rows[1][k], rows[2][k], rows[3][k], first_layer + k,
+                          fixed_init)
+            for k in range(rows[0].shape[0])]
 
 
 # --------------------------------------------------------------------------

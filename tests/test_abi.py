@@ -136,6 +136,46 @@ def test_lambda_argument_checks():
     assert lib.diffattn_lambda(64, 1, *ptr[:4], ctypes.c_void_p(A + 8), None) == da.E_ARG
 
 
+def test_lambda_layers_argument_checks():
+    lib = da.lib()
+    ptr = [addr(i * 64) for i in range(5)]   # four [n, 64] vectors and the states
+    call = lambda d, n, first, mode, init, p: lib.diffattn_lambda_layers(d, n, first, mode,
+                                                                         init, *p, None)
+    assert call(0, 4, 1, 0, 0.0, ptr) == da.E_ARG
+    assert call(1025, 4, 1, 0, 0.0, ptr) == da.E_ARG
+    assert call(64, -1, 1, 0, 0.0, ptr) == da.E_ARG
+    assert call(64, 65536, 1, 0, 0.0, ptr) == da.E_ARG
+    assert call(64, 4, 0, 0, 0.0, ptr) == da.E_ARG
+    assert call(64, 4, 2 ** 31 - 2, 0, 0.0, ptr) == da.E_ARG      # last index past int32
+    assert call(64, 4, 1, 2, 0.8, ptr) == da.E_ARG                # unknown mode
+    for bad_init in (float("inf"), float("-inf"), float("nan")):
+        assert call(64, 4, 1, 1, bad_init, ptr) == da.E_ARG
+    # nothing to do: OK without touching any pointer; the schedule ignores lambda_init
+    assert call(64, 0, 1, 0, float("nan"), [None] * 5) == da.OK
+    assert call(64, 0, 1, 1, 0.8, [None] * 5) == da.OK
+    bad = list(ptr); bad[2] = None
+    assert call(64, 4, 1, 1, 0.8, bad) == da.E_ARG
+    bad = list(ptr); bad[4] = ctypes.c_void_p(A * 4 * 64 + 4)   # states not 8-byte aligned
+    assert call(64, 4, 1, 0, 0.0, bad) == da.E_ARG
+    bad = list(ptr); bad[1] = ctypes.c_void_p(A * 64 + 2)   # vector not 4-byte aligned
+    assert call(64, 4, 1, 0, 0.0, bad) == da.E_ARG
+    # states overlapping the last row of the third vector array ([4, 64] float32 = 1 KiB)
+    bad = list(ptr); bad[4] = ctypes.c_void_p(A * (2 * 64 + 1) + 1024 - 8)
+    assert call(64, 4, 1, 0, 0.0, bad) == da.E_ARG
+
+
+def test_rms_eps_must_be_finite():
+    lib = da.lib()
+    ptrs = [addr(i * 64) for i in range(9)]
+    for eps in (float("nan"), float("inf"), -1e-6):
+        p = da.problem(1, 1, 16, 64, da.BF16)
+        p.rms_eps = eps
+        assert lib.diffattn_fwd(ctypes.byref(p), *ptrs[:8], None, None, 0, None) == da.E_ARG
+    # the same call with a valid eps gets past the problem checks (to the workspace check)
+    p = da.problem(1, 1, 16, 64, da.BF16)
+    assert lib.diffattn_fwd(ctypes.byref(p), *ptrs[:8], None, None, 0, None) == da.E_WORKSPACE
+
+
 def test_decode_argument_checks():
     lib = da.lib()
     p = da.problem(64, 16, 8192, 64, da.BF16)

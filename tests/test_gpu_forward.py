@@ -5,6 +5,7 @@ relative error per (b, h); bf16 outputs (after RMSNorm and the 1 - lambda_init
 scale) within 2e-2 max-abs.
 """
 import math
+from typing import Dict
 
 import numpy as np
 import pytest
@@ -25,6 +26,16 @@ def ulp_diff(a: float, b: float) -> float:
     return abs(a - b) / np.spacing(max(abs(a), abs(b)))
 
 
+def lambda_f64_ok(got: float, ref: Dict[str, float]) -> bool:
+    """The float64 lambda within the rounding it inherits: each exp may be off by one
+    unit in the last place (device exp is faithfully rounded), then the difference and
+    the sum with lambda_init each round once."""
+    ea, eb, lam = ref["exp_a"], ref["exp_b"], ref["lambda"]
+    bound = (np.spacing(ea) + np.spacing(eb) + np.spacing(abs(ea - eb)) +
+             np.spacing(abs(lam)))
+    return abs(got - lam) <= bound
+
+
 @pytest.mark.parametrize("layer", [1, 2, 4, 6, 8, 12, 30])
 @pytest.mark.parametrize("d", [16, 64])
 def test_lambda_bitwise(layer, d):
@@ -34,8 +45,9 @@ def test_lambda_bitwise(layer, d):
     got = da.read_lambda_state(st)
     for k in ("lambda_f32", "lambda_init_f32", "one_minus_init_f32"):
         assert np.float32(got[k]).tobytes() == np.float32(ls[k]).tobytes(), k
-    for k in ("lambda", "lambda_init", "exp_a", "exp_b"):
+    for k in ("lambda_init", "exp_a", "exp_b"):
         assert ulp_diff(got[k], ls[k]) <= 1.0, (k, got[k], ls[k])
+    assert lambda_f64_ok(got["lambda"], ls), (got["lambda"], ls["lambda"])
     assert got["lambda_init"] == orc.lambda_init(layer) or \
         ulp_diff(got["lambda_init"], orc.lambda_init(layer)) <= 1.0
 
@@ -47,6 +59,72 @@ def test_lambda_zero_vectors():
         li = orc.lambda_init(layer)
         assert np.float32(got["lambda_f32"]) == np.float32(li)
         assert got["exp_a"] == 1.0 and got["exp_b"] == 1.0
+
+
+def _layer_vectors(n, d, seed):
+    x = synth.make_lambda_layers(n, d, DEV, seed=seed)
+    torch.cuda.synchronize()
+    return x, {k: np64(v) for k, v in x.items()}
+
+
+@pytest.mark.parametrize("n,first,d", [(1, 1, 64), (7, 3, 64), (12, 1, 16), (5, 40, 1024)])
+def test_lambda_layers_schedule_equals_per_layer_calls(n, first, d):
+    x, h = _layer_vectors(n, d, seed=900 + n + d)
+    st = da.lambda_layers(x["lq1"], x["lk1"], x["lq2"], x["lk2"], first)
+    ref = orc.lambda_layers(h["lq1"], h["lk1"], h["lq2"], h["lk2"], first)
+    torch.cuda.synchronize()
+    for k in range(n):
+        one = da.lambda_(x["lq1"][k].contiguous(), x["lk1"][k].contiguous(),
+                         x["lq2"][k].contiguous(), x["lk2"][k].contiguous(), first + k)
+        assert torch.equal(st[k].cpu(), one.cpu()), k
+        got = da.read_lambda_state(st[k])
+        for key in ("lambda_f32", "lambda_init_f32", "one_minus_init_f32"):
+            assert np.float32(got[key]).tobytes() == np.float32(ref[k][key]).tobytes(), (k, key)
+        for key in ("lambda_init", "exp_a", "exp_b"):
+            assert ulp_diff(got[key], ref[k][key]) <= 1.0, (k, key)
+        assert lambda_f64_ok(got["lambda"], ref[k]), k
+
+
+@pytest.mark.parametrize("init", [0.8, 0.5, 0.2])
+def test_lambda_layers_fixed_init(init):
+    n, first, d = 9, 2, 64
+    x, h = _layer_vectors(n, d, seed=950)
+    st = da.lambda_layers(x["lq1"], x["lk1"], x["lq2"], x["lk2"], first, lambda_init=init)
+    init32 = float(np.float32(init))          # the value the float argument carries
+    ref = orc.lambda_layers(h["lq1"], h["lk1"], h["lq2"], h["lk2"], first, fixed_init=init32)
+    for k in range(n):
+        got = da.read_lambda_state(st[k])
+        assert got["lambda_init"] == init32, k
+        for key in ("lambda_f32", "lambda_init_f32", "one_minus_init_f32"):
+            assert np.float32(got[key]).tobytes() == np.float32(ref[k][key]).tobytes(), (k, key)
+        for key in ("exp_a", "exp_b"):
+            assert ulp_diff(got[key], ref[k][key]) <= 1.0, (k, key)
+        assert lambda_f64_ok(got["lambda"], ref[k]), k
+
+
+def test_lambda_layers_zero_vectors_fixed_init_is_the_init():
+    z = torch.zeros(4, 64, dtype=torch.float32, device=DEV)
+    st = da.lambda_layers(z, z, z, z, 6, lambda_init=0.8)
+    for k in range(4):
+        got = da.read_lambda_state(st[k])
+        assert got["lambda"] == float(np.float32(0.8)) and got["exp_a"] == 1.0, k
+
+
+def test_lambda_layers_maximum_count():
+    """65535 layers in one launch; sampled layers against the oracle."""
+    n, d = 65535, 64
+    x, h = _layer_vectors(n, d, seed=990)
+    st = da.lambda_layers(x["lq1"], x["lk1"], x["lq2"], x["lk2"], 1).cpu()
+    for k in (0, 1, 777, 40000, n - 1):
+        ref = orc.lambda_scalar(h["lq1"][k], h["lk1"][k], h["lq2"][k], h["lk2"][k], 1 + k)
+        got = da.read_lambda_state(st[k])
+        for key in ("lambda_f32", "lambda_init_f32", "one_minus_init_f32"):
+            assert np.float32(got[key]).tobytes() == np.float32(ref[key]).tobytes(), (k, key)
+
+
+def test_lambda_layers_empty():
+    z = torch.zeros(0, 64, dtype=torch.float32, device=DEV)
+    assert da.lambda_layers(z, z, z, z, 1).shape == (0, da.LAMBDA_STATE_BYTES)
 
 
 def _run_fwd(w, seed=None, weight=None):

@@ -416,6 +416,33 @@ def _pin_failures(m):
     st = m.lambda_scalar(lq1, lk1, np.zeros(d), np.zeros(d), 5)
     if abs(st["lambda"] - (1.0 + m.lambda_init(5))) > 1e-14:
         fails.append("lambda closed form")
+    # one lambda_init for every layer: zero vectors give lambda = lambda_init at any layer,
+    # and the closed form above gives 1 + lambda_init
+    fixed = json.load(open(os.path.join(GOLDEN, "lambda_init_fixed.json")))
+    li_fix = fixed["fixed_lambda_init_example"]
+    for layer in (1, 9):
+        z = np.zeros(d)
+        if m.lambda_scalar(z, z, z, z, layer, fixed_init=li_fix)["lambda"] != li_fix:
+            fails.append("fixed lambda_init")
+    st = m.lambda_scalar(lq1, lk1, np.zeros(d), np.zeros(d), 5, fixed_init=li_fix)
+    if abs(st["lambda"] - (1.0 + li_fix)) > 1e-14:
+        fails.append("fixed lambda_init closed form")
+    # many layers at once: row k is layer first + k (zero vectors: lambda = lambda_init,
+    # 0.2 at layer 1 and the gap to 0.8 shrinking by e^-0.3 per layer)
+    zs = np.zeros((3, d))
+    lays = m.lambda_layers(zs, zs, zs, zs, 1)
+    if abs(lays[0]["lambda"] - golden["layer_1"]) > 1e-15:
+        fails.append("layers: first row")
+    g0, g1 = (golden["limit_deep_layers"] - lays[k]["lambda"] for k in (0, 1))
+    if abs(g1 - math.exp(-0.3) * g0) > 1e-15:
+        fails.append("layers: row k is layer first + k")
+    rows = rand(r, 4, 2, d)
+    lays = m.lambda_layers(rows[0], rows[1], rows[2], rows[3], 4, fixed_init=li_fix)
+    for k in range(2):
+        ea = math.exp(float(np.dot(rows[0][k], rows[1][k])))
+        eb = math.exp(float(np.dot(rows[2][k], rows[3][k])))
+        if abs(lays[k]["lambda"] - (ea - eb + li_fix)) > 1e-12:
+            fails.append("layers: row k uses vectors k")
     # forward: two-map composition of torch's causal attention, on one head
     n, d = 12, 4
     q1, q2, k1, k2 = (rand(r, 1, 1, n, d) for _ in range(4))
@@ -501,6 +528,11 @@ def test_pins_hold_on_the_oracle():
 PLANTS = [
     ("lambda sign", "lam = (ea - eb) + li", "lam = (eb - ea) + li"),
     ("lambda_init form", "return 0.8 - 0.6 * e", "return 0.8 - 0.6 / e"),
+    ("fixed lambda_init ignored",
+     "li = lambda_init(layer) if fixed_init is None else float(fixed_init)",
+     "li = lambda_init(layer)"),
+    ("layers all use the first index", "rows[3][k], first_layer + k,", "rows[3][k], first_layer,"),
+    ("layers read row 0 only", "lambda_scalar(rows[0][k], rows[1][k],", "lambda_scalar(rows[0][0], rows[1][0],"),
     ("DiffAttn sign", "o[r0:r1] = (a1 - lam * a2) @ v[:kend]",
      "o[r0:r1] = (a1 + lam * a2) @ v[:kend]"),
     ("second map uses K1", "s2 = s * (q2[r0:r1] @ k2[:kend].T)",
