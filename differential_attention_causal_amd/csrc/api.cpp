@@ -9,6 +9,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include <hip/hip_runtime.h>
 
 #include "diffattn.h"
@@ -304,6 +307,71 @@ diffattn_status diffattn_cache_append(const diffattn_problem* p, const void* k1_
   a.B = p->batch; a.H = p->heads; a.L = p->seqlen;
   return hip_status(diffattn::launch_cache_append_bf16(a, static_cast<hipStream_t>(stream)),
                     "cache_append");
+}
+
+// Shapes the projection GEMMs take: K (d_model, or H 2d for W_O) a multiple of 64 up to
+// 65536, M = B N rows below 2^31, d a multiple of 32 (so no 32-column block of the fused
+// QKV output straddles two tensors).
+diffattn_status check_proj(const diffattn_problem* p, int64_t d_model, bool* empty) {
+  diffattn_status st = check_problem(p, empty);
+  if (st != DIFFATTN_OK) return st;
+  if (d_model < 64 || d_model > 65536) return DIFFATTN_E_ARG;
+  if (p->dtype != DIFFATTN_BF16) return DIFFATTN_E_UNSUPPORTED;
+  const int d = p->head_dim;
+  if (d % 32 != 0 || d > 256 || d_model % 64 != 0) return DIFFATTN_E_UNSUPPORTED;
+  if (p->heads * 2 * d > 65536) return DIFFATTN_E_UNSUPPORTED;
+  if (p->batch * p->seqlen >= (int64_t(1) << 31)) return DIFFATTN_E_UNSUPPORTED;
+  // The GEMM numbers its 256 x 256 output tiles with 32-bit integers.
+  const int64_t m_tiles = (p->batch * p->seqlen + 255) / 256;
+  const int64_t n_widest = std::max<int64_t>(d_model, 6 * p->heads * d);
+  if (m_tiles * ((n_widest + 255) / 256) >= (int64_t(1) << 31)) return DIFFATTN_E_UNSUPPORTED;
+  return DIFFATTN_OK;
+}
+
+diffattn_status diffattn_qkv_proj(const diffattn_problem* p, int64_t d_model, const void* x,
+                                  const void* w_qkv, void* q1, void* q2, void* k1, void* k2,
+                                  void* v, void* stream) {
+  bool empty = false;
+  diffattn_status st = check_proj(p, d_model, &empty);
+  if (st != DIFFATTN_OK) return st;
+  if (empty) return DIFFATTN_OK;
+  const void* ptrs[7] = {x, w_qkv, q1, q2, k1, k2, v};
+  for (const void* ptr : ptrs)
+    if (!ptr || !aligned(ptr, 16)) return DIFFATTN_E_ARG;
+  const size_t m = static_cast<size_t>(p->batch) * p->seqlen;
+  const size_t hd = static_cast<size_t>(p->heads) * p->head_dim;
+  const Span in[2] = {{x, m * d_model * 2}, {w_qkv, 6 * hd * d_model * 2}};
+  const Span outs[5] = {{q1, m * hd * 2}, {q2, m * hd * 2}, {k1, m * hd * 2},
+                        {k2, m * hd * 2}, {v, m * hd * 4}};
+  if (any_overlap(outs, 5, in, 2)) return DIFFATTN_E_ARG;
+  diffattn::QkvProjArgs a;
+  a.x = x; a.w = w_qkv;
+  a.q1 = q1; a.q2 = q2; a.k1 = k1; a.k2 = k2; a.v = v;
+  a.B = p->batch; a.H = p->heads; a.N = p->seqlen; a.d_model = d_model;
+  a.d = p->head_dim;
+  return hip_status(diffattn::launch_qkv_proj_bf16(a, static_cast<hipStream_t>(stream)),
+                    "qkv_proj");
+}
+
+diffattn_status diffattn_out_proj(const diffattn_problem* p, int64_t d_model, const void* attn,
+                                  const void* w_o, void* y, void* stream) {
+  bool empty = false;
+  diffattn_status st = check_proj(p, d_model, &empty);
+  if (st != DIFFATTN_OK) return st;
+  if (empty) return DIFFATTN_OK;
+  const void* ptrs[3] = {attn, w_o, y};
+  for (const void* ptr : ptrs)
+    if (!ptr || !aligned(ptr, 16)) return DIFFATTN_E_ARG;
+  const size_t m = static_cast<size_t>(p->batch) * p->seqlen;
+  const size_t k = static_cast<size_t>(p->heads) * 2 * p->head_dim;
+  const Span in[2] = {{attn, m * k * 2}, {w_o, static_cast<size_t>(d_model) * k * 2}};
+  const Span outs[1] = {{y, m * d_model * 2}};
+  if (any_overlap(outs, 1, in, 2)) return DIFFATTN_E_ARG;
+  diffattn::OutProjArgs a;
+  a.attn = attn; a.w = w_o; a.y = y;
+  a.M = static_cast<int64_t>(m); a.d_model = d_model; a.k = static_cast<int64_t>(k);
+  return hip_status(diffattn::launch_out_proj_bf16(a, static_cast<hipStream_t>(stream)),
+                    "out_proj");
 }
 
 diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const void* q2,

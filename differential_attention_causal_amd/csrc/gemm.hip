@@ -1,0 +1,246 @@
+// The projections on either side of DiffAttn, as bf16 MFMA GEMMs (float32 accumulation).
+//
+// The input embeddings X are projected into two queries, two keys and one value per head
+// (Q1, Q2 from W_Q; K1, K2 from W_K; V from W_V), and the per-head outputs, concatenated
+// over heads, are projected back to the model width by W_O (intoai.pub, "Moving On To The
+// Differential Transformer" and "Differential Attention With Multiple Heads";
+// pt.news.hada.io, "Estrutura multi-head e arquitetura completa").
+//
+// One kernel computes C = A B^T for A [M, K] and B [Nc, K], both row-major with K
+// contiguous (B is a weight in the [out_features, in_features] layout), and writes C in
+// bf16 (round to nearest even) through one of two epilogues:
+//   plain  C row-major [M, Nc] (the W_O projection into [B, N, d_model]);
+//   qkv    the fused [3 H 2d, d_model] weight's columns scattered into Q1, Q2, K1, K2
+//          [B, H, N, d] and V [B, H, N, 2d]: column h 2d + j d + c of the query block is
+//          channel c of Q_(j+1) in head h, likewise for keys; column h 2d + c of the value
+//          block is channel c of V in head h. Row b N + i is token i of sequence b.
+//
+// Tiling: a 512-thread workgroup (8 waves, 4 x 2) computes a 256 x 256 tile of C in
+// K-steps of 64; each wave holds a 64 x 128 sub-tile as 2 x 4 accumulators of the
+// 32x32x16 bf16 MFMA. A and B K-slabs (32 KiB each) are copied global -> LDS by the
+// buffer unit (buffer_load ... lds), double-buffered, one barrier per K-step; operands are
+// read from LDS with 16-byte reads. Tiles are ordered in groups of four 256-row panels
+// (so the 32 tiles one XCD runs at a time share A and B slabs in its L2), and each XCD
+// is given a contiguous range of that order.
+#include "common.h"
+#include "launch.h"
+
+namespace diffattn {
+namespace gemm {
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NT = 512, NWAVE = 8;
+constexpr int SLAB = BM * BK * 2;          // bytes of one A (or B) K-slab: 32 KiB
+constexpr int STAGE = 2 * SLAB;            // A slab then B slab
+constexpr int LDS_BYTES = 2 * STAGE;       // two stages: 128 KiB
+constexpr int GROUP_M = 4;                 // 256-row panels per tile group
+static_assert(BM == BN, "A and B slabs share one layout");
+
+// Slab rows are 128 bytes (64 bf16 of K); the 16-byte unit u of row r is stored at
+// u ^ swz(r). The 32 rows that one operand read touches (lanes 0..31, then 32..63) then
+// fall into distinct bank groups: bits (b0 ^ b2, b1, b3) of the row pick the unit, so any
+// 8 consecutive rows use 8 different 16-byte slots of a 128-byte line and any 16 use 16
+// different slots of 256 bytes.
+__device__ __forceinline__ int swz(int row) {
+  return ((row ^ (row >> 2)) & 1) | (row & 2) | ((row >> 1) & 4);
+}
+
+// Buffer resource words (raw buffer, no swizzle) covering `bytes` bytes at `base`: loads
+// past the end return zeros, which pads the M and Nc tails of a tile.
+__device__ __forceinline__ u32x4 rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const u32x4 r = {static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes,
+                   0x00020000u};
+  return r;
+}
+
+// 16 bytes per lane from the buffer at byte offset voff into LDS at m0 + 16 lane. Issued
+// as assembly so the compiler does not make later LDS reads wait on it; the K-step
+// barrier orders the two. (m0 is used by nothing else in this kernel.)
+__device__ __forceinline__ void dma16(const u32x4& rs, uint32_t m0, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rs));
+}
+
+// This wave's share of one K-slab: 32 transfers of 1 KiB (8 rows each) per slab, four per
+// wave. Lane l of transfer t fills 16-byte slot l of its KiB: row 8 t + l / 8, stored
+// unit l % 8, which holds K unit (l % 8) ^ swz(row) of that row.
+__device__ __forceinline__ void load_slab(const u32x4& rs, uint32_t dst, int k0, int row_bytes,
+                                          int wv, int lane) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = wv + NWAVE * r;
+    const int row = 8 * t + (lane >> 3);
+    const int unit = (lane & 7) ^ swz(row);
+    dma16(rs, dst + 1024 * t, row * row_bytes + k0 * 2 + 16 * unit);
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_operand(uint32_t slab, int row, int unit) {
+  const int addr = static_cast<int>(slab) + row * 128 + 16 * (unit ^ swz(row));
+  return *reinterpret_cast<const LDS_AS bf16x8*>((LDS_AS char*)nullptr + addr);
+}
+
+struct QkvOut {
+  bf16_t *q1, *q2, *k1, *k2, *v;
+  uint32_t n;    // tokens per sequence
+  int h;         // heads
+  int d;         // width of Q1 / K1 (V is 2d)
+};
+
+// Column block [n, n + 32) of the fused projection (never straddling a head half, as d
+// is a multiple of 32): its destination tensor, offset by head and channel, and the row
+// stride there; row (b, i) then sits (b H N + i) rows further.
+__device__ __forceinline__ bf16_t* qkv_column(const QkvOut& o, int n, int& width) {
+  const int hd2 = 2 * o.d * o.h;
+  const int which = n / hd2, hc = n - which * hd2;
+  const int head = hc / (2 * o.d), within = hc - head * 2 * o.d;
+  const int64_t head_off = static_cast<int64_t>(head) * o.n;
+  if (which == 2) {
+    width = 2 * o.d;
+    return o.v + head_off * width + within;
+  }
+  const int half = within >= o.d;
+  width = o.d;
+  bf16_t* base = which == 0 ? (half ? o.q2 : o.q1) : (half ? o.k2 : o.k1);
+  return base + head_off * width + (within - half * o.d);
+}
+
+template <bool QKV>
+__global__ void __launch_bounds__(NT, 1)
+    gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bw,
+                     bf16_t* __restrict__ C, QkvOut qo, int64_t M, int Nc, int K) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (LDS bases in SGPRs)
+  const int wm = wv >> 1, wn = wv & 1;
+
+  // Tile of this workgroup: XCD x (= block id mod 8) takes a contiguous range of the
+  // grouped tile order.
+  const int m_tiles = static_cast<int>((M + BM - 1) / BM), n_tiles = (Nc + BN - 1) / BN;
+  const int T = m_tiles * n_tiles;
+  const int id = blockIdx.x, x = id & 7, q = T >> 3, rem = T & 7;
+  const int t = x * q + (x < rem ? x : rem) + (id >> 3);
+  const int per_group = GROUP_M * n_tiles;
+  const int g = t / per_group, in_g = t - g * per_group;
+  const int gm = min(GROUP_M, m_tiles - g * GROUP_M);
+  const int mt = g * GROUP_M + in_g % gm, nt = in_g / gm;
+  const int64_t m0 = static_cast<int64_t>(mt) * BM;
+  const int n0 = nt * BN;
+
+  const int64_t a_rows = min<int64_t>(BM, M - m0);
+  const int b_rows = min(BN, Nc - n0);
+  const u32x4 ra = rsrc(A + m0 * K, static_cast<uint32_t>(a_rows * K * 2));
+  const u32x4 rb = rsrc(Bw + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(b_rows) * K * 2);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)smem));
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int KT = K / BK;
+  load_slab(ra, lds0, 0, K * 2, wv, lane);
+  load_slab(rb, lds0 + SLAB, 0, K * 2, wv, lane);
+  const int r32 = lane & 31, hi = lane >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    // Slab kt has landed for this wave; after the barrier, for every wave, and every wave
+    // is done reading slab kt - 1, whose stage the next transfer overwrites.
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const uint32_t cur = lds0 + (kt & 1) * STAGE;
+    if (kt + 1 < KT) {
+      const uint32_t nxt = lds0 + ((kt + 1) & 1) * STAGE;
+      load_slab(ra, nxt, (kt + 1) * BK, K * 2, wv, lane);
+      load_slab(rb, nxt + SLAB, (kt + 1) * BK, K * 2, wv, lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int unit = 2 * kk + hi;
+      bf16x8 a[2], b[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = lds_operand(cur, 64 * wm + 32 * i + r32, unit);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = lds_operand(cur + SLAB, 128 * wn + 32 * j + r32, unit);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Accumulator element e of block (i, j): row 8 (e / 4) + 4 hi + e % 4, column r32.
+  bf16_t* col[4];
+  int width[4];
+  bool col_ok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 128 * wn + 32 * j;
+    col_ok[j] = n + r32 < Nc;
+    if (QKV) {
+      col[j] = (n < Nc ? qkv_column(qo, n, width[j]) : qo.q1) + r32;
+    } else {
+      col[j] = C + n + r32;
+      width[j] = Nc;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * hi + (e & 3);
+      if (m >= M) continue;
+      int64_t row = m;
+      if (QKV) {   // m = b N + i  ->  (b H + 0) N + i; the head is in col[j]
+        const uint32_t b = static_cast<uint32_t>(m) / qo.n;
+        row = static_cast<int64_t>(b) * (qo.h - 1) * qo.n + m;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (col_ok[j]) col[j][row * width[j]] = f32_to_bf16(acc[i][j][e]);
+    }
+  }
+}
+
+template <bool QKV>
+hipError_t launch(const bf16_t* A, const bf16_t* B, bf16_t* C, const QkvOut& qo, int64_t M,
+                  int Nc, int K, hipStream_t s) {
+  static bool attr_set = false;   // the attribute is per kernel, set once per process
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<QKV>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t tiles = ((M + BM - 1) / BM) * ((Nc + BN - 1) / BN);
+  hipLaunchKernelGGL(gemm_bf16_kernel<QKV>, dim3(static_cast<unsigned>(tiles)), dim3(NT),
+                     LDS_BYTES, s, A, B, C, qo, M, Nc, K);
+  return hipGetLastError();
+}
+
+}  // namespace gemm
+
+hipError_t launch_qkv_proj_bf16(const QkvProjArgs& a, hipStream_t s) {
+  gemm::QkvOut qo{static_cast<bf16_t*>(a.q1), static_cast<bf16_t*>(a.q2),
+                  static_cast<bf16_t*>(a.k1), static_cast<bf16_t*>(a.k2),
+                  static_cast<bf16_t*>(a.v),  static_cast<uint32_t>(a.N), static_cast<int>(a.H),
+                  a.d};
+  const int nc = static_cast<int>(3 * 2 * a.d * a.H);
+  return gemm::launch<true>(static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.w),
+                            nullptr, qo, a.B * a.N, nc, static_cast<int>(a.d_model), s);
+}
+
+hipError_t launch_out_proj_bf16(const OutProjArgs& a, hipStream_t s) {
+  gemm::QkvOut none{};
+  return gemm::launch<false>(static_cast<const bf16_t*>(a.attn), static_cast<const bf16_t*>(a.w),
+                             static_cast<bf16_t*>(a.y), none, a.M, static_cast<int>(a.d_model),
+                             static_cast<int>(a.k), s);
+}
+
+}  // namespace diffattn

@@ -57,6 +57,25 @@ struct AppendArgs {
   int64_t B, H, L;
 };
 
+// x [B, N, d_model] times the fused weight w [3 H 2d, d_model] (rows: W_Q, W_K, W_V),
+// scattered into q1, q2, k1, k2 [B, H, N, d] and v [B, H, N, 2d].
+struct QkvProjArgs {
+  const void *x, *w;
+  void *q1, *q2, *k1, *k2, *v;
+  int64_t B, H, N, d_model;
+  int d;
+};
+
+// y [M, d_model] = attn [M, k] times w [d_model, k] transposed.
+struct OutProjArgs {
+  const void *attn, *w;
+  void* y;
+  int64_t M, d_model, k;
+};
+
+hipError_t launch_qkv_proj_bf16(const QkvProjArgs& a, hipStream_t s);
+hipError_t launch_out_proj_bf16(const OutProjArgs& a, hipStream_t s);
+
 hipError_t launch_lambda(int dim, int layer, const float* lq1, const float* lk1,
                          const float* lq2, const float* lk2, diffattn_lambda_state* out,
                          hipStream_t s);

@@ -22,7 +22,8 @@ FP32, BF16 = 0, 1
 OP_FWD, OP_DECODE, OP_BWD = 0, 1, 2
 
 # Every symbol declared in include/diffattn.h.
-EXPORTS = ("diffattn_lambda", "diffattn_lambda_layers", "diffattn_fwd", "diffattn_decode", "diffattn_cache_append",
+EXPORTS = ("diffattn_lambda", "diffattn_lambda_layers", "diffattn_qkv_proj",
+           "diffattn_out_proj", "diffattn_fwd", "diffattn_decode", "diffattn_cache_append",
            "diffattn_bwd", "diffattn_workspace_bytes", "diffattn_status_string",
            "diffattn_last_hip_error")
 
@@ -73,6 +74,10 @@ def _lib():
         lib.diffattn_lambda_layers.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32, ctypes.c_float, P, P, P, P, P,
                                                P]
+        lib.diffattn_qkv_proj.restype = ctypes.c_int
+        lib.diffattn_qkv_proj.argtypes = [ctypes.POINTER(Problem), ctypes.c_int64] + [P] * 8
+        lib.diffattn_out_proj.restype = ctypes.c_int
+        lib.diffattn_out_proj.argtypes = [ctypes.POINTER(Problem), ctypes.c_int64] + [P] * 4
         lib.diffattn_fwd.restype = ctypes.c_int
         lib.diffattn_fwd.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P,
                                      ctypes.POINTER(Saved), P, ctypes.c_size_t, P]
@@ -186,6 +191,48 @@ def read_lambda_state(st: torch.Tensor) -> Dict[str, float]:
     v = struct.unpack(_STATE_FMT, raw)
     return {"lambda": v[0], "lambda_init": v[1], "exp_a": v[2], "exp_b": v[3],
             "lambda_f32": v[4], "lambda_init_f32": v[5], "one_minus_init_f32": v[6]}
+
+
+# ------------------------------------------------------------------ projections
+def qkv_proj(x, w_qkv, heads: int, head_dim: int, out=None):
+    """X [B, N, d_model] (bf16) times the fused weight [3 H 2d, d_model] (W_Q, W_K, W_V
+    rows). Returns (q1, q2, k1, k2 [B, H, N, d], v [B, H, N, 2d])."""
+    _need_cuda(x, w_qkv)
+    if x.dim() != 3 or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be contiguous bfloat16 [B, N, d_model]")
+    B, N, dm = x.shape
+    H, d = int(heads), int(head_dim)
+    if (tuple(w_qkv.shape) != (6 * H * d, dm) or w_qkv.dtype != torch.bfloat16
+            or not w_qkv.is_contiguous()):
+        raise ValueError("w_qkv must be contiguous bfloat16 [3 H 2d, d_model]")
+    if out is None:
+        f = dict(dtype=torch.bfloat16, device=x.device)
+        out = tuple(torch.empty(B, H, N, d, **f) for _ in range(4)) + \
+            (torch.empty(B, H, N, 2 * d, **f),)
+    p = problem(B, H, N, d, BF16)
+    _check("diffattn_qkv_proj", _lib().diffattn_qkv_proj(
+        ctypes.byref(p), dm, _ptr(x), _ptr(w_qkv), *(_ptr(t) for t in out),
+        _stream(x.device)))
+    return out
+
+
+def out_proj(attn, w_o, out=None):
+    """attn [B, N, H, 2d] (the forward's token-major output, bf16) times W_O^T, W_O
+    [d_model, H 2d]. Returns Y [B, N, d_model]."""
+    _need_cuda(attn, w_o)
+    if attn.dim() != 4 or attn.dtype != torch.bfloat16 or not attn.is_contiguous():
+        raise ValueError("attn must be contiguous bfloat16 [B, N, H, 2d]")
+    B, N, H, d2 = attn.shape
+    if (w_o.dim() != 2 or w_o.shape[1] != H * d2 or w_o.dtype != torch.bfloat16
+            or not w_o.is_contiguous()):
+        raise ValueError("w_o must be contiguous bfloat16 [d_model, H 2d]")
+    dm = w_o.shape[0]
+    if out is None:
+        out = torch.empty(B, N, dm, dtype=torch.bfloat16, device=attn.device)
+    p = problem(B, H, N, d2 // 2, BF16)
+    _check("diffattn_out_proj", _lib().diffattn_out_proj(
+        ctypes.byref(p), dm, _ptr(attn), _ptr(w_o), _ptr(out), _stream(attn.device)))
+    return out
 
 
 # ------------------------------------------------------------------ forward

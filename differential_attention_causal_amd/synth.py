@@ -135,3 +135,21 @@ def make_lambda_layers(n_layers: int, head_dim: int, device="cpu", seed: int = 0
     gen.manual_seed(seed)
     return {name: _normal(gen, (n_layers, head_dim), device).mul_(std)
             for name in ("lq1", "lk1", "lq2", "lk2")}
+
+
+def make_proj_inputs(batch: int, seqlen: int, heads: int, head_dim: int, d_model: int,
+                     device="cpu", seed: int = 0) -> Dict[str, torch.Tensor]:
+    """Inputs of the projections, bf16: x [B, N, d_model] standard normal, the fused
+    weight w_qkv [3 H 2d, d_model] normal with variance 1 / d_model and w_o
+    [d_model, H 2d] with variance 1 / (H 2d) (outputs of order one), and attn
+    [B, N, H, 2d] standard normal (an input of the output projection)."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    hd2 = 2 * heads * head_dim
+    bf = torch.bfloat16
+    out = {"x": _normal(gen, (batch, seqlen, d_model), device).to(bf)}
+    out["w_qkv"] = _normal(gen, (3 * hd2, d_model), device).mul_(d_model ** -0.5).to(bf)
+    out["w_o"] = _normal(gen, (d_model, hd2), device).mul_(hd2 ** -0.5).to(bf)
+    out["attn"] = _normal(gen, (batch, seqlen, heads, 2 * head_dim), device).to(bf)
+    return out

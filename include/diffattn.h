@@ -204,6 +204,35 @@ diffattn_status diffattn_cache_append(const diffattn_problem* p, const void* k1_
                                       const void* k2_new, const void* v_new, void* k1c,
                                       void* k2c, void* vc, int32_t* cache_len, void* stream);
 
+/* The input projection of multi-head DiffAttn: the embeddings X are projected into two
+ * queries, two keys and one value per head (intoai.pub, "Moving On To The Differential
+ * Transformer": X times W_Q, W_K, W_V, with Q and K split into two groups; "Differential
+ * Attention With Multiple Heads": separate projections per head). One bf16 MFMA GEMM,
+ * float32 accumulation, outputs rounded once to bf16 (nearest even).
+ *   x       [B, N, d_model] (p->batch, p->seqlen)
+ *   w_qkv   [3 H 2d, d_model], the fused weight in the [out_features, in_features] layout:
+ *           rows [0, H 2d) are W_Q, then W_K, then W_V. Row h 2d + j d + c of W_Q gives
+ *           channel c of Q_(j+1) in head h (j = 0, 1), likewise for W_K; row h 2d + c of
+ *           W_V gives channel c of V in head h.
+ *   q1, q2, k1, k2 [B, H, N, d];  v [B, H, N, 2d]   (outputs, the forward's input layout)
+ * bf16 only; d a multiple of 32 (at most 256); d_model a multiple of 64 in [64, 65536];
+ * H 2d <= 65536; B N < 2^31. Pointers 16-byte aligned; outputs must not overlap each
+ * other or the inputs (E_ARG). No workspace. */
+diffattn_status diffattn_qkv_proj(const diffattn_problem* p, int64_t d_model, const void* x,
+                                  const void* w_qkv, void* q1, void* q2, void* k1, void* k2,
+                                  void* v, void* stream);
+
+/* The output projection: the per-head outputs, concatenated over heads along the channel
+ * dimension, times W_O back to the model width (intoai.pub, "Differential Attention With
+ * Multiple Heads"; pt.news.hada.io, "Estrutura multi-head e arquitetura completa").
+ *   attn    [B, N, H 2d]: diffattn_fwd's output in the token-major layout
+ *           (p->out_layout = DIFFATTN_LAYOUT_BNH)
+ *   w_o     [d_model, H 2d] ([out_features, in_features])
+ *   y       [B, N, d_model] (output)
+ * bf16 only, float32 accumulation; the same shape limits as diffattn_qkv_proj. */
+diffattn_status diffattn_out_proj(const diffattn_problem* p, int64_t d_model, const void* attn,
+                                  const void* w_o, void* y, void* stream);
+
 /* Backward of the forward above for the loss sum(Y * dout), recomputing A1 and A2 from
  * the saved log-sum-exps. The pages print no gradient formulas; these follow from the
  * forward by the chain rule:

@@ -341,6 +341,46 @@ def cache_append(k1_new, k2_new, v_new, k1c, k2c, vc, cache_len):
 
 
 # --------------------------------------------------------------------------
+# projections
+# --------------------------------------------------------------------------
+def qkv_proj(x, w_qkv, heads: int, head_dim: int):
+    """The input projections: X times W_Q, W_K, W_V ([INTOAI] "Moving On To The
+    Differential Transformer": Q and K are each split into two groups; "Differential
+    Attention With Multiple Heads": two queries, two keys and a value per head).
+
+    x [B, N, d_model]; w_qkv [3 H 2d, d_model] in the [out_features, in_features]
+    layout, rows W_Q, then W_K, then W_V. Reading (the pages fix no column order):
+    row h 2d + j d + c of W_Q gives channel c of Q_(j+1) in head h, likewise for W_K,
+    and row h 2d + c of W_V gives channel c of V in head h.
+    Returns q1, q2, k1, k2 [B, H, N, d] and v [B, H, N, 2d], in float64.
+    """
+    x, w = _f64(x), _f64(w_qkv)
+    B, N, dm = x.shape
+    H, d = heads, head_dim
+    if w.shape != (6 * H * d, dm):
+        raise ValueError("w_qkv must be [3 H 2d, d_model]")
+    y = x @ w.T                                   # [B, N, 3 H 2d]
+    hd2 = 2 * H * d
+    q = y[..., :hd2].reshape(B, N, H, 2, d)
+    k = y[..., hd2:2 * hd2].reshape(B, N, H, 2, d)
+    v = y[..., 2 * hd2:].reshape(B, N, H, 2 * d)
+    per_head = lambda t: np.ascontiguousarray(t.transpose(0, 2, 1, 3))   # [B, H, N, *]
+    return (per_head(q[..., 0, :]), per_head(q[..., 1, :]), per_head(k[..., 0, :]),
+            per_head(k[..., 1, :]), per_head(v))
+
+
+def out_proj(attn, w_o):
+    """The output projection: the heads' outputs concatenated along channels, times
+    W_O ([INTOAI] "Differential Attention With Multiple Heads"; [HADA] "Estrutura
+    multi-head e arquitetura completa"). attn [B, N, H, 2d] (token-major, head h at
+    channels h 2d .. h 2d + 2d - 1 of the concatenation); w_o [d_model, H 2d].
+    Returns [B, N, d_model] in float64."""
+    a = _f64(attn)
+    B, N, H, d2 = a.shape
+    return a.reshape(B, N, H * d2) @ _f64(w_o).T
+
+
+# --------------------------------------------------------------------------
 # backward (derived by the chain rule; the pages print no gradient formulas)
 # --------------------------------------------------------------------------
 def head_backward(q1, q2, k1, k2, v, dy, lam: float, lam_init: float,
@@ -357,7 +397,8 @@ def head_backward(q1, q2, k1, k2, v, dy, lam: float, lam_init: float,
       dS_k = A_k * (dA_k - rowsum(A_k * dA_k))      (softmax Jacobian)
       dQ_k = s dS_k K_k,   dK_k = s dS_k^T Q_k
       dlam = -sum(A2 * (G V^T)) = -sum_i rowsum(G * O2)
-    Returns a dict with dq1, dq2, dk1, dk2, dv, d_attn (= G) and dlam.
+      dw = (1 - lam_init) * sum over rows of dY * O * r   (the RMSNorm weight)
+    Returns a dict with dq1, dq2, dk1, dk2, dv, d_attn (= G), dw and dlam.
     """
     q1, q2, k1, k2, v, dy = (_f64(x) for x in (q1, q2, k1, k2, v, dy))
     n, d = q1.shape
@@ -379,6 +420,7 @@ def head_backward(q1, q2, k1, k2, v, dy, lam: float, lam_init: float,
         "dq1": s * ds1 @ k1, "dk1": s * ds1.T @ q1,
         "dq2": s * ds2 @ k2, "dk2": s * ds2.T @ q2,
         "dv": dv, "d_attn": G, "dlam": float(-np.sum(a2 * gv)),
+        "dw": (1.0 - lam_init) * np.sum(dy * o * r, axis=0),
     }
 
 
@@ -391,6 +433,8 @@ def backward(q1, q2, k1, k2, v, dy, lq1, lk1, lq2, lk2, layer: int,
       dlq1 = dlam e^a lk1, dlk1 = dlam e^a lq1,
       dlq2 = -dlam e^b lk2, dlk2 = -dlam e^b lq2.
     lambda_init is a constant of the layer index and receives no gradient.
+    d_rms_weight [H, 2d] sums each head's dw over the batch (the weight is one
+    per head and channel).
     ``heads`` restricts the per-head tensors to the listed (b, h) pairs (the
     others stay NaN); dlam and the vector gradients then cover only those.
     """
@@ -402,6 +446,7 @@ def backward(q1, q2, k1, k2, v, dy, lq1, lk1, lq2, lk2, layer: int,
     out = {k: np.full((B, H, N, d), np.nan) for k in ("dq1", "dq2", "dk1", "dk2")}
     out["dv"] = np.full((B, H, N, dvw), np.nan)
     out["d_attn"] = np.full((B, H, N, dvw), np.nan)
+    out["d_rms_weight"] = np.zeros((H, dvw))
     dlam = 0.0
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
@@ -410,6 +455,7 @@ def backward(q1, q2, k1, k2, v, dy, lq1, lk1, lq2, lk2, layer: int,
                           lam, li, eps, w)
         for k in ("dq1", "dq2", "dk1", "dk2", "dv", "d_attn"):
             out[k][b, h] = r[k]
+        out["d_rms_weight"][h] += r["dw"]
         dlam += r["dlam"]
     lq1, lk1, lq2, lk2 = (_f64(x) for x in (lq1, lk1, lq2, lk2))
     out["dlam"] = dlam

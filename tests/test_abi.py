@@ -259,3 +259,30 @@ def test_workspace_queries():
     assert n % (64 * 16 * 2 * 130 * 4) == 0
     bad = da.problem(-1, 1, 1, 64, da.BF16)
     assert da.workspace_bytes(da.OP_BWD, bad) == 0
+
+
+def test_projection_argument_checks():
+    lib = da.lib()
+    ptr = [addr(i * 64) for i in range(7)]
+    p = da.problem(1, 16, 1024, 64, da.BF16)
+    qkv = lambda p, dm, ptrs: lib.diffattn_qkv_proj(ctypes.byref(p), dm, *ptrs, None)
+    outp = lambda p, dm, ptrs: lib.diffattn_out_proj(ctypes.byref(p), dm, *ptrs, None)
+    assert qkv(p, 100, ptr) == da.E_UNSUPPORTED            # d_model not a multiple of 64
+    assert qkv(p, 32, ptr) == da.E_ARG
+    assert qkv(p, 1 << 17, ptr) == da.E_ARG
+    assert qkv(da.problem(1, 16, 1024, 64, da.FP32), 2048, ptr) == da.E_UNSUPPORTED
+    assert qkv(da.problem(1, 16, 1024, 48, da.BF16), 2048, ptr) == da.E_UNSUPPORTED
+    assert qkv(da.problem(0, 16, 1024, 64, da.BF16), 2048, [None] * 7) == da.OK
+    bad = list(ptr); bad[3] = None
+    assert qkv(p, 2048, bad) == da.E_ARG
+    bad = list(ptr); bad[0] = ctypes.c_void_p(A + 8)      # x misaligned
+    assert qkv(p, 2048, bad) == da.E_ARG
+    bad = list(ptr); bad[6] = ptr[0]                      # v aliases x
+    assert qkv(p, 2048, bad) == da.E_ARG
+    bad = list(ptr); bad[3] = ptr[2]                      # q2 aliases q1
+    assert qkv(p, 2048, bad) == da.E_ARG
+    assert outp(p, 96, ptr[:3]) == da.E_UNSUPPORTED
+    bad = [ptr[0], ptr[1], ptr[0]]                        # y aliases attn
+    assert outp(p, 2048, bad) == da.E_ARG
+    # more rows than the GEMM takes
+    assert qkv(da.problem(1 << 16, 1, 1 << 15, 64, da.BF16), 2048, ptr) == da.E_UNSUPPORTED

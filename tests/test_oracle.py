@@ -315,6 +315,22 @@ def _fd_check(n, d, B, H, layer, n_samples, seed, weight_on):
         an = g[gname].reshape(-1)[idx]
         scale = max(np.max(np.abs(an)), 1e-12)
         assert np.max(np.abs(an - fd)) / scale < 2e-6, name
+    # the RMSNorm weight (one per head and channel), perturbed entry by entry
+    if weight is not None:
+        flat = weight.reshape(-1)
+        idx = np.arange(flat.size) if flat.size <= n_samples else \
+            r.choice(flat.size, n_samples, replace=False)
+        fd = np.empty(len(idx))
+        for t, i in enumerate(idx):
+            old = flat[i]
+            flat[i] = old + h
+            lp = _loss(p, dy, layer, eps, weight)
+            flat[i] = old - h
+            lm = _loss(p, dy, layer, eps, weight)
+            flat[i] = old
+            fd[t] = (lp - lm) / (2 * h)
+        an = g["d_rms_weight"].reshape(-1)[idx]
+        assert np.max(np.abs(an - fd)) / max(np.max(np.abs(an)), 1e-12) < 2e-6, "weight"
     # gradient at the RMSNorm input: perturb O directly through the norm
     st = orc.lambda_scalar(p["lq1"], p["lk1"], p["lq2"], p["lk2"], layer)
     _, sv = orc.forward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"], st["lambda"],
@@ -518,6 +534,60 @@ def _pin_failures(m):
         an = g["d" + name].reshape(-1)
         if np.max(np.abs(an - fd)) > 1e-5 * max(np.max(np.abs(fd)), 1e-9):
             fails.append("fd " + name)
+    # the RMSNorm weight gradient, by central differences of the same loss
+    wgt = 1.0 + 0.3 * rand(r, H, 2 * d)
+    gw = m.backward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"], dy, p["lq1"], p["lk1"],
+                    p["lq2"], p["lk2"], 3, weight=wgt)["d_rms_weight"]
+    st = m.lambda_scalar(p["lq1"], p["lk1"], p["lq2"], p["lk2"], 3)
+    fdw = np.empty(wgt.size)
+    for j in range(wgt.size):
+        old = wgt.flat[j]
+        wgt.flat[j] = old + h
+        lp = float(np.sum(m.forward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"], st["lambda"],
+                                    st["lambda_init"], weight=wgt) * dy))
+        wgt.flat[j] = old - h
+        lm = float(np.sum(m.forward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"], st["lambda"],
+                                    st["lambda_init"], weight=wgt) * dy))
+        wgt.flat[j] = old
+        fdw[j] = (lp - lm) / (2 * h)
+    if np.max(np.abs(gw.reshape(-1) - fdw)) > 1e-5 * max(np.max(np.abs(fdw)), 1e-9):
+        fails.append("fd rms weight")
+    # projections. One-hot tokens: token t of the flattened batch is unit vector
+    # e_(t mod d_model), so each output entry is one weight entry; the weight is coded
+    # w[row, col] = row + 1000 col, which names the weight row that fed each output.
+    B, N, H, d, dm = 2, 3, 2, 4, 8
+    x = np.zeros((B, N, dm))
+    for t in range(B * N):
+        x.reshape(B * N, dm)[t, t % dm] = 1.0
+    w = np.add.outer(np.arange(6 * H * d), 1000.0 * np.arange(dm))
+    q1, q2, k1, k2, v = m.qkv_proj(x, w, H, d)
+    hd2 = 2 * H * d
+    ok = True
+    for b in range(B):
+        for i in range(N):
+            col = 1000.0 * ((b * N + i) % dm)
+            for hh in range(H):
+                for c in range(d):
+                    base = hh * 2 * d + c
+                    ok &= q1[b, hh, i, c] == base + col and q2[b, hh, i, c] == base + d + col
+                    ok &= k1[b, hh, i, c] == hd2 + base + col
+                    ok &= k2[b, hh, i, c] == hd2 + base + d + col
+                for c in range(2 * d):
+                    ok &= v[b, hh, i, c] == 2 * hd2 + hh * 2 * d + c + col
+    if not ok:
+        fails.append("qkv projection placement")
+    # output projection: brute-force sums over the concatenated channels
+    attn = rand(r, B, N, H, 2 * d)
+    wo = rand(r, 5, H * 2 * d)
+    y = m.out_proj(attn, wo)
+    for b, i, o in [(0, 0, 0), (1, 2, 4), (0, 1, 3)]:
+        acc = 0.0
+        for hh in range(H):
+            for c in range(2 * d):
+                acc += attn[b, i, hh, c] * wo[o, hh * 2 * d + c]
+        if abs(y[b, i, o] - acc) > 1e-12:
+            fails.append("out projection sum")
+            break
     return fails
 
 
@@ -552,6 +622,14 @@ PLANTS = [
     ("dK transposed", '"dk1": s * ds1.T @ q1', '"dk1": s * ds1 @ q1'),
     ("dS2 uses A1", "ds2 = a2 * (da2 - np.sum(a2 * da2", "ds2 = a2 * (da2 - np.sum(a1 * da2"),
     ("dlq2 sign", 'out["dlq2"] = -dlam * st["exp_b"] * lk2', 'out["dlq2"] = dlam * st["exp_b"] * lk2'),
+    ("rms weight gradient without r", '"dw": (1.0 - lam_init) * np.sum(dy * o * r, axis=0)',
+     '"dw": (1.0 - lam_init) * np.sum(dy * o, axis=0)'),
+    ("query halves swapped", "return (per_head(q[..., 0, :]), per_head(q[..., 1, :]),",
+     "return (per_head(q[..., 1, :]), per_head(q[..., 0, :]),"),
+    ("value block from the key rows", "v = y[..., 2 * hd2:].reshape", "v = y[..., hd2:2 * hd2].reshape"),
+    ("projection not transposed", "y = x @ w.T ", "y = x @ w.reshape(dm, -1) "),
+    ("heads concatenated in reverse", "return a.reshape(B, N, H * d2) @",
+     "return a[:, :, ::-1].reshape(B, N, H * d2) @"),
     ("dlam sign", '"dlam": float(-np.sum(a2 * gv))', '"dlam": float(np.sum(a2 * gv))'),
 ]
 
