@@ -11,6 +11,11 @@ Also reported in the same line:
             8192 tokens: HBM GB/s = (cache + query + output bytes) / step time.
   train   - forward (with saves) + backward on B8 H12 N4096 when the backward
             kernels are present: TFLOP/s under 12 d P + 20 d P per head.
+  proj    - the projection GEMMs at the forward workload's shape (d_model = H 2d = 2048):
+            the fused QKV projection (X [32768, 2048] x W [6144, 2048]^T, scattered into
+            Q1/Q2/K1/K2/V) and the output projection (token-major Y [32768, 2048] x W_O^T),
+            TFLOP/s at 2 M N K each against the bf16 peak, and the whole module step
+            (projection, lambda, forward with token-major output, projection).
   copy    - a plain 2 GiB device-to-device copy: the HBM rate this machine reaches,
             and the kernel the HBM byte counters are calibrated on.
   roofline - for the dominant kernel (the forward), achieved TFLOP/s from HIP
@@ -21,7 +26,8 @@ Also reported in the same line:
             forward workload (query rows from the last one down, head by head,
             ~12 s of CPU work).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs fwd,decode,train,copy]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--legs fwd,decode,train,proj,copy]
                        [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -207,6 +213,50 @@ def leg_train(steps, warmup):
     }
 
 
+def leg_proj(steps, warmup):
+    import torch
+    from differential_attention_causal_amd import diffattn as da
+    from differential_attention_causal_amd import synth
+    w = synth.WORKLOADS[3]
+    B, N, H, d = w.batch, w.seqlen, w.heads, w.head_dim
+    dm = 2 * H * d
+    x = synth.make_proj_inputs(B, N, H, d, dm, "cuda:0", seed=5)
+    lv = synth.make_inputs(w, "cuda:0")     # the forward workload's lambda vectors
+    qkv = da.qkv_proj(x["x"], x["w_qkv"], H, d)
+    y = torch.empty(B, N, H, 2 * d, dtype=torch.bfloat16, device="cuda:0")
+    out = torch.empty(B, N, dm, dtype=torch.bfloat16, device="cuda:0")
+    p = da.problem(B, H, N, d, da.BF16)
+    ws = torch.empty(da.workspace_bytes(da.OP_FWD, p), dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn, fl in (
+            ("qkv_proj", lambda: da.qkv_proj(x["x"], x["w_qkv"], H, d, out=qkv),
+             2.0 * B * N * dm * 6 * H * d),
+            ("out_proj", lambda: da.out_proj(x["attn"], x["w_o"], out=out),
+             2.0 * B * N * dm * 2 * H * d)):
+        def step(ev, fn=fn):
+            if ev:
+                ev[0].record()
+            fn()
+            if ev:
+                ev[1].record()
+        ms, wall, inner = time_steps(step, steps, warmup, inner_events=True)
+        k_ms = sum(inner) / len(inner)
+        tf = fl / (k_ms * 1e-3) / 1e12
+        res[name] = {"us": k_ms * 1e3, "tflops": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS}
+
+    def module(ev):
+        q1, q2, k1, k2, v = da.qkv_proj(x["x"], x["w_qkv"], H, d, out=qkv)
+        st = da.lambda_(lv["lq1"], lv["lk1"], lv["lq2"], lv["lk2"], w.layer)
+        da.forward(q1, q2, k1, k2, v, st, out=y, workspace=ws, layout="bnh")
+        da.out_proj(y, x["w_o"], out=out)
+
+    ms, wall, _ = time_steps(module, max(1, steps // 2), warmup)
+    res["shape"] = f"B{B} N{N} H{H} d{d} d_model {dm}"
+    res["module_ms"] = ms
+    return res
+
+
 def leg_copy(steps, warmup):
     """A plain 2 GiB device-to-device copy: the measured HBM reference, and the kernel the
     FETCH_SIZE / WRITE_SIZE counters are calibrated on."""
@@ -308,7 +358,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="fwd,decode,train,copy")
+    ap.add_argument("--legs", default="fwd,decode,train,proj,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -339,6 +389,8 @@ def main():
         rec["decode"] = leg_decode(args.steps, args.warmup)
     if "train" in legs:
         rec["train"] = leg_train(max(1, args.steps // 2), args.warmup)
+    if "proj" in legs:
+        rec["proj"] = leg_proj(args.steps, args.warmup)
     if "copy" in legs:
         rec["copy"] = leg_copy(args.steps, args.warmup)
     if not args.no_cpu_baseline:

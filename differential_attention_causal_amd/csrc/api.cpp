@@ -74,6 +74,8 @@ diffattn_status check_problem(const diffattn_problem* p, bool* empty) {
   if (p->head_dim <= 0) return DIFFATTN_E_ARG;
   if (p->dtype != DIFFATTN_FP32 && p->dtype != DIFFATTN_BF16) return DIFFATTN_E_ARG;
   if (!(p->rms_eps >= 0.0f) || !isfinite(p->rms_eps)) return DIFFATTN_E_ARG;
+  if (p->out_layout != DIFFATTN_LAYOUT_BHN && p->out_layout != DIFFATTN_LAYOUT_BNH)
+    return DIFFATTN_E_ARG;
   if (p->causal != 1) return DIFFATTN_E_UNSUPPORTED;
   // Largest tensor: [B, H, N, 2d] float32 must stay far from int64 overflow.
   int64_t t = 0;
@@ -228,6 +230,7 @@ diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const vo
   a.B = p->batch; a.H = p->heads; a.N = p->seqlen;
   a.d = d;
   a.eps = p->rms_eps;
+  a.out_bnh = p->out_layout == DIFFATTN_LAYOUT_BNH;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (p->dtype == DIFFATTN_FP32) return hip_status(diffattn::launch_fwd_fp32(a, s), "fwd_fp32");
   return hip_status(diffattn::launch_fwd_bf16(a, s), "fwd_bf16");
@@ -381,7 +384,8 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
                              const diffattn_saved* saved, const void* dout, void* dq1,
                              void* dq2, void* dk1, void* dk2, void* dv, float* d_attn,
                              float* dlq1, float* dlk1, float* dlq2, float* dlk2,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             float* d_rms_weight, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   bool empty = false;
   diffattn_status st = check_problem(p, &empty);
   if (st != DIFFATTN_OK) return st;
@@ -407,7 +411,8 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
   for (const void* x : p4)
     if (!aligned(x, 4)) return DIFFATTN_E_ARG;
   if (!aligned(dlq1, 4) || !aligned(dlk1, 4) || !aligned(dlq2, 4) || !aligned(dlk2, 4) ||
-      !aligned(lam, 8) || (rms_weight && !aligned(rms_weight, 16)))
+      !aligned(lam, 8) || (rms_weight && !aligned(rms_weight, 16)) ||
+      (d_rms_weight && !aligned(d_rms_weight, 4)))
     return DIFFATTN_E_ARG;
   const size_t need = diffattn_workspace_bytes(DIFFATTN_OP_BWD, p);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DIFFATTN_E_WORKSPACE;
@@ -421,10 +426,12 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
                        {lam, sizeof(diffattn_lambda_state)},
                        {rms_weight, static_cast<size_t>(p->heads) * 2 * d * sizeof(float)},
                        {s.lse1, rb}, {s.lse2, rb}, {s.o1, ob}, {s.o2, ob}};
-  const Span outs[11] = {{dq1, qk}, {dq2, qk}, {dk1, qk}, {dk2, qk}, {dv, vb}, {d_attn, ob},
-                         {dlq1, lb}, {dlk1, lb}, {dlq2, lb}, {dlk2, lb}, {workspace, need}};
-  if (any_overlap(outs, 11, in, 16) || overlap(outs[0], {s.rstd, rb})) return DIFFATTN_E_ARG;
-  for (int i = 0; i < 11; ++i)
+  const size_t wb = static_cast<size_t>(p->heads) * 2 * d * sizeof(float);
+  const Span outs[12] = {{dq1, qk}, {dq2, qk}, {dk1, qk}, {dk2, qk}, {dv, vb}, {d_attn, ob},
+                         {dlq1, lb}, {dlk1, lb}, {dlq2, lb}, {dlk2, lb}, {workspace, need},
+                         {d_rms_weight, wb}};
+  if (any_overlap(outs, 12, in, 16)) return DIFFATTN_E_ARG;
+  for (int i = 0; i < 12; ++i)
     if (overlap(outs[i], {s.rstd, rb})) return DIFFATTN_E_ARG;
   diffattn::BwdArgs a;
   memset(&a, 0, sizeof(a));
@@ -436,6 +443,8 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
   a.dq1 = dq1; a.dq2 = dq2; a.dk1 = dk1; a.dk2 = dk2; a.dv = dv;
   a.d_attn = d_attn;
   a.dlq1 = dlq1; a.dlk1 = dlk1; a.dlq2 = dlq2; a.dlk2 = dlk2;
+  a.d_rms_weight = d_rms_weight;
+  a.dout_bnh = p->out_layout == DIFFATTN_LAYOUT_BNH;
   a.ws = static_cast<float*>(workspace);
   a.B = empty ? 0 : p->batch; a.H = p->heads; a.N = p->seqlen;
   a.d = d;

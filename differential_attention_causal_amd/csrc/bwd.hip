@@ -16,6 +16,8 @@
 //   dlambda = -sum over rows of D2; lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init gives
 //   dlq1 = dlambda e^a lk1, dlk1 = dlambda e^a lq1, dlq2 = -dlambda e^b lk2,
 //   dlk2 = -dlambda e^b lq2                               (lambda_grad_kernel)
+//   dw_h = (1 - lambda_init) sum over (b, i) of dout O r  (bwd_pre_kernel partials,
+//                                                          rms_weight_grad_kernel)
 // A_k is recomputed from the log-sum-exps the forward saved: A_k = exp(S_k - lse_k).
 //
 // Two matrix-core kernels, no atomics (deterministic). Both have the same shape:
@@ -265,26 +267,39 @@ __device__ __forceinline__ void a_product(f32x16& s1, f32x16& s2, f32x16& dp, co
 // 64 rows per workgroup, 8 at a time, 32 threads per row, 4 channels per thread.
 // Writes G (float32 to d_attn, bf16 to gb), the per-row vector (lse1 log2 e, lse2 log2 e,
 // D1, D2) the main kernels read, and one partial sum of D2 per workgroup.
+// Workgroup blk covers rows n0 .. n0 + 63 (n0 = 64 (blk % nchunk)) of head bh = blk / nchunk,
+// 8 rows at a time, 32 lanes per row with 4 channels each. Besides G, the bf16 copy of G
+// and the per-row vector, it writes part[blk] = the sum of D2 over its rows and
+// pw[blk] = its rows' share of the RMSNorm weight gradient (2d floats), both summed in a
+// fixed order.
 __global__ void __launch_bounds__(256) bwd_pre_kernel(
     const float* __restrict__ o1, const float* __restrict__ o2, const float* __restrict__ rstd,
     const float* __restrict__ lse1, const float* __restrict__ lse2,
     const bf16_t* __restrict__ dout, const diffattn_lambda_state* __restrict__ lamst,
     const float* __restrict__ rms_w, float* __restrict__ d_attn, bf16_t* __restrict__ gb,
-    f32x4* __restrict__ vec, float* __restrict__ part, int64_t rows, int64_t N, int64_t H) {
+    f32x4* __restrict__ vec, float* __restrict__ part, f32x4* __restrict__ pw, int64_t N,
+    int64_t H, int64_t nchunk, int dout_bnh) {
   __shared__ float red[8];
+  __shared__ f32x4 redw[8][32];
   const int tid = threadIdx.x;
   const int t = tid & 31;
   const float lam = lamst->lambda_f;
   const float gsc = lamst->one_minus_init_f;
+  const int64_t blk = blockIdx.x;
+  const int64_t bh = blk / nchunk;
+  const int64_t n0 = (blk - bh * nchunk) * 64;
+  const int64_t hh = bh % H, bb = bh / H;
   float d2 = 0.f;
+  f32x4 dw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
   for (int it = 0; it < 8; ++it) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + 8 * it + (tid >> 5);
-    if (r >= rows) break;
-    const int64_t hh = (r / N) % H;
+    const int64_t n = n0 + 8 * it + (tid >> 5);
+    if (n >= N) break;
+    const int64_t r = bh * N + n;
+    const int64_t yr = dout_bnh ? (bb * N + n) * H + hh : r;   // dout row in its layout
     const f32x4 a = *reinterpret_cast<const f32x4*>(o1 + r * DV + 4 * t);
     const f32x4 b = *reinterpret_cast<const f32x4*>(o2 + r * DV + 4 * t);
-    const u32x2 dy = *reinterpret_cast<const u32x2*>(dout + r * DV + 4 * t);
+    const u32x2 dy = *reinterpret_cast<const u32x2*>(dout + yr * DV + 4 * t);
     f32x4 w = {1.f, 1.f, 1.f, 1.f};
     if (rms_w) w = *reinterpret_cast<const f32x4*>(rms_w + hh * DV + 4 * t);
     const float dyv[4] = {__uint_as_float(dy[0] << 16), __uint_as_float(dy[0] & 0xffff0000u),
@@ -296,6 +311,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(
       o[e] = a[e] - lam * b[e];
       g[e] = gsc * w[e] * dyv[e];
       go = fmaf(g[e], o[e], go);
+      dw[e] = fmaf(gsc * dyv[e], o[e] * rs, dw[e]);
     }
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1) go += __shfl_xor(go, off);
@@ -335,12 +351,46 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(
     d2 += dd2f;
   }
   if (t == 0) red[tid >> 5] = d2;
+  redw[tid >> 5][t] = dw;
   __syncthreads();
   if (tid == 0) {
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) s += red[i];
-    part[blockIdx.x] = s;   // sum of D2 (float32 G) over this block's rows
+    part[blk] = s;   // sum of D2 (float32 G) over this block's rows
+  }
+  if (tid < 32) {
+    f32x4 s = redw[0][tid];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) s += redw[i][tid];
+    pw[blk * 32 + tid] = s;   // channels 4 tid .. 4 tid + 3
+  }
+}
+
+// d_rms_weight[h, c] = the sum of head h's partials over (b, chunk), in float64 and in a
+// fixed order: thread group g (of 32) sums partials q = g, g + 32, ... (q = b nchunk +
+// chunk), then the 32 group sums are added in order. Workgroup (h, 8-channel slice),
+// thread 8 g + channel.
+constexpr int WG_GROUPS = 32, WG_CH = 8;
+__global__ void __launch_bounds__(WG_GROUPS * WG_CH) rms_weight_grad_kernel(
+    const float* __restrict__ pw, int64_t B, int64_t H, int64_t nchunk, float* __restrict__ dw) {
+  __shared__ double red[WG_GROUPS][WG_CH];
+  const int64_t h = blockIdx.x;
+  const int c = blockIdx.y * WG_CH + threadIdx.x % WG_CH, g = threadIdx.x / WG_CH;
+  const int64_t nq = B * nchunk;
+  double s = 0.0;
+#pragma unroll 4
+  for (int64_t q = g; q < nq; q += WG_GROUPS) {
+    const int64_t b = q / nchunk, k = q - b * nchunk;
+    s += static_cast<double>(pw[((b * H + h) * nchunk + k) * DV + c]);
+  }
+  red[g][threadIdx.x % WG_CH] = s;
+  __syncthreads();
+  if (g == 0) {
+    double t = red[0][threadIdx.x];
+#pragma unroll
+    for (int i = 1; i < WG_GROUPS; ++i) t += red[i][threadIdx.x];
+    dw[h * DV + c] = static_cast<float>(t);
   }
 }
 
@@ -1112,10 +1162,15 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
 
 // Workspace (floats): bf16 G [rows, 128] (64 floats per row), the per-row vector
 // (lse1 log2 e, lse2 log2 e, D1, D2) [rows, 4], and one partial sum of D2 per 64 rows.
+// Workspace (float32 words): G in bf16 [rows, 2d] | per-row vectors [rows, 4] |
+// D2 partials [nparts, padded to 4] | weight-gradient partials [nparts, 2d] | 64 spare;
+// nparts = B H ceil(N / 64) (one per bwd_pre_kernel workgroup).
 size_t bwd_workspace_floats(int64_t B, int64_t H, int64_t N, int d) {
   (void)d;
   const int64_t rows = B * H * N;
-  return static_cast<size_t>(rows) * (bwd::DV / 2 + 4) + static_cast<size_t>((rows + 63) / 64) + 64;
+  const int64_t nparts = B * H * ((N + 63) / 64);
+  return static_cast<size_t>(rows) * (bwd::DV / 2 + 4) +
+         static_cast<size_t>((nparts + 3) / 4 * 4) + static_cast<size_t>(nparts) * bwd::DV + 64;
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
@@ -1131,15 +1186,18 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     attr_set = true;
   }
   const int64_t rows = a.B * a.H * a.N;
-  const int64_t nparts = (rows + 63) / 64;
+  const int64_t nchunk = (a.N + 63) / 64;
+  const int64_t nparts = a.B * a.H * nchunk;
   bf16_t* gbuf = reinterpret_cast<bf16_t*>(a.ws);
   f32x4* vec = reinterpret_cast<f32x4*>(a.ws + rows * (DV / 2));
   float* part = a.ws + rows * (DV / 2 + 4);
+  float* pw = part + (nparts + 3) / 4 * 4;
   if (rows > 0) {
     hipLaunchKernelGGL(bwd_pre_kernel, dim3(static_cast<unsigned>(nparts)), dim3(256), 0, s,
                        a.saved.o1, a.saved.o2, a.saved.rstd, a.saved.lse1, a.saved.lse2,
                        static_cast<const bf16_t*>(a.dout), a.lam, a.rms_weight, a.d_attn, gbuf,
-                       vec, part, rows, a.N, a.H);
+                       vec, part, reinterpret_cast<f32x4*>(pw), a.N, a.H, nchunk,
+                       a.dout_bnh ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int BH = static_cast<int>(a.B * a.H);
@@ -1163,6 +1221,14 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL(lambda_grad_kernel, dim3(1), dim3(1024), 0, s, part, rows > 0 ? nparts : 0,
                      a.lam, a.lq1, a.lk1, a.lq2, a.lk2, a.dlq1, a.dlk1, a.dlq2, a.dlk2, a.d);
+  if (a.d_rms_weight && a.H > 0) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // With no rows (B = 0 or N = 0) the sums are empty and the gradient is zero.
+    hipLaunchKernelGGL(rms_weight_grad_kernel, dim3(static_cast<unsigned>(a.H), DV / WG_CH),
+                       dim3(WG_GROUPS * WG_CH), 0, s,
+                       pw, rows > 0 ? a.B : 0, a.H, nchunk, a.d_rms_weight);
+  }
   return hipGetLastError();
 }
 

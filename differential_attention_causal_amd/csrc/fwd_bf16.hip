@@ -417,7 +417,7 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     const float* __restrict__ rms_w, bf16_t* __restrict__ out, float* __restrict__ sv_lse1,
     float* __restrict__ sv_lse2, float* __restrict__ sv_o1, float* __restrict__ sv_o2,
     float* __restrict__ sv_rstd, uint32_t* __restrict__ flags, int BH, int H, int N, int nqb,
-    float eps) {
+    float eps, int out_bnh) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x;
@@ -726,7 +726,9 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     const float rstd = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
     const int qr = q0 + 8 * m + 2 * wv + g;
     if (qr < N && (!decltype(only_bad)::value || row_bad)) {
-      bf16_t* Y = out + (hoff + qr) * DV;
+      // Y row of (b, h, qr): [B, H, N, 2d], or [B, N, H, 2d] with out_bnh.
+      const int64_t yrow = out_bnh ? (static_cast<int64_t>(bh / H) * N + qr) * H + hh : hoff + qr;
+      bf16_t* Y = out + yrow * DV;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
 #pragma unroll
@@ -803,7 +805,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
                        a.training ? sv.lse2 : nullptr, a.training ? sv.o1 : nullptr,
                        a.training ? sv.o2 : nullptr, a.training ? sv.rstd : nullptr, flags,
                        static_cast<int>(BH), static_cast<int>(a.H), static_cast<int>(a.N), nqb,
-                       a.eps);
+                       a.eps, a.out_bnh ? 1 : 0);
     return hipGetLastError();
   };
   hipError_t e = launch(fwd_bf16_kernel<false>);

@@ -19,7 +19,7 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(
     const float* __restrict__ q1, const float* __restrict__ q2, const float* __restrict__ k1,
     const float* __restrict__ k2, const float* __restrict__ v,
     const diffattn_lambda_state* __restrict__ lamst, const float* __restrict__ rms_w,
-    float* __restrict__ out, int64_t H, int64_t N, float eps) {
+    float* __restrict__ out, int64_t H, int64_t N, float eps, int out_bnh) {
   constexpr int DV = 2 * D;
   constexpr int CPL = (DV + 63) / 64;  // output columns per lane
   __shared__ float qs[4][2][D];
@@ -106,7 +106,8 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(
       const int col = lane + 64 * c;
       if (col < DV) {
         const float w = rms_w ? rms_w[h * DV + col] : 1.0f;
-        out[(bh * N + i) * DV + col] = g * (w * (o[c] * rstd));
+        const int64_t yrow = out_bnh ? ((bh / H) * N + i) * H + h : bh * N + i;
+        out[yrow * DV + col] = g * (w * (o[c] * rstd));
       }
     }
   }
@@ -120,7 +121,7 @@ hipError_t launch_fwd_fp32(const FwdArgs& a, hipStream_t s) {
                      static_cast<const float*>(a.q1), static_cast<const float*>(a.q2),      \
                      static_cast<const float*>(a.k1), static_cast<const float*>(a.k2),      \
                      static_cast<const float*>(a.v), a.lam, a.rms_weight,                   \
-                     static_cast<float*>(a.out), a.H, a.N, a.eps)
+                     static_cast<float*>(a.out), a.H, a.N, a.eps, a.out_bnh ? 1 : 0)
   switch (a.d) {
     case 16: DA_LAUNCH(16); break;
     case 32: DA_LAUNCH(32); break;

@@ -15,13 +15,16 @@
 //          channel c of Q_(j+1) in head h, likewise for keys; column h 2d + c of the value
 //          block is channel c of V in head h. Row b N + i is token i of sequence b.
 //
-// Tiling: a 512-thread workgroup (8 waves, 4 x 2) computes a 256 x 256 tile of C in
-// K-steps of 64; each wave holds a 64 x 128 sub-tile as 2 x 4 accumulators of the
-// 32x32x16 bf16 MFMA. A and B K-slabs (32 KiB each) are copied global -> LDS by the
-// buffer unit (buffer_load ... lds), double-buffered, one barrier per K-step; operands are
-// read from LDS with 16-byte reads. Tiles are ordered in groups of four 256-row panels
-// (so the 32 tiles one XCD runs at a time share A and B slabs in its L2), and each XCD
-// is given a contiguous range of that order.
+// Tiling: a 256-thread workgroup (4 waves, 2 x 2, one per SIMD) computes a 256 x 256
+// tile of C in K-steps of 64; each wave holds a 128 x 128 sub-tile as 4 x 4 accumulators
+// of the 32x32x16 bf16 MFMA (256 accumulation registers, so they live in the AGPRs). Per
+// 16-deep step a wave reads 4 A and 4 B operands from LDS for 16 products: half an LDS
+// read per product, which keeps the LDS well below its bandwidth. A and B K-slabs
+// (32 KiB each) are copied global -> LDS by the buffer unit (buffer_load ... lds),
+// double-buffered, one barrier per K-step. The finished tile is rounded to bf16 and
+// staged through LDS, so that every lane stores 16 contiguous bytes. Tiles are ordered in
+// groups of four 256-row panels (so the 32 tiles one XCD runs at a time share A and B
+// slabs in its L2), and each XCD is given a contiguous range of that order.
 #include "common.h"
 #include "launch.h"
 
@@ -31,7 +34,8 @@ namespace gemm {
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int NT = 512, NWAVE = 8;
+constexpr int NT = 256, NWAVE = 4;
+constexpr int WT = 128;                    // wave sub-tile: WT x WT
 constexpr int SLAB = BM * BK * 2;          // bytes of one A (or B) K-slab: 32 KiB
 constexpr int STAGE = 2 * SLAB;            // A slab then B slab
 constexpr int LDS_BYTES = 2 * STAGE;       // two stages: 128 KiB
@@ -65,13 +69,13 @@ __device__ __forceinline__ void dma16(const u32x4& rs, uint32_t m0, int voff) {
                : "s"(m0), "v"(voff), "s"(rs));
 }
 
-// This wave's share of one K-slab: 32 transfers of 1 KiB (8 rows each) per slab, four per
-// wave. Lane l of transfer t fills 16-byte slot l of its KiB: row 8 t + l / 8, stored
+// This wave's share of one K-slab: 32 transfers of 1 KiB (8 rows each) per slab, eight
+// per wave. Lane l of transfer t fills 16-byte slot l of its KiB: row 8 t + l / 8, stored
 // unit l % 8, which holds K unit (l % 8) ^ swz(row) of that row.
 __device__ __forceinline__ void load_slab(const u32x4& rs, uint32_t dst, int k0, int row_bytes,
                                           int wv, int lane) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < 32 / NWAVE; ++r) {
     const int t = wv + NWAVE * r;
     const int row = 8 * t + (lane >> 3);
     const int unit = (lane & 7) ^ swz(row);
@@ -137,74 +141,126 @@ __global__ void __launch_bounds__(NT, 1)
   const u32x4 rb = rsrc(Bw + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(b_rows) * K * 2);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)smem));
 
-  f32x16 acc[2][4];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int KT = K / BK;
+  const int r32 = lane & 31, hi = lane >> 5;
+  // Operands of one 16-deep step: A rows 128 wm + 32 i + r32, B rows 128 wn + 32 j + r32.
+  auto read_ops = [&](bf16x8 (&a)[4], bf16x8 (&b)[4], uint32_t stage, int kk)
+                      __attribute__((always_inline)) {
+    const int unit = 2 * kk + hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = lds_operand(stage, WT * wm + 32 * i + r32, unit);
+      b[i] = lds_operand(stage + SLAB, WT * wn + 32 * i + r32, unit);
+    }
+  };
+  auto products = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[4], int first, int count)
+                      __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = first; t < first + count; ++t)
+      acc[t >> 2][t & 3] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t >> 2], b[t & 3], acc[t >> 2][t & 3], 0, 0, 0);
+  };
+  // One read issued after each of the first 8 products (the reads of the next step run
+  // while the matrix core works), then the remaining products.
+  auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+
+  // Slabs 0 and 1 in flight; slab 0 landed for every wave; step 0's operands read.
   load_slab(ra, lds0, 0, K * 2, wv, lane);
   load_slab(rb, lds0 + SLAB, 0, K * 2, wv, lane);
-  const int r32 = lane & 31, hi = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    // Slab kt has landed for this wave; after the barrier, for every wave, and every wave
-    // is done reading slab kt - 1, whose stage the next transfer overwrites.
+  if (KT > 1) {
+    load_slab(ra, lds0 + STAGE, BK, K * 2, wv, lane);
+    load_slab(rb, lds0 + STAGE + SLAB, BK, K * 2, wv, lane);
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  } else {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  bf16x8 fa[2][4], fb[2][4];
+  read_ops(fa[0], fb[0], lds0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
     const uint32_t cur = lds0 + (kt & 1) * STAGE;
+    read_ops(fa[1], fb[1], cur, 1);
+    products(fa[0], fb[0], 0, 16);
+    interleave();
+    read_ops(fa[0], fb[0], cur, 2);
+    products(fa[1], fb[1], 0, 16);
+    interleave();
+    read_ops(fa[1], fb[1], cur, 3);
+    products(fa[0], fb[0], 0, 16);
+    interleave();
+    // Last step of slab kt. Its operands are in registers once the first product has
+    // issued; then slab kt + 1 (sent one K-step ago) must have landed for every wave, and
+    // every wave is done reading slab kt, so its stage can take slab kt + 2.
+    products(fa[1], fb[1], 0, 4);
     if (kt + 1 < KT) {
-      const uint32_t nxt = lds0 + ((kt + 1) & 1) * STAGE;
-      load_slab(ra, nxt, (kt + 1) * BK, K * 2, wv, lane);
-      load_slab(rb, nxt + SLAB, (kt + 1) * BK, K * 2, wv, lane);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      // The remaining products stay below the barrier: they consume these registers.
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+      if (kt + 2 < KT) {
+        load_slab(ra, cur, (kt + 2) * BK, K * 2, wv, lane);
+        load_slab(rb, cur + SLAB, (kt + 2) * BK, K * 2, wv, lane);
+      }
+      read_ops(fa[0], fb[0], lds0 + ((kt + 1) & 1) * STAGE, 0);
     }
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int unit = 2 * kk + hi;
-      bf16x8 a[2], b[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = lds_operand(cur, 64 * wm + 32 * i + r32, unit);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = lds_operand(cur + SLAB, 128 * wn + 32 * j + r32, unit);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+    products(fa[1], fb[1], 4, 12);
   }
 
-  // Accumulator element e of block (i, j): row 8 (e / 4) + 4 hi + e % 4, column r32.
-  bf16_t* col[4];
-  int width[4];
-  bool col_ok[4];
+  // Epilogue. Accumulator element e of block (i, j) is row 8 (e / 4) + 4 hi + e % 4,
+  // column r32 of the block. Each wave rounds its 128 x 128 sub-tile to bf16 into its own
+  // 32 KiB of LDS (rows of 256 bytes; the 16-byte unit u of row r at u ^ (r & 15)), then
+  // stores it back row by row, 16 bytes per lane.
+  asm volatile("s_barrier" ::: "memory");   // every wave is done with the last slab
+  LDS_AS char* const stage = (LDS_AS char*)smem + wv * (WT * WT * 2);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 128 * wn + 32 * j;
-    col_ok[j] = n + r32 < Nc;
-    if (QKV) {
-      col[j] = (n < Nc ? qkv_column(qo, n, width[j]) : qo.q1) + r32;
-    } else {
-      col[j] = C + n + r32;
-      width[j] = Nc;
-    }
-  }
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * hi + (e & 3);
-      if (m >= M) continue;
-      int64_t row = m;
-      if (QKV) {   // m = b N + i  ->  (b H + 0) N + i; the head is in col[j]
-        const uint32_t b = static_cast<uint32_t>(m) / qo.n;
-        row = static_cast<int64_t>(b) * (qo.h - 1) * qo.n + m;
+      for (int e = 0; e < 16; ++e) {
+        const int r = 32 * i + 8 * (e >> 2) + 4 * hi + (e & 3);
+        const int c = 32 * j + r32;
+        const int u = (c >> 3) ^ (r & 15);
+        *reinterpret_cast<LDS_AS bf16_t*>(stage + r * 256 + 16 * u + 2 * (c & 7)) =
+            f32_to_bf16(acc[i][j][e]);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (col_ok[j]) col[j][row * width[j]] = f32_to_bf16(acc[i][j][e]);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's staging writes done
+  // Each pass stores 4 rows: lane l takes unit l % 16 of row 4 pass + l / 16.
+  const int u = lane & 15;
+  const int n = n0 + WT * wn + 8 * u;              // first column of this lane's 16 bytes
+  const bool col_ok = n < Nc;                       // Nc is a multiple of 8
+  int width = Nc;
+  bf16_t* col = C + n;
+  if (QKV) col = (col_ok ? qkv_column(qo, n & ~31, width) : qo.q1) + (n & 31);
+  const int64_t mrow0 = m0 + WT * wm;
+#pragma unroll 4
+  for (int pass = 0; pass < WT / 4; ++pass) {
+    const int r = 4 * pass + (lane >> 4);
+    const int64_t m = mrow0 + r;
+    const u32x4 val = *reinterpret_cast<const LDS_AS u32x4*>(stage + r * 256 + 16 * (u ^ (r & 15)));
+    if (m >= M || !col_ok) continue;
+    int64_t row = m;
+    if (QKV) {   // m = b N + i  ->  (b H + 0) N + i; the head is in col
+      const uint32_t b = static_cast<uint32_t>(m) / qo.n;
+      row = static_cast<int64_t>(b) * (qo.h - 1) * qo.n + m;
     }
+    *reinterpret_cast<u32x4*>(col + row * width) = val;
   }
 }
 

@@ -21,6 +21,7 @@ struct FwdArgs {
   int64_t B, H, N;
   int d;
   float eps;
+  bool out_bnh;              // out is [B, N, H, 2d] instead of [B, H, N, 2d]
 };
 
 struct DecodeArgs {
@@ -45,6 +46,8 @@ struct BwdArgs {
   void *dq1, *dq2, *dk1, *dk2, *dv;
   float* d_attn;
   float *dlq1, *dlk1, *dlq2, *dlk2;
+  float* d_rms_weight;       // [H, 2d] or nullptr
+  bool dout_bnh;             // dout is [B, N, H, 2d] instead of [B, H, N, 2d]
   float* ws;                 // workspace (float32)
   int64_t B, H, N;
   int d;

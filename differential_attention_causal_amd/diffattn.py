@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libdiffattn.so")
 OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4
 FP32, BF16 = 0, 1
 OP_FWD, OP_DECODE, OP_BWD = 0, 1, 2
+LAYOUT_BHN, LAYOUT_BNH = 0, 1
+_LAYOUTS = {"bhn": LAYOUT_BHN, "bnh": LAYOUT_BNH}
 
 # Every symbol declared in include/diffattn.h.
 EXPORTS = ("diffattn_lambda", "diffattn_lambda_layers", "diffattn_qkv_proj",
@@ -31,7 +33,8 @@ EXPORTS = ("diffattn_lambda", "diffattn_lambda_layers", "diffattn_qkv_proj",
 class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("seqlen", ctypes.c_int64),
                 ("head_dim", ctypes.c_int32), ("causal", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int)]
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int),
+                ("out_layout", ctypes.c_int32)]
 
 
 class Saved(ctypes.Structure):
@@ -88,7 +91,7 @@ def _lib():
         lib.diffattn_cache_append.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P]
         lib.diffattn_bwd.restype = ctypes.c_int
         lib.diffattn_bwd.argtypes = ([ctypes.POINTER(Problem)] + [P] * 11 +
-                                     [ctypes.POINTER(Saved)] + [P] * 12 +
+                                     [ctypes.POINTER(Saved)] + [P] * 13 +
                                      [ctypes.c_size_t, P])
         _LIB = lib
     return _LIB
@@ -134,9 +137,19 @@ def _need_cuda(*ts):
                 raise ValueError("libdiffattn tensors must be contiguous")
 
 
-def problem(batch, heads, seqlen, head_dim, dtype_code, eps=1e-5) -> Problem:
+def problem(batch, heads, seqlen, head_dim, dtype_code, eps=1e-5, layout=LAYOUT_BHN) -> Problem:
     return Problem(int(batch), int(heads), int(seqlen), int(head_dim), 1, float(eps),
-                   int(dtype_code))
+                   int(dtype_code), int(layout))
+
+
+def _layout(name: str) -> int:
+    if name not in _LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(_LAYOUTS)}")
+    return _LAYOUTS[name]
+
+
+def _y_shape(B, H, N, d, layout: int):
+    return (B, N, H, 2 * d) if layout == LAYOUT_BNH else (B, H, N, 2 * d)
 
 
 def workspace_bytes(op: int, p: Problem) -> int:
@@ -251,13 +264,15 @@ def _saved_struct(sv: Optional[Dict[str, torch.Tensor]]):
 
 def forward(q1, q2, k1, k2, v, lam_state, rms_weight=None, eps: float = 1e-5,
             out: Optional[torch.Tensor] = None, saved: Optional[Dict[str, torch.Tensor]] = None,
-            workspace: Optional[torch.Tensor] = None):
+            workspace: Optional[torch.Tensor] = None, layout: str = "bhn"):
     """Causal DiffAttn forward. Q/K [B,H,N,d], V [B,H,N,2d] (float32 or bfloat16).
 
-    Returns Y [B,H,N,2d].  ``saved`` (from ``alloc_saved``) requests the training
-    saves.  ``workspace``: a uint8 device tensor of at least
-    ``workspace_bytes(OP_FWD, ...)`` bytes (allocated here when omitted).
+    Returns Y [B,H,N,2d] (layout "bhn") or [B,N,H,2d] (layout "bnh", the heads of a
+    token side by side, as the output projection takes them).  ``saved`` (from
+    ``alloc_saved``) requests the training saves.  ``workspace``: a uint8 device tensor
+    of at least ``workspace_bytes(OP_FWD, ...)`` bytes (allocated here when omitted).
     """
+    lay = _layout(layout)
     _need_cuda(q1, q2, k1, k2, v, lam_state, rms_weight, out, workspace)
     B, H, N, d = q1.shape
     for t in (q2, k1, k2):
@@ -266,8 +281,10 @@ def forward(q1, q2, k1, k2, v, lam_state, rms_weight=None, eps: float = 1e-5,
     if tuple(v.shape) != (B, H, N, 2 * d) or v.dtype != q1.dtype:
         raise ValueError("V must be [B, H, N, 2d] of the same dtype")
     if out is None:
-        out = torch.empty_like(v)
-    p = problem(B, H, N, d, _dtype_code(q1), eps)
+        out = torch.empty(_y_shape(B, H, N, d, lay), dtype=v.dtype, device=v.device)
+    elif tuple(out.shape) != _y_shape(B, H, N, d, lay):
+        raise ValueError("out does not match the layout")
+    p = problem(B, H, N, d, _dtype_code(q1), eps, lay)
     svs = _saved_struct(saved)
     need = workspace_bytes(OP_FWD, p)
     if workspace is None and need > 0:
@@ -312,16 +329,23 @@ def cache_append(k1_new, k2_new, v_new, k1c, k2c, vc, cache_len):
 
 # ------------------------------------------------------------------ backward
 def backward(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, lam_state, saved, dout, rms_weight=None,
-             eps: float = 1e-5, workspace=None):
-    """Gradients of sum(Y * dout); returns a dict of device tensors."""
+             eps: float = 1e-5, workspace=None, layout: str = "bhn",
+             weight_grad: bool = True):
+    """Gradients of sum(Y * dout); returns a dict of device tensors. ``dout`` is in the
+    forward's output layout; ``d_rms_weight`` [H, 2d] is included when weight_grad."""
     _need_cuda(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, lam_state, dout, rms_weight, workspace)
     B, H, N, d = q1.shape
-    p = problem(B, H, N, d, _dtype_code(q1), eps)
+    lay = _layout(layout)
+    if tuple(dout.shape) != _y_shape(B, H, N, d, lay):
+        raise ValueError("dout does not match the layout")
+    p = problem(B, H, N, d, _dtype_code(q1), eps, lay)
     g = {"dq1": torch.empty_like(q1), "dq2": torch.empty_like(q2), "dk1": torch.empty_like(k1),
          "dk2": torch.empty_like(k2), "dv": torch.empty_like(v),
          "d_attn": torch.empty(B, H, N, 2 * d, dtype=torch.float32, device=q1.device)}
     for k in ("dlq1", "dlk1", "dlq2", "dlk2"):
         g[k] = torch.empty(d, dtype=torch.float32, device=q1.device)
+    if weight_grad:
+        g["d_rms_weight"] = torch.empty(H, 2 * d, dtype=torch.float32, device=q1.device)
     need = workspace_bytes(OP_BWD, p)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
@@ -332,5 +356,5 @@ def backward(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, lam_state, saved, dout, rms_
         ctypes.byref(svs) if svs is not None else None, _ptr(dout),
         _ptr(g["dq1"]), _ptr(g["dq2"]), _ptr(g["dk1"]), _ptr(g["dk2"]), _ptr(g["dv"]),
         _ptr(g["d_attn"]), _ptr(g["dlq1"]), _ptr(g["dlk1"]), _ptr(g["dlq2"]), _ptr(g["dlk2"]),
-        _ptr(workspace), _nbytes(workspace), _stream(q1.device)))
+        _ptr(g.get("d_rms_weight")), _ptr(workspace), _nbytes(workspace), _stream(q1.device)))
     return g

@@ -27,7 +27,8 @@
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers unless stated otherwise. Layout is contiguous
- *     row-major [B, H, N, feature] (feature = d for Q1/Q2/K1/K2, 2d for V and outputs).
+ *     row-major [B, H, N, feature] (feature = d for Q1/Q2/K1/K2, 2d for V and outputs);
+ *     p->out_layout may make Y and dout token-major instead (diffattn_layout).
  *   - The caller owns every buffer, including the workspace whose size is given by
  *     diffattn_workspace_bytes. The library keeps no state between calls and allocates
  *     no device memory.
@@ -64,6 +65,13 @@ typedef enum { DIFFATTN_FP32 = 0, DIFFATTN_BF16 = 1 } diffattn_dtype;
 
 typedef enum { DIFFATTN_OP_FWD = 0, DIFFATTN_OP_DECODE = 1, DIFFATTN_OP_BWD = 2 } diffattn_op;
 
+/* Layout of the attention output Y (and of dout in the backward). BHN: [B, H, N, 2d], head
+ * by head. BNH: [B, N, H, 2d] = [B, N, H 2d], the heads of each token concatenated along
+ * channels, which is what the output projection W_O consumes (intoai.pub, "Differential
+ * Attention With Multiple Heads"). Q/K/V, the saved tensors and every gradient stay
+ * [B, H, N, *]. */
+typedef enum { DIFFATTN_LAYOUT_BHN = 0, DIFFATTN_LAYOUT_BNH = 1 } diffattn_layout;
+
 typedef struct {
   int64_t batch;      /* B >= 0 */
   int64_t heads;      /* H >= 0 */
@@ -72,6 +80,7 @@ typedef struct {
   int32_t causal;     /* must be 1 */
   float rms_eps;      /* eps of the per-head RMSNorm, >= 0, added inside the square root */
   diffattn_dtype dtype; /* element type of Q/K/V, outputs and gradients */
+  int32_t out_layout;   /* diffattn_layout of Y and dout; 0 (BHN) when zero-initialised */
 } diffattn_problem;
 
 /* The per-layer lambda scalar, as written by diffattn_lambda into device memory and read
@@ -239,13 +248,17 @@ diffattn_status diffattn_out_proj(const diffattn_problem* p, int64_t d_model, co
  *   G   = dL/dO = r g - O r^3 rowsum(g O) / 2d,  g = (1 - lambda_init) w dout, r = rstd
  *   dV  = (A1 - lambda A2)^T G;   dS1 = A1 (G V^T - D1);   dS2 = -lambda A2 (G V^T - D2)
  *   D_k = rowsum(G * O_k);  dQ_k = dS_k K_k / sqrt(d);  dK_k = dS_k^T Q_k / sqrt(d)
+ *   dw_h    = (1 - lambda_init) sum over (b, i) of dout * O r   (RMSNorm weight, per head)
  *   dlambda = -sum over (b, h, i) of D2;  dlq1 = dlambda e^a lk1;  dlk1 = dlambda e^a lq1;
  *   dlq2 = -dlambda e^b lk2;  dlk2 = -dlambda e^b lq2   (lambda_init gets no gradient)
  *   inputs  q1..v, lq1..lk2 (device float32 [d]), lam, rms_weight (or NULL), saved (from
  *           diffattn_fwd in training mode on the same inputs), dout [B, H, N, 2d]
  *   outputs dq1, dq2, dk1, dk2 [B, H, N, d]; dv [B, H, N, 2d] (all p->dtype);
  *           d_attn [B, H, N, 2d] float32 = G, the gradient at the RMSNorm input;
- *           dlq1, dlk1, dlq2, dlk2 device float32 [d]
+ *           dlq1, dlk1, dlq2, dlk2 device float32 [d];
+ *           d_rms_weight device float32 [H, 2d] (the RMSNorm weight gradient), or NULL to
+ *           skip it; computed whether or not rms_weight is NULL (then for w = 1)
+ *   dout    in p->out_layout (the layout the forward wrote Y in)
  *   workspace at least diffattn_workspace_bytes(OP_BWD, p) bytes
  * bf16 only, d = 64, 16-byte aligned pointers. */
 diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const void* q2,
@@ -255,7 +268,8 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
                              const diffattn_saved* saved, const void* dout, void* dq1,
                              void* dq2, void* dk1, void* dk2, void* dv, float* d_attn,
                              float* dlq1, float* dlk1, float* dlq2, float* dlk2,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             float* d_rms_weight, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Workspace bytes an operation needs for problem p (0 if none; also 0 for an invalid p). */
 size_t diffattn_workspace_bytes(diffattn_op op, const diffattn_problem* p);

@@ -232,7 +232,7 @@ def test_backward_argument_checks():
     ptrs = [addr(i * 64) for i in range(27)]
     sv = da.Saved(*(A * 64 * (40 + i) for i in range(5)))
     def call(p, ptrs, saved, ws, n):
-        args = ptrs[:11] + [saved] + ptrs[11:22]
+        args = ptrs[:11] + [saved] + ptrs[11:23]
         return lib.diffattn_bwd(ctypes.byref(p), *args, ws, n, None)
     ws = addr(64 * 60)
     assert call(p, ptrs, ctypes.byref(sv), None, need) == da.E_WORKSPACE
@@ -246,6 +246,12 @@ def test_backward_argument_checks():
     assert call(p, bad, ctypes.byref(sv), ws, need) == da.E_ARG
     long = da.problem(1, 1, (1 << 22) + 1, 64, da.BF16)
     assert call(long, ptrs, ctypes.byref(sv), ws, need) == da.E_UNSUPPORTED
+    bad = list(ptrs); bad[22] = ptrs[5]     # d_rms_weight aliases lq1
+    assert call(p, bad, ctypes.byref(sv), ws, need) == da.E_ARG
+    bad = list(ptrs); bad[22] = ctypes.c_void_p(A * 64 * 30 + 2)   # misaligned
+    assert call(p, bad, ctypes.byref(sv), ws, need) == da.E_ARG
+    lay = da.problem(2, 2, 128, 64, da.BF16, layout=2)                # unknown layout
+    assert call(lay, ptrs, ctypes.byref(sv), ws, need) == da.E_ARG
 
 
 def test_workspace_queries():

@@ -81,6 +81,13 @@ def compare(g, ref, heads, h=None, layer=None, weight=None):
                                    atol=1e-6 * abs(dlam_gpu) * np.max(np.abs(f)))
 
 
+def check_weight_grad(g, ref):
+    """d_rms_weight [H, 2d] against the oracle's (summed over the whole batch): normwise
+    relative error within the gradient tolerance."""
+    e = rel(np64(g["d_rms_weight"]), ref["d_rms_weight"], 1.0)
+    assert e <= TOL, ("d_rms_weight", e)
+
+
 @pytest.mark.parametrize("b,hh,n", [(1, 1, 1), (1, 1, 32), (1, 2, 33), (2, 1, 64), (1, 2, 129),
                                     (1, 2, 200), (1, 1, 300), (1, 2, 1000)])
 def test_backward_small(b, hh, n):
@@ -90,6 +97,7 @@ def test_backward_small(b, hh, n):
     ref = orc.backward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], h["dout"], h["lq1"],
                        h["lk1"], h["lq2"], h["lk2"], w.layer)
     compare(g, ref, [(i, j) for i in range(b) for j in range(hh)], h, w.layer)
+    check_weight_grad(g, ref)
 
 
 def test_backward_rms_weight():
@@ -101,6 +109,38 @@ def test_backward_rms_weight():
     ref = orc.backward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], h["dout"], h["lq1"],
                        h["lk1"], h["lq2"], h["lk2"], w.layer, weight=np64(weight))
     compare(g, ref, [(0, 0), (0, 1)], h, w.layer, np64(weight))
+    check_weight_grad(g, ref)
+
+
+@pytest.mark.parametrize("b,hh,n", [(2, 3, 100), (1, 2, 64)])
+def test_backward_token_major_dout(b, hh, n):
+    """dout given as [B, N, H, 2d] (layout "bnh") yields bitwise the gradients of the same
+    dout given as [B, H, N, 2d]."""
+    w = synth.custom("train", b, hh, n, 64, 4, "bf16", number=760 + n)
+    x, h = draw(w)
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    sv = da.alloc_saved(b, hh, n, 64, DEV)
+    da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, saved=sv)
+    args = (x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lq1"], x["lk1"], x["lq2"], x["lk2"],
+            st, sv)
+    ga = da.backward(*args, x["dout"])
+    gb = da.backward(*args, x["dout"].transpose(1, 2).contiguous(), layout="bnh")
+    torch.cuda.synchronize()
+    for k in ga:
+        assert torch.equal(ga[k], gb[k]), k
+
+
+def test_backward_weight_grad_empty_is_zero():
+    d = 64
+    st = da.lambda_state_tensor(0.5, 0.2, DEV)
+    z = torch.empty(2, 3, 0, d, dtype=torch.bfloat16, device=DEV)
+    zv = torch.empty(2, 3, 0, 2 * d, dtype=torch.bfloat16, device=DEV)
+    lv = [torch.randn(d, device=DEV) for _ in range(4)]
+    sv = da.alloc_saved(2, 3, 0, d, DEV)
+    g = da.backward(z, z, z, z, zv, *lv, st, sv, zv)
+    torch.cuda.synchronize()
+    assert g["d_rms_weight"].shape == (3, 2 * d)
+    assert torch.count_nonzero(g["d_rms_weight"]).item() == 0
 
 
 def test_backward_one_head_n32_slice():

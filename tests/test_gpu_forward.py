@@ -314,3 +314,27 @@ def test_bf16_fixup_pass_for_large_score_jump():
     ref = orc.forward(hh["q1"], hh["q2"], hh["k1"], hh["k2"], hh["v"], ls["lambda"],
                       ls["lambda_init"])
     assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype,d,B,H,N", [("bf16", 64, 2, 3, 300), ("bf16", 64, 1, 2, 1),
+                                           ("fp32", 32, 2, 3, 77)])
+def test_token_major_output_is_the_transpose(dtype, d, B, H, N):
+    """layout "bnh" writes the same values as "bhn", as [B, N, H, 2d] (bitwise), and the
+    training saves do not depend on it."""
+    w = synth.custom("fwd", B, H, N, d, 5, dtype, number=1400 + N)
+    x, h = draw(w)
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    wgt = 1.0 + 0.25 * torch.randn(H, 2 * d, generator=torch.Generator().manual_seed(7)).to(DEV)
+    kw = dict(rms_weight=wgt)
+    if dtype == "bf16":
+        sa, sb = (da.alloc_saved(B, H, N, d, DEV) for _ in range(2))
+    else:
+        sa = sb = None
+    ya = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, saved=sa, **kw)
+    yb = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, saved=sb, layout="bnh", **kw)
+    torch.cuda.synchronize()
+    assert tuple(yb.shape) == (B, N, H, 2 * d)
+    assert torch.equal(ya.transpose(1, 2), yb)
+    if sa is not None:
+        for k in sa:
+            assert torch.equal(sa[k], sb[k]), k

@@ -87,3 +87,25 @@ def test_proj_empty_and_deterministic():
     b = da.qkv_proj(x["x"], x["w_qkv"], 2, 64)
     for s, t in zip(a, b):
         assert torch.equal(s, t)
+
+
+def test_projection_attention_projection_chain():
+    """X -> fused QKV projection -> DiffAttn (token-major output) -> W_O, all on the
+    device, against the oracle's float64 chain on the same bf16 weights and X. Each stage
+    rounds its output to bf16 on the device; the float64 chain does not, so the bound is
+    the composition of the stage bars: 5e-2 max-abs on outputs of order one."""
+    B, N, H, d, dm = 1, 200, 2, 64, 256
+    x = synth.make_proj_inputs(B, N, H, d, dm, DEV, seed=1500)
+    lv = synth.make_lambda_layers(1, d, DEV, seed=1501)
+    lam = [lv[k][0].contiguous() for k in ("lq1", "lk1", "lq2", "lk2")]
+    st = da.lambda_(*lam, 4)
+    q1, q2, k1, k2, v = da.qkv_proj(x["x"], x["w_qkv"], H, d)
+    y = da.forward(q1, q2, k1, k2, v, st, layout="bnh")
+    out = da.out_proj(y, x["w_o"])
+    torch.cuda.synchronize()
+    ls = orc.lambda_scalar(*(np64(t) for t in lam), 4)
+    rq = orc.qkv_proj(np64(x["x"]), np64(x["w_qkv"]), H, d)
+    ry = orc.forward(*rq, ls["lambda"], ls["lambda_init"])
+    ref = orc.out_proj(ry.transpose(0, 2, 1, 3), np64(x["w_o"]))
+    err = np.abs(np64(out) - ref)
+    assert float(err.max()) <= 5e-2, float(err.max())
