@@ -159,6 +159,27 @@ def leg_decode(steps, warmup):
 
     _, _, app = time_steps(append_step, steps, warmup, inner_events=True)
     app_ms = sum(app) / len(app)
+
+    # Grouped-query variant: the 16 query heads share 4 cache heads (a quarter of the
+    # cache bytes per step).
+    hkv = 4
+    kv = {k: x[k][:, :hkv].contiguous() for k in ("k1", "k2", "v")}
+    torch.cuda.synchronize()
+
+    def gqa_step(ev):
+        st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+        if ev:
+            ev[0].record()
+        da.decode(x["q1"], x["q2"], kv["k1"], kv["k2"], kv["v"], st, out=out, workspace=ws)
+        if ev:
+            ev[1].record()
+
+    _, _, gq = time_steps(gqa_step, steps, warmup, inner_events=True)
+    gq_ms = sum(gq) / len(gq)
+    bh = w.batch * w.heads
+    gq_bytes = (w.batch * hkv * w.seqlen * 4 * w.head_dim * 2 + 2 * bh * w.head_dim * 2 +
+                bh * 2 * w.head_dim * 2)
+    del kv
     app_bytes = 2 * w.batch * w.heads * (4 * w.head_dim) * 2   # rows read + rows written
     return {
         "workload": w.name, "value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
@@ -166,6 +187,9 @@ def leg_decode(steps, warmup):
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS,
                      "traffic": traffic_from_profiles("decode_split_kernel", "decode.hip", w.name)},
+        "gqa": {"workload": f"{w.name}, 4 cache heads (groups of 4)", "decode_ms": gq_ms,
+                "bytes_per_step": gq_bytes, "GB_s": gq_bytes / (gq_ms * 1e-3) / 1e9,
+                "speedup_vs_mha": kern_ms / gq_ms},
         "append": {"us_per_call": app_ms * 1e3, "bytes": app_bytes,
                    "GB_s": app_bytes / (app_ms * 1e-3) / 1e9, "bound": "launch latency"},
     }

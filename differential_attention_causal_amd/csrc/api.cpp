@@ -76,6 +76,8 @@ diffattn_status check_problem(const diffattn_problem* p, bool* empty) {
   if (!(p->rms_eps >= 0.0f) || !isfinite(p->rms_eps)) return DIFFATTN_E_ARG;
   if (p->out_layout != DIFFATTN_LAYOUT_BHN && p->out_layout != DIFFATTN_LAYOUT_BNH)
     return DIFFATTN_E_ARG;
+  if (p->kv_heads < 0 || p->kv_heads > p->heads) return DIFFATTN_E_ARG;
+  if (p->kv_heads > 0 && p->heads % p->kv_heads != 0) return DIFFATTN_E_ARG;
   if (p->causal != 1) return DIFFATTN_E_UNSUPPORTED;
   // Largest tensor: [B, H, N, 2d] float32 must stay far from int64 overflow.
   int64_t t = 0;
@@ -87,6 +89,9 @@ diffattn_status check_problem(const diffattn_problem* p, bool* empty) {
   *empty = p->batch == 0 || p->heads == 0 || p->seqlen == 0;
   return DIFFATTN_OK;
 }
+
+// Heads of K1, K2 and V: p->kv_heads, or heads when it is 0.
+int64_t kv_heads_of(const diffattn_problem* p) { return p->kv_heads > 0 ? p->kv_heads : p->heads; }
 
 size_t decode_ws_bytes(const diffattn_problem* p) {
   int ns = 0, sl = 0;
@@ -201,7 +206,9 @@ diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const vo
   const size_t rows = static_cast<size_t>(p->batch) * p->heads * p->seqlen;
   const size_t eb = elem_bytes(p->dtype);
   const size_t qk = rows * d * eb, vb = rows * 2 * d * eb;
-  const Span in[7] = {{q1, qk}, {q2, qk}, {k1, qk}, {k2, qk}, {v, vb},
+  const size_t kv_rows = static_cast<size_t>(p->batch) * kv_heads_of(p) * p->seqlen;
+  const size_t kk = kv_rows * d * eb, kvb = kv_rows * 2 * d * eb;
+  const Span in[7] = {{q1, qk}, {q2, qk}, {k1, kk}, {k2, kk}, {v, kvb},
                       {lam, sizeof(diffattn_lambda_state)},
                       {rms_weight, static_cast<size_t>(p->heads) * 2 * d * sizeof(float)}};
   diffattn::FwdArgs a;
@@ -228,6 +235,7 @@ diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const vo
   a.rms_weight = rms_weight;
   a.out = out;
   a.B = p->batch; a.H = p->heads; a.N = p->seqlen;
+  a.G = static_cast<int>(p->heads / kv_heads_of(p));
   a.d = d;
   a.eps = p->rms_eps;
   a.out_bnh = p->out_layout == DIFFATTN_LAYOUT_BNH;
@@ -259,7 +267,8 @@ diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const
   if (!aligned(workspace, 16)) return DIFFATTN_E_ARG;
   const int d = p->head_dim;
   const size_t bh = static_cast<size_t>(p->batch) * p->heads;
-  const size_t qb = bh * d * 2, kb = bh * p->seqlen * d * 2, vb = bh * p->seqlen * 2 * d * 2;
+  const size_t bhk = static_cast<size_t>(p->batch) * kv_heads_of(p);
+  const size_t qb = bh * d * 2, kb = bhk * p->seqlen * d * 2, vb = bhk * p->seqlen * 2 * d * 2;
   const Span in[8] = {{q1, qb}, {q2, qb}, {k1c, kb}, {k2c, kb}, {vc, vb},
                       {cache_len, static_cast<size_t>(p->batch) * 4},
                       {lam, sizeof(diffattn_lambda_state)},
@@ -275,6 +284,7 @@ diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const
   a.out = out;
   a.partial = static_cast<float*>(workspace);
   a.B = p->batch; a.H = p->heads; a.L = p->seqlen;
+  a.G = static_cast<int>(p->heads / kv_heads_of(p));
   diffattn::decode_split_geometry(a.B, a.H, a.L, &a.n_split, &a.split_len);
   a.d = d;
   a.eps = p->rms_eps;
@@ -296,7 +306,7 @@ diffattn_status diffattn_cache_append(const diffattn_problem* p, const void* k1_
     if (!aligned(x, 16)) return DIFFATTN_E_ARG;
   if (!aligned(cache_len, 4)) return DIFFATTN_E_ARG;
   const int d = p->head_dim;
-  const size_t bh = static_cast<size_t>(p->batch) * p->heads;
+  const size_t bh = static_cast<size_t>(p->batch) * kv_heads_of(p);   // cache heads
   const size_t kr = bh * d * 2, vr = bh * 2 * d * 2;
   const size_t kc = kr * p->seqlen, vcb = vr * p->seqlen;
   const Span in[3] = {{k1_new, kr}, {k2_new, kr}, {v_new, vr}};
@@ -307,7 +317,7 @@ diffattn_status diffattn_cache_append(const diffattn_problem* p, const void* k1_
   a.k1n = k1_new; a.k2n = k2_new; a.vn = v_new;
   a.k1c = k1c; a.k2c = k2c; a.vc = vc;
   a.cache_len = cache_len;
-  a.B = p->batch; a.H = p->heads; a.L = p->seqlen;
+  a.B = p->batch; a.H = kv_heads_of(p); a.L = p->seqlen;
   return hip_status(diffattn::launch_cache_append_bf16(a, static_cast<hipStream_t>(stream)),
                     "cache_append");
 }
@@ -343,14 +353,16 @@ diffattn_status diffattn_qkv_proj(const diffattn_problem* p, int64_t d_model, co
     if (!ptr || !aligned(ptr, 16)) return DIFFATTN_E_ARG;
   const size_t m = static_cast<size_t>(p->batch) * p->seqlen;
   const size_t hd = static_cast<size_t>(p->heads) * p->head_dim;
-  const Span in[2] = {{x, m * d_model * 2}, {w_qkv, 6 * hd * d_model * 2}};
-  const Span outs[5] = {{q1, m * hd * 2}, {q2, m * hd * 2}, {k1, m * hd * 2},
-                        {k2, m * hd * 2}, {v, m * hd * 4}};
+  const size_t hkd = static_cast<size_t>(kv_heads_of(p)) * p->head_dim;
+  const Span in[2] = {{x, m * d_model * 2}, {w_qkv, 2 * (hd + 2 * hkd) * d_model * 2}};
+  const Span outs[5] = {{q1, m * hd * 2}, {q2, m * hd * 2}, {k1, m * hkd * 2},
+                        {k2, m * hkd * 2}, {v, m * hkd * 4}};
   if (any_overlap(outs, 5, in, 2)) return DIFFATTN_E_ARG;
   diffattn::QkvProjArgs a;
   a.x = x; a.w = w_qkv;
   a.q1 = q1; a.q2 = q2; a.k1 = k1; a.k2 = k2; a.v = v;
   a.B = p->batch; a.H = p->heads; a.N = p->seqlen; a.d_model = d_model;
+  a.Hkv = kv_heads_of(p);
   a.d = p->head_dim;
   return hip_status(diffattn::launch_qkv_proj_bf16(a, static_cast<hipStream_t>(stream)),
                     "qkv_proj");
@@ -391,6 +403,7 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
   if (st != DIFFATTN_OK) return st;
   if (p->dtype != DIFFATTN_BF16 || p->head_dim != 64) return DIFFATTN_E_UNSUPPORTED;
   if (p->seqlen > kMaxSeqBf16) return DIFFATTN_E_UNSUPPORTED;
+  if (kv_heads_of(p) != p->heads) return DIFFATTN_E_UNSUPPORTED;
   const int d = p->head_dim;
   // The lambda-vector gradients exist even for an empty problem (they are then zero).
   if (!lq1 || !lk1 || !lq2 || !lk2 || !lam || !dlq1 || !dlk1 || !dlq2 || !dlk2)

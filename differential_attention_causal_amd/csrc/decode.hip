@@ -38,7 +38,7 @@ __global__ void __launch_bounds__(NT, 2) decode_split_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
     const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cache_len,
-    float* __restrict__ partial, int64_t H, int64_t L, int n_split, int rounds) {
+    float* __restrict__ partial, int64_t H, int64_t L, int n_split, int rounds, int G) {
   __shared__ float red[4][2][PART];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -55,12 +55,14 @@ __global__ void __launch_bounds__(NT, 2) decode_split_kernel(
   // Cache rows through buffer resources bounded at len rows: keys at or beyond len read
   // as zero, and each load needs only a 32-bit lane offset plus the round's scalar offset.
   constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer, no swizzle
+  // Cache head of this query head (grouped-query attention: G query heads per cache head).
+  const int64_t kvh = b * (H / G) + (bh - b * H) / G;
   const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(k1 + bh * L * D), 0, static_cast<int>(len * D * 2), kBufFlags);
+      (void*)(k1 + kvh * L * D), 0, static_cast<int>(len * D * 2), kBufFlags);
   const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(k2 + bh * L * D), 0, static_cast<int>(len * D * 2), kBufFlags);
+      (void*)(k2 + kvh * L * D), 0, static_cast<int>(len * D * 2), kBufFlags);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(v + bh * L * DV), 0, static_cast<int>(len * DV * 2), kBufFlags);
+      (void*)(v + kvh * L * DV), 0, static_cast<int>(len * DV * 2), kBufFlags);
 
   // Score lanes: key r = lane / 8 of each group of 8, channel slice c = lane % 8.
   const int r = lane >> 3, c = lane & 7;
@@ -279,7 +281,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
                      0, s, static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
                      static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
                      static_cast<const bf16_t*>(a.v), a.cache_len, a.partial, a.H, a.L,
-                     a.n_split, rounds);
+                     a.n_split, rounds, a.G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(BH)), dim3(DV), 0, s,

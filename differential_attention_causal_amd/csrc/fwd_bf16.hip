@@ -417,7 +417,7 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     const float* __restrict__ rms_w, bf16_t* __restrict__ out, float* __restrict__ sv_lse1,
     float* __restrict__ sv_lse2, float* __restrict__ sv_o1, float* __restrict__ sv_o2,
     float* __restrict__ sv_rstd, uint32_t* __restrict__ flags, int BH, int H, int N, int nqb,
-    float eps, int out_bnh) {
+    float eps, int out_bnh, int G) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x;
@@ -433,10 +433,12 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   const int q0 = qb * BR;
   const int64_t hoff = static_cast<int64_t>(bh) * N;
 
+  // K/V head of this query head (grouped-query attention: G query heads per K/V head).
+  const int64_t kvoff = (static_cast<int64_t>(bh / H) * (H / G) + (bh % H) / G) * N;
   HeadRsrc rs;
-  rs.k1 = rsrc_words(k1 + hoff * D, N * D * 2);
-  rs.k2 = rsrc_words(k2 + hoff * D, N * D * 2);
-  rs.v = rsrc_words(v + hoff * DV, N * DV * 2);
+  rs.k1 = rsrc_words(k1 + kvoff * D, N * D * 2);
+  rs.k2 = rsrc_words(k2 + kvoff * D, N * D * 2);
+  rs.v = rsrc_words(v + kvoff * DV, N * DV * 2);
 
   // Every wave walks the same sub-tiles: keys 0 .. q0 + BR - 1 (rows beyond N are
   // zero-filled and masked). The first jd are wholly below the block's first row.
@@ -805,7 +807,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
                        a.training ? sv.lse2 : nullptr, a.training ? sv.o1 : nullptr,
                        a.training ? sv.o2 : nullptr, a.training ? sv.rstd : nullptr, flags,
                        static_cast<int>(BH), static_cast<int>(a.H), static_cast<int>(a.N), nqb,
-                       a.eps, a.out_bnh ? 1 : 0);
+                       a.eps, a.out_bnh ? 1 : 0, a.G);
     return hipGetLastError();
   };
   hipError_t e = launch(fwd_bf16_kernel<false>);

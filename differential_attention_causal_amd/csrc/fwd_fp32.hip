@@ -19,7 +19,7 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(
     const float* __restrict__ q1, const float* __restrict__ q2, const float* __restrict__ k1,
     const float* __restrict__ k2, const float* __restrict__ v,
     const diffattn_lambda_state* __restrict__ lamst, const float* __restrict__ rms_w,
-    float* __restrict__ out, int64_t H, int64_t N, float eps, int out_bnh) {
+    float* __restrict__ out, int64_t H, int64_t N, float eps, int out_bnh, int64_t G) {
   constexpr int DV = 2 * D;
   constexpr int CPL = (DV + 63) / 64;  // output columns per lane
   __shared__ float qs[4][2][D];
@@ -31,9 +31,10 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(
   const int64_t ii = row_ok ? i : N - 1;
   const float* Q1 = q1 + (bh * N + ii) * D;
   const float* Q2 = q2 + (bh * N + ii) * D;
-  const float* K1 = k1 + bh * N * D;
-  const float* K2 = k2 + bh * N * D;
-  const float* V = v + bh * N * DV;
+  const int64_t kvh = (bh / H) * (H / G) + (bh % H) / G;   // K/V head (G per group)
+  const float* K1 = k1 + kvh * N * D;
+  const float* K2 = k2 + kvh * N * D;
+  const float* V = v + kvh * N * DV;
   if (lane < D) {
     qs[wv][0][lane] = Q1[lane];
     qs[wv][1][lane] = Q2[lane];
@@ -121,7 +122,8 @@ hipError_t launch_fwd_fp32(const FwdArgs& a, hipStream_t s) {
                      static_cast<const float*>(a.q1), static_cast<const float*>(a.q2),      \
                      static_cast<const float*>(a.k1), static_cast<const float*>(a.k2),      \
                      static_cast<const float*>(a.v), a.lam, a.rms_weight,                   \
-                     static_cast<float*>(a.out), a.H, a.N, a.eps, a.out_bnh ? 1 : 0)
+                     static_cast<float*>(a.out), a.H, a.N, a.eps, a.out_bnh ? 1 : 0,   \
+                     static_cast<int64_t>(a.G))
   switch (a.d) {
     case 16: DA_LAUNCH(16); break;
     case 32: DA_LAUNCH(32); break;

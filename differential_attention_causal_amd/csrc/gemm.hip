@@ -10,9 +10,10 @@
 // contiguous (B is a weight in the [out_features, in_features] layout), and writes C in
 // bf16 (round to nearest even) through one of two epilogues:
 //   plain  C row-major [M, Nc] (the W_O projection into [B, N, d_model]);
-//   qkv    the fused [3 H 2d, d_model] weight's columns scattered into Q1, Q2, K1, K2
-//          [B, H, N, d] and V [B, H, N, 2d]: column h 2d + j d + c of the query block is
-//          channel c of Q_(j+1) in head h, likewise for keys; column h 2d + c of the value
+//   qkv    the fused [(H + 2 Hkv) 2d, d_model] weight's columns scattered into Q1, Q2
+//          [B, H, N, d], K1, K2 [B, Hkv, N, d] and V [B, Hkv, N, 2d] (Hkv < H: grouped-
+//          query attention): column h 2d + j d + c of the query block is channel c of
+//          Q_(j+1) in head h, likewise for the key block; column h 2d + c of the value
 //          block is channel c of V in head h. Row b N + i is token i of sequence b.
 //
 // Tiling: a 256-thread workgroup (4 waves, 2 x 2, one per SIMD) computes a 256 x 256
@@ -91,20 +92,25 @@ __device__ __forceinline__ bf16x8 lds_operand(uint32_t slab, int row, int unit) 
 struct QkvOut {
   bf16_t *q1, *q2, *k1, *k2, *v;
   uint32_t n;    // tokens per sequence
-  int h;         // heads
+  int h;         // query heads
+  int hkv;       // key / value heads
   int d;         // width of Q1 / K1 (V is 2d)
 };
 
 // Column block [n, n + 32) of the fused projection (never straddling a head half, as d
-// is a multiple of 32): its destination tensor, offset by head and channel, and the row
-// stride there; row (b, i) then sits (b H N + i) rows further.
-__device__ __forceinline__ bf16_t* qkv_column(const QkvOut& o, int n, int& width) {
-  const int hd2 = 2 * o.d * o.h;
-  const int which = n / hd2, hc = n - which * hd2;
-  const int head = hc / (2 * o.d), within = hc - head * 2 * o.d;
+// is a multiple of 32): its destination tensor, offset by head and channel, its row
+// stride (width) and the heads of that tensor; row (b, i) then sits (b heads N + i) rows
+// further.
+__device__ __forceinline__ bf16_t* qkv_column(const QkvOut& o, int n, int& width, int& heads) {
+  const int d2 = 2 * o.d;
+  const int q_cols = d2 * o.h, kv_cols = d2 * o.hkv;
+  const int which = n < q_cols ? 0 : (n < q_cols + kv_cols ? 1 : 2);
+  const int hc = n - (which == 0 ? 0 : (which == 1 ? q_cols : q_cols + kv_cols));
+  const int head = hc / d2, within = hc - head * d2;
   const int64_t head_off = static_cast<int64_t>(head) * o.n;
+  heads = which == 0 ? o.h : o.hkv;
   if (which == 2) {
-    width = 2 * o.d;
+    width = d2;
     return o.v + head_off * width + within;
   }
   const int half = within >= o.d;
@@ -245,9 +251,9 @@ __global__ void __launch_bounds__(NT, 1)
   const int u = lane & 15;
   const int n = n0 + WT * wn + 8 * u;              // first column of this lane's 16 bytes
   const bool col_ok = n < Nc;                       // Nc is a multiple of 8
-  int width = Nc;
+  int width = Nc, heads = 1;
   bf16_t* col = C + n;
-  if (QKV) col = (col_ok ? qkv_column(qo, n & ~31, width) : qo.q1) + (n & 31);
+  if (QKV) col = (col_ok ? qkv_column(qo, n & ~31, width, heads) : qo.q1) + (n & 31);
   const int64_t mrow0 = m0 + WT * wm;
 #pragma unroll 4
   for (int pass = 0; pass < WT / 4; ++pass) {
@@ -256,9 +262,9 @@ __global__ void __launch_bounds__(NT, 1)
     const u32x4 val = *reinterpret_cast<const LDS_AS u32x4*>(stage + r * 256 + 16 * (u ^ (r & 15)));
     if (m >= M || !col_ok) continue;
     int64_t row = m;
-    if (QKV) {   // m = b N + i  ->  (b H + 0) N + i; the head is in col
+    if (QKV) {   // m = b N + i  ->  (b heads + 0) N + i; the head is in col
       const uint32_t b = static_cast<uint32_t>(m) / qo.n;
-      row = static_cast<int64_t>(b) * (qo.h - 1) * qo.n + m;
+      row = static_cast<int64_t>(b) * (heads - 1) * qo.n + m;
     }
     *reinterpret_cast<u32x4*>(col + row * width) = val;
   }
@@ -286,8 +292,8 @@ hipError_t launch_qkv_proj_bf16(const QkvProjArgs& a, hipStream_t s) {
   gemm::QkvOut qo{static_cast<bf16_t*>(a.q1), static_cast<bf16_t*>(a.q2),
                   static_cast<bf16_t*>(a.k1), static_cast<bf16_t*>(a.k2),
                   static_cast<bf16_t*>(a.v),  static_cast<uint32_t>(a.N), static_cast<int>(a.H),
-                  a.d};
-  const int nc = static_cast<int>(3 * 2 * a.d * a.H);
+                  static_cast<int>(a.Hkv), a.d};
+  const int nc = static_cast<int>(2 * a.d * (a.H + 2 * a.Hkv));
   return gemm::launch<true>(static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.w),
                             nullptr, qo, a.B * a.N, nc, static_cast<int>(a.d_model), s);
 }

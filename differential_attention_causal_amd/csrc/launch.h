@@ -19,6 +19,7 @@ struct FwdArgs {
   bool training;
   void* workspace;           // bf16: per row block, 8 words of row flags
   int64_t B, H, N;
+  int G;                     // query heads per K/V head (K1, K2, V have H / G heads)
   int d;
   float eps;
   bool out_bnh;              // out is [B, N, H, 2d] instead of [B, H, N, 2d]
@@ -32,6 +33,7 @@ struct DecodeArgs {
   void* out;
   float* partial;            // workspace
   int64_t B, H, L;
+  int G;                     // query heads per cache head (caches have H / G heads)
   int n_split, split_len;
   int d;
   float eps;
@@ -60,12 +62,13 @@ struct AppendArgs {
   int64_t B, H, L;
 };
 
-// x [B, N, d_model] times the fused weight w [3 H 2d, d_model] (rows: W_Q, W_K, W_V),
-// scattered into q1, q2, k1, k2 [B, H, N, d] and v [B, H, N, 2d].
+// x [B, N, d_model] times the fused weight w [(H + 2 Hkv) 2d, d_model] (rows: W_Q, W_K,
+// W_V), scattered into q1, q2 [B, H, N, d], k1, k2 [B, Hkv, N, d] and v [B, Hkv, N, 2d].
 struct QkvProjArgs {
   const void *x, *w;
   void *q1, *q2, *k1, *k2, *v;
   int64_t B, H, N, d_model;
+  int64_t Hkv;               // heads of k1, k2, v
   int d;
 };
 

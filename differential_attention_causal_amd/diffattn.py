@@ -34,7 +34,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("seqlen", ctypes.c_int64),
                 ("head_dim", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int),
-                ("out_layout", ctypes.c_int32)]
+                ("out_layout", ctypes.c_int32), ("kv_heads", ctypes.c_int64)]
 
 
 class Saved(ctypes.Structure):
@@ -137,9 +137,10 @@ def _need_cuda(*ts):
                 raise ValueError("libdiffattn tensors must be contiguous")
 
 
-def problem(batch, heads, seqlen, head_dim, dtype_code, eps=1e-5, layout=LAYOUT_BHN) -> Problem:
+def problem(batch, heads, seqlen, head_dim, dtype_code, eps=1e-5, layout=LAYOUT_BHN,
+            kv_heads=0) -> Problem:
     return Problem(int(batch), int(heads), int(seqlen), int(head_dim), 1, float(eps),
-                   int(dtype_code), int(layout))
+                   int(dtype_code), int(layout), int(kv_heads))
 
 
 def _layout(name: str) -> int:
@@ -207,22 +208,25 @@ def read_lambda_state(st: torch.Tensor) -> Dict[str, float]:
 
 
 # ------------------------------------------------------------------ projections
-def qkv_proj(x, w_qkv, heads: int, head_dim: int, out=None):
-    """X [B, N, d_model] (bf16) times the fused weight [3 H 2d, d_model] (W_Q, W_K, W_V
-    rows). Returns (q1, q2, k1, k2 [B, H, N, d], v [B, H, N, 2d])."""
+def qkv_proj(x, w_qkv, heads: int, head_dim: int, out=None, kv_heads: Optional[int] = None):
+    """X [B, N, d_model] (bf16) times the fused weight [(H + 2 Hkv) 2d, d_model] (W_Q, W_K,
+    W_V rows; Hkv = kv_heads, default H). Returns (q1, q2 [B, H, N, d], k1, k2
+    [B, Hkv, N, d], v [B, Hkv, N, 2d])."""
     _need_cuda(x, w_qkv)
     if x.dim() != 3 or x.dtype != torch.bfloat16 or not x.is_contiguous():
         raise ValueError("x must be contiguous bfloat16 [B, N, d_model]")
     B, N, dm = x.shape
     H, d = int(heads), int(head_dim)
-    if (tuple(w_qkv.shape) != (6 * H * d, dm) or w_qkv.dtype != torch.bfloat16
+    Hkv = H if kv_heads is None else int(kv_heads)
+    if (tuple(w_qkv.shape) != (2 * d * (H + 2 * Hkv), dm) or w_qkv.dtype != torch.bfloat16
             or not w_qkv.is_contiguous()):
-        raise ValueError("w_qkv must be contiguous bfloat16 [3 H 2d, d_model]")
+        raise ValueError("w_qkv must be contiguous bfloat16 [(H + 2 Hkv) 2d, d_model]")
     if out is None:
         f = dict(dtype=torch.bfloat16, device=x.device)
-        out = tuple(torch.empty(B, H, N, d, **f) for _ in range(4)) + \
-            (torch.empty(B, H, N, 2 * d, **f),)
-    p = problem(B, H, N, d, BF16)
+        out = (torch.empty(B, H, N, d, **f), torch.empty(B, H, N, d, **f),
+               torch.empty(B, Hkv, N, d, **f), torch.empty(B, Hkv, N, d, **f),
+               torch.empty(B, Hkv, N, 2 * d, **f))
+    p = problem(B, H, N, d, BF16, kv_heads=Hkv)
     _check("diffattn_qkv_proj", _lib().diffattn_qkv_proj(
         ctypes.byref(p), dm, _ptr(x), _ptr(w_qkv), *(_ptr(t) for t in out),
         _stream(x.device)))
@@ -275,16 +279,19 @@ def forward(q1, q2, k1, k2, v, lam_state, rms_weight=None, eps: float = 1e-5,
     lay = _layout(layout)
     _need_cuda(q1, q2, k1, k2, v, lam_state, rms_weight, out, workspace)
     B, H, N, d = q1.shape
-    for t in (q2, k1, k2):
-        if tuple(t.shape) != (B, H, N, d) or t.dtype != q1.dtype:
-            raise ValueError("Q1, Q2, K1, K2 must share shape and dtype")
-    if tuple(v.shape) != (B, H, N, 2 * d) or v.dtype != q1.dtype:
-        raise ValueError("V must be [B, H, N, 2d] of the same dtype")
+    Hkv = k1.shape[1]     # fewer K/V heads than query heads: grouped-query attention
+    if tuple(q2.shape) != (B, H, N, d) or q2.dtype != q1.dtype:
+        raise ValueError("Q1, Q2 must share shape and dtype")
+    for t in (k1, k2):
+        if tuple(t.shape) != (B, Hkv, N, d) or t.dtype != q1.dtype:
+            raise ValueError("K1, K2 must be [B, Hkv, N, d] of the queries' dtype")
+    if tuple(v.shape) != (B, Hkv, N, 2 * d) or v.dtype != q1.dtype:
+        raise ValueError("V must be [B, Hkv, N, 2d] of the same dtype")
     if out is None:
         out = torch.empty(_y_shape(B, H, N, d, lay), dtype=v.dtype, device=v.device)
     elif tuple(out.shape) != _y_shape(B, H, N, d, lay):
         raise ValueError("out does not match the layout")
-    p = problem(B, H, N, d, _dtype_code(q1), eps, lay)
+    p = problem(B, H, N, d, _dtype_code(q1), eps, lay, kv_heads=Hkv)
     svs = _saved_struct(saved)
     need = workspace_bytes(OP_FWD, p)
     if workspace is None and need > 0:
@@ -299,10 +306,16 @@ def forward(q1, q2, k1, k2, v, lam_state, rms_weight=None, eps: float = 1e-5,
 # ------------------------------------------------------------------ decode
 def decode(q1, q2, k1c, k2c, vc, lam_state, cache_len=None, rms_weight=None, eps: float = 1e-5,
            out=None, workspace=None):
-    """One decode step: q [B,H,d], caches [B,H,L,d] / [B,H,L,2d], cache_len int32 [B]."""
+    """One decode step: q [B,H,d], caches [B,Hkv,L,d] / [B,Hkv,L,2d] (Hkv dividing H:
+    grouped-query attention when Hkv < H), cache_len int32 [B]."""
     _need_cuda(q1, q2, k1c, k2c, vc, lam_state, cache_len, rms_weight, out, workspace)
-    B, H, L, d = k1c.shape
-    p = problem(B, H, L, d, _dtype_code(k1c), eps)
+    B, Hkv, L, d = k1c.shape
+    H = q1.shape[1]
+    if tuple(q1.shape) != (B, H, d) or tuple(q2.shape) != (B, H, d):
+        raise ValueError("queries must be [B, H, d]")
+    if tuple(k2c.shape) != (B, Hkv, L, d) or tuple(vc.shape) != (B, Hkv, L, 2 * d):
+        raise ValueError("caches must be [B, Hkv, L, d] and [B, Hkv, L, 2d]")
+    p = problem(B, H, L, d, _dtype_code(k1c), eps, kv_heads=Hkv)
     if out is None:
         out = torch.empty(B, H, 2 * d, dtype=vc.dtype, device=vc.device)
     need = workspace_bytes(OP_DECODE, p)

@@ -29,6 +29,13 @@
  *   - Tensor pointers are DEVICE pointers unless stated otherwise. Layout is contiguous
  *     row-major [B, H, N, feature] (feature = d for Q1/Q2/K1/K2, 2d for V and outputs);
  *     p->out_layout may make Y and dout token-major instead (diffattn_layout).
+ *   - Grouped-query attention: with p->kv_heads = Hkv < H, K1, K2 and V (and the decode
+ *     caches) hold Hkv heads, [B, Hkv, N, *], and query head h uses K/V head h / (H / Hkv).
+ *     Combining DiffAttn with GQA is named as a likely further speed-up
+ *     ("The Evolution of Transformer Attention", open-bookmarks-2024.blogspot.com, section
+ *     "Implementation and Future Prospects"); for decode the cache is 1 / (H / Hkv) the
+ *     size. Forward, decode, cache append and the QKV
+ *     projection take it; the backward needs kv_heads = heads (E_UNSUPPORTED otherwise).
  *   - The caller owns every buffer, including the workspace whose size is given by
  *     diffattn_workspace_bytes. The library keeps no state between calls and allocates
  *     no device memory.
@@ -81,6 +88,8 @@ typedef struct {
   float rms_eps;      /* eps of the per-head RMSNorm, >= 0, added inside the square root */
   diffattn_dtype dtype; /* element type of Q/K/V, outputs and gradients */
   int32_t out_layout;   /* diffattn_layout of Y and dout; 0 (BHN) when zero-initialised */
+  int64_t kv_heads;     /* heads of K1, K2, V (grouped-query attention: query head h reads
+                           K/V head h / (heads / kv_heads)); must divide heads; 0 = heads */
 } diffattn_problem;
 
 /* The per-layer lambda scalar, as written by diffattn_lambda into device memory and read
@@ -219,11 +228,13 @@ diffattn_status diffattn_cache_append(const diffattn_problem* p, const void* k1_
  * Attention With Multiple Heads": separate projections per head). One bf16 MFMA GEMM,
  * float32 accumulation, outputs rounded once to bf16 (nearest even).
  *   x       [B, N, d_model] (p->batch, p->seqlen)
- *   w_qkv   [3 H 2d, d_model], the fused weight in the [out_features, in_features] layout:
- *           rows [0, H 2d) are W_Q, then W_K, then W_V. Row h 2d + j d + c of W_Q gives
- *           channel c of Q_(j+1) in head h (j = 0, 1), likewise for W_K; row h 2d + c of
- *           W_V gives channel c of V in head h.
- *   q1, q2, k1, k2 [B, H, N, d];  v [B, H, N, 2d]   (outputs, the forward's input layout)
+ *   w_qkv   [(H + 2 Hkv) 2d, d_model], the fused weight in the [out_features, in_features]
+ *           layout: rows [0, H 2d) are W_Q, then Hkv 2d rows of W_K, then Hkv 2d of W_V
+ *           (Hkv = p->kv_heads, or H). Row h 2d + j d + c of W_Q gives channel c of
+ *           Q_(j+1) in head h (j = 0, 1), likewise for W_K; row h 2d + c of W_V gives
+ *           channel c of V in head h.
+ *   q1, q2 [B, H, N, d]; k1, k2 [B, Hkv, N, d]; v [B, Hkv, N, 2d]   (outputs, the
+ *           forward's input layout)
  * bf16 only; d a multiple of 32 (at most 256); d_model a multiple of 64 in [64, 65536];
  * H 2d <= 65536; B N < 2^31. Pointers 16-byte aligned; outputs must not overlap each
  * other or the inputs (E_ARG). No workspace. */

@@ -22,6 +22,9 @@ Sources (page title, then section / equation):
            Into Attention Calculations" (causal mask) and "Differential Attention
            With Multiple Heads" (lambda shared per layer, per-head RMSNorm,
            scale by 1 - lambda_init).
+  [BOOK]   "The Evolution of Transformer Attention" (open-bookmarks-2024.blogspot.com),
+           section "Implementation and Future Prospects" (DiffAttn combined with
+           grouped-query attention).
   [MLA]    "Multi-Head Latent Attention: Scaling LLM Serving Throughput via
            Low-Rank KV Compression" (priorstack.com, same tag page), section
            "The Memory Wall: Why the KV Cache Constrains LLM Serving" (the decode
@@ -42,7 +45,8 @@ lambda vectors, lambda = 0 against torch's float64 causal scaled-dot-product
 attention, Q2 = Q1 and K2 = K1 giving (1 - lambda) times softmax attention,
 rows of each map summing to one, row 0 attending only to V row 0, mask
 perturbation invariance, RMSNorm against torch's rms_norm, a scalar brute-force
-twin on tiny shapes, decode equal to the last prefill row, append-then-decode
+twin on tiny shapes, decode equal to the last prefill row, grouped-query
+attention equal to the same computation with K/V repeated per head, append-then-decode
 equal to the prefill row of the extended sequence, and central finite
 differences of the forward for every gradient.
 """
@@ -232,6 +236,10 @@ def forward(q1, q2, k1, k2, v, lam: float, lam_init: float, eps: float = DEFAULT
             weight=None, block: int = 1024, want_saved: bool = False, heads=None):
     """Batched DiffAttn forward: tensors [B, H, N, d] and V [B, H, N, 2d].
 
+    K1, K2 and V may have Hkv heads dividing H (grouped-query attention, named as
+    a further speed-up for DiffAttn in [BOOK] "Implementation and Future
+    Prospects"): query head h then uses K/V head h // (H / Hkv), the heads of a
+    group being consecutive.
     ``weight`` is the per-channel RMSNorm weight, shape [H, 2d] or None (unit).
     ``heads`` optionally restricts the work to a list of (b, h) pairs; the
     other outputs are left as NaN.
@@ -245,10 +253,12 @@ def forward(q1, q2, k1, k2, v, lam: float, lam_init: float, eps: float = DEFAULT
     if want_saved:
         saved = {k: np.full((B, H, N, dv), np.nan) for k in ("o1", "o2", "o")}
         saved.update({k: np.full((B, H, N), np.nan) for k in ("lse1", "lse2", "rstd")})
+    g = H // np.asarray(k1).shape[1]     # query heads per K/V head
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
         w = None if weight is None else np.asarray(weight)[h]
-        r = head_forward(q1[b, h], q2[b, h], k1[b, h], k2[b, h], v[b, h], lam, lam_init,
+        kh = h // g
+        r = head_forward(q1[b, h], q2[b, h], k1[b, kh], k2[b, kh], v[b, kh], lam, lam_init,
                          eps, w, block, want_saved)
         if want_saved:
             y[b, h], sv = r
@@ -288,7 +298,8 @@ def decode(q1, q2, k1c, k2c, vc, cache_len, lam: float, lam_init: float,
            eps: float = DEFAULT_EPS, weight=None):
     """One decode step: a single query per (b, h) against its cached keys.
 
-    q1, q2 [B, H, d]; k1c, k2c [B, H, L, d]; vc [B, H, L, 2d]; cache_len [B] or
+    q1, q2 [B, H, d]; k1c, k2c [B, Hkv, L, d]; vc [B, Hkv, L, 2d] (query head
+    h reads cache head h // (H / Hkv), as in ``forward``); cache_len [B] or
     None (= L).  The cache already holds the new token, so the query sits at
     position len - 1 and sees keys 0 .. len - 1 (the causal mask of the
     prefill, last row).  Returns Y [B, H, 2d].
@@ -299,16 +310,18 @@ def decode(q1, q2, k1c, k2c, vc, cache_len, lam: float, lam_init: float,
     dv = np.asarray(vc).shape[-1]
     s = 1.0 / math.sqrt(d)
     y = np.empty((B, H, dv))
+    g = H // np.asarray(k1c).shape[1]
     for b in range(B):
         n = L if cache_len is None else int(cache_len[b])
         for h in range(H):
-            s1 = s * (_f64(k1c[b, h, :n]) @ _f64(q1[b, h]))
-            s2 = s * (_f64(k2c[b, h, :n]) @ _f64(q2[b, h]))
+            kh = h // g
+            s1 = s * (_f64(k1c[b, kh, :n]) @ _f64(q1[b, h]))
+            s2 = s * (_f64(k2c[b, kh, :n]) @ _f64(q2[b, h]))
             a1 = np.exp(s1 - s1.max())
             a1 /= a1.sum()
             a2 = np.exp(s2 - s2.max())
             a2 /= a2.sum()
-            o = (a1 - lam * a2) @ _f64(vc[b, h, :n])
+            o = (a1 - lam * a2) @ _f64(vc[b, kh, :n])
             w = None if weight is None else np.asarray(weight)[h]
             yy, _ = rms_norm_rows(o[None, :], eps, w)
             y[b, h] = (1.0 - lam_init) * yy[0]
@@ -343,27 +356,31 @@ def cache_append(k1_new, k2_new, v_new, k1c, k2c, vc, cache_len):
 # --------------------------------------------------------------------------
 # projections
 # --------------------------------------------------------------------------
-def qkv_proj(x, w_qkv, heads: int, head_dim: int):
+def qkv_proj(x, w_qkv, heads: int, head_dim: int, kv_heads=None):
     """The input projections: X times W_Q, W_K, W_V ([INTOAI] "Moving On To The
     Differential Transformer": Q and K are each split into two groups; "Differential
     Attention With Multiple Heads": two queries, two keys and a value per head).
 
-    x [B, N, d_model]; w_qkv [3 H 2d, d_model] in the [out_features, in_features]
-    layout, rows W_Q, then W_K, then W_V. Reading (the pages fix no column order):
-    row h 2d + j d + c of W_Q gives channel c of Q_(j+1) in head h, likewise for W_K,
-    and row h 2d + c of W_V gives channel c of V in head h.
-    Returns q1, q2, k1, k2 [B, H, N, d] and v [B, H, N, 2d], in float64.
+    x [B, N, d_model]; w_qkv [(H + 2 Hkv) 2d, d_model] in the [out_features,
+    in_features] layout, rows W_Q (H 2d), then W_K and W_V (Hkv 2d each; Hkv =
+    kv_heads, default H: grouped-query attention when smaller). Reading (the
+    pages fix no column order): row h 2d + j d + c of W_Q gives channel c of
+    Q_(j+1) in head h, likewise for W_K, and row h 2d + c of W_V gives channel c
+    of V in head h.
+    Returns q1, q2 [B, H, N, d], k1, k2 [B, Hkv, N, d] and v [B, Hkv, N, 2d], in
+    float64.
     """
     x, w = _f64(x), _f64(w_qkv)
     B, N, dm = x.shape
     H, d = heads, head_dim
-    if w.shape != (6 * H * d, dm):
-        raise ValueError("w_qkv must be [3 H 2d, d_model]")
-    y = x @ w.T                                   # [B, N, 3 H 2d]
-    hd2 = 2 * H * d
+    Hkv = H if kv_heads is None else kv_heads
+    if w.shape != (2 * d * (H + 2 * Hkv), dm):
+        raise ValueError("w_qkv must be [(H + 2 Hkv) 2d, d_model]")
+    y = x @ w.T                                   # [B, N, (H + 2 Hkv) 2d]
+    hd2, kd2 = 2 * H * d, 2 * Hkv * d
     q = y[..., :hd2].reshape(B, N, H, 2, d)
-    k = y[..., hd2:2 * hd2].reshape(B, N, H, 2, d)
-    v = y[..., 2 * hd2:].reshape(B, N, H, 2 * d)
+    k = y[..., hd2:hd2 + kd2].reshape(B, N, Hkv, 2, d)
+    v = y[..., hd2 + kd2:].reshape(B, N, Hkv, 2 * d)
     per_head = lambda t: np.ascontiguousarray(t.transpose(0, 2, 1, 3))   # [B, H, N, *]
     return (per_head(q[..., 0, :]), per_head(q[..., 1, :]), per_head(k[..., 0, :]),
             per_head(k[..., 1, :]), per_head(v))

@@ -576,6 +576,40 @@ def _pin_failures(m):
                     ok &= v[b, hh, i, c] == 2 * hd2 + hh * 2 * d + c + col
     if not ok:
         fails.append("qkv projection placement")
+    # grouped-query projection: H = 4 query heads, Hkv = 2 key/value heads
+    Hq, Hk = 4, 2
+    w = np.add.outer(np.arange(2 * d * (Hq + 2 * Hk)), 1000.0 * np.arange(dm))
+    q1, q2, k1, k2, v = m.qkv_proj(x, w, Hq, d, kv_heads=Hk)
+    qc, kc = 2 * Hq * d, 2 * Hk * d
+    ok = q1.shape == (B, Hq, N, d) and k1.shape == (B, Hk, N, d) and v.shape == (B, Hk, N, 2 * d)
+    for b in range(B):
+        for i in range(N):
+            col = 1000.0 * ((b * N + i) % dm)
+            for hh in range(Hk):
+                for c in range(d):
+                    base = hh * 2 * d + c
+                    ok &= k1[b, hh, i, c] == qc + base + col
+                    ok &= k2[b, hh, i, c] == qc + base + d + col
+                for c in range(2 * d):
+                    ok &= v[b, hh, i, c] == qc + kc + hh * 2 * d + c + col
+            ok &= q2[b, Hq - 1, i, 0] == (Hq - 1) * 2 * d + d + col
+    if not ok:
+        fails.append("grouped qkv projection placement")
+    # grouped-query attention = the same computation with each K/V head repeated for the
+    # query heads of its group (consecutive heads)
+    n, dd, Hq, Hk = 7, 4, 4, 2
+    q1, q2 = (rand(r, 1, Hq, n, dd) for _ in range(2))
+    k1, k2 = (rand(r, 1, Hk, n, dd) for _ in range(2))
+    v = rand(r, 1, Hk, n, 2 * dd)
+    rep = lambda t: np.repeat(t, Hq // Hk, axis=1)
+    yg = m.forward(q1, q2, k1, k2, v, 0.4, 0.3)
+    ym = m.forward(q1, q2, rep(k1), rep(k2), rep(v), 0.4, 0.3)
+    if not np.array_equal(yg, ym):
+        fails.append("grouped forward")
+    dg = m.decode(q1[:, :, -1], q2[:, :, -1], k1, k2, v, np.array([5]), 0.4, 0.3)
+    dm_ = m.decode(q1[:, :, -1], q2[:, :, -1], rep(k1), rep(k2), rep(v), np.array([5]), 0.4, 0.3)
+    if not np.array_equal(dg, dm_):
+        fails.append("grouped decode")
     # output projection: brute-force sums over the concatenated channels
     attn = rand(r, B, N, H, 2 * d)
     wo = rand(r, 5, H * 2 * d)
@@ -626,10 +660,16 @@ PLANTS = [
      '"dw": (1.0 - lam_init) * np.sum(dy * o, axis=0)'),
     ("query halves swapped", "return (per_head(q[..., 0, :]), per_head(q[..., 1, :]),",
      "return (per_head(q[..., 1, :]), per_head(q[..., 0, :]),"),
-    ("value block from the key rows", "v = y[..., 2 * hd2:].reshape", "v = y[..., hd2:2 * hd2].reshape"),
+    ("value block from the key rows", "v = y[..., hd2 + kd2:].reshape", "v = y[..., hd2:hd2 + kd2].reshape"),
     ("projection not transposed", "y = x @ w.T ", "y = x @ w.reshape(dm, -1) "),
     ("heads concatenated in reverse", "return a.reshape(B, N, H * d2) @",
      "return a[:, :, ::-1].reshape(B, N, H * d2) @"),
+    ("grouped forward maps heads modulo", "        kh = h // g\n        r = head_forward(",
+     "        kh = h % (H // g)\n        r = head_forward("),
+    ("grouped decode maps heads modulo", "            kh = h // g\n            s1 = s *",
+     "            kh = h % (H // g)\n            s1 = s *"),
+    ("grouped keys: head and half swapped", "k = y[..., hd2:hd2 + kd2].reshape(B, N, Hkv, 2, d)",
+     "k = y[..., hd2:hd2 + kd2].reshape(B, N, 2, Hkv, d).transpose(0, 1, 3, 2, 4)"),
     ("dlam sign", '"dlam": float(-np.sum(a2 * gv))', '"dlam": float(np.sum(a2 * gv))'),
 ]
 
