@@ -218,6 +218,205 @@ __global__ void __launch_bounds__(NT, 2) decode_split_kernel(
   }
 }
 
+// Grouped-query decode: GW query heads that share one cache head (GW divides the group
+// size G) are served by one workgroup, so each cache byte is read once for all of them
+// instead of once per query head. Same structure as decode_split_kernel, with every
+// per-head quantity (queries, scores, weights, m, l, accumulators) held GW times over
+// and 32-key rounds (to keep those in registers). Writes the same per-(b, h, split)
+// partials, so decode_combine_kernel finishes both.
+template <int GW>
+__global__ void __launch_bounds__(NT, 2) decode_group_kernel(
+    const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
+    const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
+    const bf16_t* __restrict__ v, const int32_t* __restrict__ cache_len,
+    float* __restrict__ partial, int64_t H, int64_t L, int n_split, int rounds, int G) {
+  constexpr int KPR = 32;                 // keys per wavefront round
+  constexpr int SGG = KPR / 8;            // score groups of 8 keys
+  constexpr int VIG = KPR / 4;            // value loads of 4 rows
+  __shared__ float red[4][2 * GW][PART];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int split = blockIdx.x;
+  const int64_t h0 = static_cast<int64_t>(blockIdx.y) * GW;   // first query head (b H + h)
+  const int64_t b = h0 / H;
+  int64_t len = cache_len ? static_cast<int64_t>(cache_len[b]) : L;
+  len = len < 1 ? 1 : (len > L ? L : len);
+  const int64_t split_len = static_cast<int64_t>(KPR) * 4 * rounds;
+  const int64_t s0 = static_cast<int64_t>(split) * split_len;
+  if (s0 >= len) return;
+
+  const int64_t kvh = b * (H / G) + (h0 - b * H) / G;   // the shared cache head
+  constexpr int kBufFlags = 0x00020000;
+  const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(k1 + kvh * L * D), 0, static_cast<int>(len * D * 2), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(k2 + kvh * L * D), 0, static_cast<int>(len * D * 2), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(v + kvh * L * DV), 0, static_cast<int>(len * DV * 2), kBufFlags);
+
+  const int r = lane >> 3, c = lane & 7;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x8 qa[GW], qb[GW];
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+    qa[g] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q1 + (h0 + g) * D + 8 * c));
+    qb[g] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q2 + (h0 + g) * D + 8 * c));
+  }
+  const int e = lane & 15, f = lane >> 4;
+  const int ko = r * D * 2 + 16 * c;
+  const int vo = f * DV * 2 + 16 * e;
+
+  const float cs = kLog2e / 8.0f;
+  float m1[GW], m2[GW], l1[GW], l2[GW], acc1[GW][8], acc2[GW][8];
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+    m1[g] = m2[g] = -INFINITY;
+    l1[g] = l2[g] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc1[g][t] = acc2[g][t] = 0.f;
+  }
+
+#pragma clang loop unroll(disable)
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int64_t kb = s0 + (static_cast<int64_t>(wv) * rounds + rd) * KPR;
+    if (kb >= len) break;
+    const int kbs = __builtin_amdgcn_readfirstlane(static_cast<int>(kb));
+    u32x4 kx[SGG], ky[SGG], vv[VIG];
+#pragma unroll
+    for (int sg = 0; sg < SGG; ++sg) {
+      kx[sg] = __builtin_amdgcn_raw_buffer_load_b128(rk1, ko + sg * 8 * D * 2, kbs * D * 2, 0);
+      ky[sg] = __builtin_amdgcn_raw_buffer_load_b128(rk2, ko + sg * 8 * D * 2, kbs * D * 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VIG; ++i)
+      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * 4 * DV * 2, kbs * DV * 2, 0);
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      float s1[SGG], s2[SGG];
+#pragma unroll
+      for (int sg = 0; sg < SGG; ++sg) {
+        float d1 = 0.f, d2 = 0.f;
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, kx[sg]), kc = __builtin_bit_cast(bf16x8, ky[sg]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x2 q1p = {qa[g][2 * t], qa[g][2 * t + 1]}, k1p = {ka[2 * t], ka[2 * t + 1]};
+          const bf16x2 q2p = {qb[g][2 * t], qb[g][2 * t + 1]}, k2p = {kc[2 * t], kc[2 * t + 1]};
+          d1 = __builtin_amdgcn_fdot2_f32_bf16(q1p, k1p, d1, false);
+          d2 = __builtin_amdgcn_fdot2_f32_bf16(q2p, k2p, d2, false);
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+          d1 += __shfl_xor(d1, o);
+          d2 += __shfl_xor(d2, o);
+        }
+        const bool ok = kb + 8 * sg + r < len;
+        s1[sg] = ok ? d1 * cs : -INFINITY;
+        s2[sg] = ok ? d2 * cs : -INFINITY;
+      }
+      float mx1 = s1[0], mx2 = s2[0];
+#pragma unroll
+      for (int sg = 1; sg < SGG; ++sg) {
+        mx1 = fmaxf(mx1, s1[sg]);
+        mx2 = fmaxf(mx2, s2[sg]);
+      }
+#pragma unroll
+      for (int o = 8; o < 64; o <<= 1) {
+        mx1 = fmaxf(mx1, __shfl_xor(mx1, o));
+        mx2 = fmaxf(mx2, __shfl_xor(mx2, o));
+      }
+      const float mn1 = fmaxf(m1[g], mx1), mn2 = fmaxf(m2[g], mx2);
+      const float al1 = fast_exp2(m1[g] - mn1), al2 = fast_exp2(m2[g] - mn2);
+      float sum1 = 0.f, sum2 = 0.f;
+#pragma unroll
+      for (int sg = 0; sg < SGG; ++sg) {
+        s1[sg] = fast_exp2(s1[sg] - mn1);   // now the weights p
+        s2[sg] = fast_exp2(s2[sg] - mn2);
+        sum1 += s1[sg];
+        sum2 += s2[sg];
+      }
+#pragma unroll
+      for (int o = 8; o < 64; o <<= 1) {
+        sum1 += __shfl_xor(sum1, o);
+        sum2 += __shfl_xor(sum2, o);
+      }
+      l1[g] = fmaf(l1[g], al1, sum1);
+      l2[g] = fmaf(l2[g], al2, sum2);
+      m1[g] = mn1;
+      m2[g] = mn2;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        acc1[g][t] *= al1;
+        acc2[g][t] *= al2;
+      }
+      // values: key 4 i + f, whose weight sits in register i / 2 of lanes 8 (key % 8)
+#pragma unroll
+      for (int i = 0; i < VIG; ++i) {
+        const int src = 32 * (i & 1) + 8 * f;
+        const float w1 = __shfl(s1[i >> 1], src);
+        const float w2 = __shfl(s2[i >> 1], src);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float lo = __uint_as_float(vv[i][t] << 16);
+          const float hi = __uint_as_float(vv[i][t] & 0xffff0000u);
+          acc1[g][2 * t] = fmaf(w1, lo, acc1[g][2 * t]);
+          acc1[g][2 * t + 1] = fmaf(w1, hi, acc1[g][2 * t + 1]);
+          acc2[g][2 * t] = fmaf(w2, lo, acc2[g][2 * t]);
+          acc2[g][2 * t + 1] = fmaf(w2, hi, acc2[g][2 * t + 1]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc1[g][t] += __shfl_xor(acc1[g][t], 16);
+      acc1[g][t] += __shfl_xor(acc1[g][t], 32);
+      acc2[g][t] += __shfl_xor(acc2[g][t], 16);
+      acc2[g][t] += __shfl_xor(acc2[g][t], 32);
+    }
+    if (lane == 0) {
+      red[wv][2 * g][0] = m1[g];
+      red[wv][2 * g][1] = l1[g];
+      red[wv][2 * g + 1][0] = m2[g];
+      red[wv][2 * g + 1][1] = l2[g];
+    }
+    if (f == 0) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        red[wv][2 * g][2 + 8 * e + t] = acc1[g][t];
+        red[wv][2 * g + 1][2 + 8 * e + t] = acc2[g][t];
+      }
+    }
+  }
+  __syncthreads();
+  // Merge the 4 wavefront states per head: thread = (map, channel), looping over heads.
+  if (tid < 2 * DV) {
+    const int mp = tid / DV, ch = tid % DV;
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      float* out = partial + ((h0 + g) * n_split + split) * 2 * PART;
+      const int row = 2 * g + mp;
+      float M = red[0][row][0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, red[w][row][0]);
+      float A = 0.f, S = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sc = fast_exp2(red[w][row][0] - M);
+        A = fmaf(red[w][row][2 + ch], sc, A);
+        S = fmaf(red[w][row][1], sc, S);
+      }
+      out[mp * PART + 2 + ch] = A;
+      if (ch == 0) {
+        out[mp * PART + 0] = M;
+        out[mp * PART + 1] = S;
+      }
+    }
+  }
+}
+
 __global__ void __launch_bounds__(DV) decode_combine_kernel(
     const float* __restrict__ partial, const int32_t* __restrict__ cache_len,
     const diffattn_lambda_state* __restrict__ lamst, const float* __restrict__ rms_w,
@@ -277,11 +476,29 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   using namespace dec;
   const int rounds = a.split_len / (KEYS_PER_ROUND * 4);
   const int64_t BH = a.B * a.H;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(a.n_split, static_cast<unsigned>(BH)), dim3(NT),
-                     0, s, static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
-                     static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
-                     static_cast<const bf16_t*>(a.v), a.cache_len, a.partial, a.H, a.L,
-                     a.n_split, rounds, a.G);
+  // Query heads served per workgroup: the largest of 4, 3, 2 dividing the group size.
+  const int gw = a.G % 4 == 0 ? 4 : (a.G % 3 == 0 ? 3 : (a.G % 2 == 0 ? 2 : 1));
+  auto group = [&](auto kern, int heads_per_wg) {
+    // 32-key rounds: twice as many per split as the 64-key rounds of the single-head kernel.
+    hipLaunchKernelGGL(kern, dim3(a.n_split, static_cast<unsigned>(BH / heads_per_wg)),
+                       dim3(NT), 0, s, static_cast<const bf16_t*>(a.q1),
+                       static_cast<const bf16_t*>(a.q2), static_cast<const bf16_t*>(a.k1),
+                       static_cast<const bf16_t*>(a.k2), static_cast<const bf16_t*>(a.v),
+                       a.cache_len, a.partial, a.H, a.L, a.n_split, 2 * rounds, a.G);
+  };
+  if (gw == 4) {
+    group(decode_group_kernel<4>, 4);
+  } else if (gw == 3) {
+    group(decode_group_kernel<3>, 3);
+  } else if (gw == 2) {
+    group(decode_group_kernel<2>, 2);
+  } else {
+    hipLaunchKernelGGL(decode_split_kernel, dim3(a.n_split, static_cast<unsigned>(BH)),
+                       dim3(NT), 0, s, static_cast<const bf16_t*>(a.q1),
+                       static_cast<const bf16_t*>(a.q2), static_cast<const bf16_t*>(a.k1),
+                       static_cast<const bf16_t*>(a.k2), static_cast<const bf16_t*>(a.v),
+                       a.cache_len, a.partial, a.H, a.L, a.n_split, rounds, a.G);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(BH)), dim3(DV), 0, s,

@@ -1,10 +1,12 @@
 """Grouped-query attention (K1, K2, V shared by groups of consecutive query heads) on the
 GPU: forward, decode and the QKV projection.
 
-Each GQA call is checked bitwise against the same library call with every K/V head
-repeated for the query heads of its group (the kernels read the same values), and
-against the float64 oracle at the bars of the MHA tests (bf16 outputs 2e-2 max-abs,
-float32 1e-5 normwise relative per head).
+Every GQA call is checked against the float64 oracle at the bars of the MHA tests (bf16
+outputs 2e-2 max-abs, float32 1e-5 normwise relative per head), and against the same
+library call with every K/V head repeated for the query heads of its group: bitwise for
+the forward (the same kernel reads the same values); for decode, where one workgroup
+serves several query heads with 32-key rounds instead of 64, within 2^-7 of each output
+(the float32 accumulation order differs, which can move a bf16 rounding by one unit).
 """
 import numpy as np
 import pytest
@@ -62,7 +64,7 @@ def test_decode_grouped(B, H, hkv, L, lens):
     y = da.decode(x["q1"], x["q2"], kv["k1"], kv["k2"], kv["v"], st, cache_len=cl)
     ym = da.decode(x["q1"], x["q2"], rep["k1"], rep["k2"], rep["v"], st, cache_len=cl)
     torch.cuda.synchronize()
-    assert torch.equal(y, ym)
+    assert np.all(np.abs(np64(y) - np64(ym)) <= 2.0 ** -7 * np.maximum(np.abs(np64(ym)), 1.0))
     ls = orc.lambda_scalar(*(np64(x[k]) for k in ("lq1", "lk1", "lq2", "lk2")), w.layer)
     ref = orc.decode(np64(x["q1"]), np64(x["q2"]), np64(kv["k1"]), np64(kv["k2"]),
                      np64(kv["v"]), lens, ls["lambda"], ls["lambda_init"])
