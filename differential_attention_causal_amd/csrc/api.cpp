@@ -403,7 +403,6 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
   if (st != DIFFATTN_OK) return st;
   if (p->dtype != DIFFATTN_BF16 || p->head_dim != 64) return DIFFATTN_E_UNSUPPORTED;
   if (p->seqlen > kMaxSeqBf16) return DIFFATTN_E_UNSUPPORTED;
-  if (kv_heads_of(p) != p->heads) return DIFFATTN_E_UNSUPPORTED;
   const int d = p->head_dim;
   // The lambda-vector gradients exist even for an empty problem (they are then zero).
   if (!lq1 || !lk1 || !lq2 || !lk2 || !lam || !dlq1 || !dlk1 || !dlq2 || !dlk2)
@@ -431,16 +430,18 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
   if (need > 0 && (!workspace || workspace_bytes < need)) return DIFFATTN_E_WORKSPACE;
   if (workspace && !aligned(workspace, 16)) return DIFFATTN_E_ARG;
   const size_t rows = static_cast<size_t>(p->batch) * p->heads * p->seqlen;
+  const size_t kv_rows = static_cast<size_t>(p->batch) * kv_heads_of(p) * p->seqlen;
   const size_t qk = rows * d * 2, vb = rows * 2 * d * 2, rb = rows * 4, ob = rows * 2 * d * 4;
+  const size_t kk = kv_rows * d * 2, kvb = kv_rows * 2 * d * 2;
   const size_t lb = static_cast<size_t>(d) * 4;
   const diffattn_saved s = saved ? *saved : diffattn_saved{nullptr, nullptr, nullptr, nullptr, nullptr};
-  const Span in[16] = {{q1, qk}, {q2, qk}, {k1, qk}, {k2, qk}, {v, vb}, {dout, vb},
+  const Span in[16] = {{q1, qk}, {q2, qk}, {k1, kk}, {k2, kk}, {v, kvb}, {dout, vb},
                        {lq1, lb}, {lk1, lb}, {lq2, lb}, {lk2, lb},
                        {lam, sizeof(diffattn_lambda_state)},
                        {rms_weight, static_cast<size_t>(p->heads) * 2 * d * sizeof(float)},
                        {s.lse1, rb}, {s.lse2, rb}, {s.o1, ob}, {s.o2, ob}};
   const size_t wb = static_cast<size_t>(p->heads) * 2 * d * sizeof(float);
-  const Span outs[12] = {{dq1, qk}, {dq2, qk}, {dk1, qk}, {dk2, qk}, {dv, vb}, {d_attn, ob},
+  const Span outs[12] = {{dq1, qk}, {dq2, qk}, {dk1, kk}, {dk2, kk}, {dv, kvb}, {d_attn, ob},
                          {dlq1, lb}, {dlk1, lb}, {dlq2, lb}, {dlk2, lb}, {workspace, need},
                          {d_rms_weight, wb}};
   if (any_overlap(outs, 12, in, 16)) return DIFFATTN_E_ARG;
@@ -460,6 +461,7 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
   a.dout_bnh = p->out_layout == DIFFATTN_LAYOUT_BNH;
   a.ws = static_cast<float*>(workspace);
   a.B = empty ? 0 : p->batch; a.H = p->heads; a.N = p->seqlen;
+  a.G = p->heads > 0 ? static_cast<int>(p->heads / kv_heads_of(p)) : 1;
   a.d = d;
   return hip_status(diffattn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream)), "bwd");
 }

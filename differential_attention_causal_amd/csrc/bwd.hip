@@ -481,23 +481,22 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2, const bf16_t* __restrict__ k1,
     const bf16_t* __restrict__ k2, const bf16_t* __restrict__ v, const bf16_t* __restrict__ gb,
     const f32x4* __restrict__ vec, const diffattn_lambda_state* __restrict__ lamst,
-    bf16_t* __restrict__ dk1, bf16_t* __restrict__ dk2, bf16_t* __restrict__ dv, int BH, int N) {
+    bf16_t* __restrict__ dk1, bf16_t* __restrict__ dk2, bf16_t* __restrict__ dv, int BHK, int N,
+    int G) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   using Sc = KvSched;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31, h = lane >> 5;
   const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int k0 = (bid / BH) * BW;      // early key blocks see the most queries: first
+  // K/V head bhk (of B x Hkv); with grouped-query attention its G query heads are the
+  // consecutive heads bhk G .. bhk G + G - 1, and their contributions to dK and dV add up
+  // in the accumulators.
+  const int bhk = bid % BHK;
+  const int k0 = (bid / BHK) * BW;     // early key blocks see the most queries: first
   const int key = k0 + 32 * wv + m;
-  const int64_t ho = static_cast<int64_t>(bh) * N;
-
+  const int64_t ho = static_cast<int64_t>(bhk) * N;   // K/V rows of this head
   KvRsrc rs;
-  rs.q1 = rsrc_words(q1 + ho * D, N * D * 2);
-  rs.q2 = rsrc_words(q2 + ho * D, N * D * 2);
-  rs.g = rsrc_words(gb + ho * DV, N * DV * 2);
-  rs.vec = rsrc_words(vec + ho, N * 16);
   // Query tiles from the block's first key on: rows beyond N read as zero (and then
   // contribute nothing: their Q and G rows are zero).
   const int qt0 = k0 / TB;
@@ -524,10 +523,6 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
       vr[i] = as_bf16x8(a);
     }
   }
-  // Tiles 0..2 on their way (the resident loads above complete before tile 0's).
-  kv_dma(rs, ldsu, 0, qt0 * TB, wv, lane);
-  if (nT > 1) kv_dma(rs, ldsu, 1, (qt0 + 1) * TB, wv, lane);
-  if (nT > 2) kv_dma(rs, ldsu, 2, (qt0 + 2) * TB, wv, lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     pin_a(kr1[i]);
@@ -555,6 +550,19 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
   const LaneAddr la = lane_addr(lane);
   const int vb = 128 * h;   // per-row vectors of rows 8 h ..
   auto slot_of = [&](int j) { return lds0 + ((j >> 1) & (NSLOT - 1)) * KV_SLOT; };
+#pragma clang loop unroll(disable)
+  for (int g = 0; g < G; ++g) {
+  const int64_t qo = (static_cast<int64_t>(bhk) * G + g) * N;   // query head bhk G + g
+  rs.q1 = rsrc_words(q1 + qo * D, N * D * 2);
+  rs.q2 = rsrc_words(q2 + qo * D, N * D * 2);
+  rs.g = rsrc_words(gb + qo * DV, N * DV * 2);
+  rs.vec = rsrc_words(vec + qo, N * 16);
+  // Every wave is done with the previous query head's tiles before the ring refills.
+  if (g > 0) barrier();
+  // Tiles 0..2 on their way (for g = 0 the resident loads above complete before tile 0's).
+  kv_dma(rs, ldsu, 0, qt0 * TB, wv, lane);
+  if (nT > 1) kv_dma(rs, ldsu, 1, (qt0 + 1) * TB, wv, lane);
+  if (nT > 2) kv_dma(rs, ldsu, 2, (qt0 + 2) * TB, wv, lane);
   const float lam = lamst->lambda_f;
   const float c = kLog2e / 8.0f;   // log2(e) / sqrt(64)
   // Causal test: key > query for register e of sub-tile j  <=>  idx_of(e, 0) > kq - 32 j.
@@ -802,6 +810,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
       if constexpr (t == 2) adk2[b] = mfma(a, words(g2w[1], ks), adk2[b]);
     });
   }
+  }   // query heads of the group
 
   // Stores: register j of block b holds channel 32 b + 8 (j / 4) + 4 h + j % 4 of the key.
   if (key < N) {
@@ -865,7 +874,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2, const bf16_t* __restrict__ k1,
     const bf16_t* __restrict__ k2, const bf16_t* __restrict__ v, const bf16_t* __restrict__ gb,
     const f32x4* __restrict__ vec, const diffattn_lambda_state* __restrict__ lamst,
-    bf16_t* __restrict__ dq1, bf16_t* __restrict__ dq2, int BH, int N, int nqb) {
+    bf16_t* __restrict__ dq1, bf16_t* __restrict__ dq2, int BH, int N, int nqb, int G) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   using Sc = QSched;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -879,9 +888,11 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
   const int64_t ho = static_cast<int64_t>(bh) * N;
 
   QRsrc rs;
-  rs.k1 = rsrc_words(k1 + ho * D, N * D * 2);
-  rs.k2 = rsrc_words(k2 + ho * D, N * D * 2);
-  rs.v = rsrc_words(v + ho * DV, N * DV * 2);
+  // K/V head of this query head (G consecutive query heads share one).
+  const int64_t kvo = static_cast<int64_t>(bh / G) * N;
+  rs.k1 = rsrc_words(k1 + kvo * D, N * D * 2);
+  rs.k2 = rsrc_words(k2 + kvo * D, N * D * 2);
+  rs.v = rsrc_words(v + kvo * DV, N * DV * 2);
   // Key tiles 0 .. up to the block's last query (keys beyond N read as zero and are
   // masked: they follow every query).
   const int kend = min(N, q0 + BW);
@@ -1203,19 +1214,20 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     const int BH = static_cast<int>(a.B * a.H);
     const int N = static_cast<int>(a.N);
     const int nb = static_cast<int>((a.N + BW - 1) / BW);
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(static_cast<unsigned>(BH * nb)), dim3(NT), KV_LDS, s,
-                       static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
+    const int BHK = BH / a.G;
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(static_cast<unsigned>(BHK * nb)), dim3(NT), KV_LDS,
+                       s, static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
                        static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
                        static_cast<const bf16_t*>(a.v), gbuf, vec, a.lam,
                        static_cast<bf16_t*>(a.dk1), static_cast<bf16_t*>(a.dk2),
-                       static_cast<bf16_t*>(a.dv), BH, N);
+                       static_cast<bf16_t*>(a.dv), BHK, N, a.G);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dq_kernel, dim3(static_cast<unsigned>(BH * nb)), dim3(NT), Q_LDS, s,
                        static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
                        static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
                        static_cast<const bf16_t*>(a.v), gbuf, vec, a.lam,
-                       static_cast<bf16_t*>(a.dq1), static_cast<bf16_t*>(a.dq2), BH, N, nb);
+                       static_cast<bf16_t*>(a.dq1), static_cast<bf16_t*>(a.dq2), BH, N, nb, a.G);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

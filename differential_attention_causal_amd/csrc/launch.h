@@ -52,6 +52,7 @@ struct BwdArgs {
   bool dout_bnh;             // dout is [B, N, H, 2d] instead of [B, H, N, 2d]
   float* ws;                 // workspace (float32)
   int64_t B, H, N;
+  int G;                     // query heads per K/V head (k1, k2, v, dk1, dk2, dv: H / G heads)
   int d;
 };
 

@@ -351,7 +351,8 @@ def backward(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, lam_state, saved, dout, rms_
     lay = _layout(layout)
     if tuple(dout.shape) != _y_shape(B, H, N, d, lay):
         raise ValueError("dout does not match the layout")
-    p = problem(B, H, N, d, _dtype_code(q1), eps, lay)
+    Hkv = k1.shape[1]     # grouped-query attention when fewer than H
+    p = problem(B, H, N, d, _dtype_code(q1), eps, lay, kv_heads=Hkv)
     g = {"dq1": torch.empty_like(q1), "dq2": torch.empty_like(q2), "dk1": torch.empty_like(k1),
          "dk2": torch.empty_like(k2), "dv": torch.empty_like(v),
          "d_attn": torch.empty(B, H, N, 2 * d, dtype=torch.float32, device=q1.device)}

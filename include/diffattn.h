@@ -35,7 +35,8 @@
  *     ("The Evolution of Transformer Attention", open-bookmarks-2024.blogspot.com, section
  *     "Implementation and Future Prospects"); for decode the cache is 1 / (H / Hkv) the
  *     size. Forward, decode, cache append and the QKV
- *     projection take it; the backward needs kv_heads = heads (E_UNSUPPORTED otherwise).
+ *     projection take it, and so does the backward (dK1, dK2 and dV of a shared head sum
+ *     the contributions of its query heads).
  *   - The caller owns every buffer, including the workspace whose size is given by
  *     diffattn_workspace_bytes. The library keeps no state between calls and allocates
  *     no device memory.
@@ -264,7 +265,8 @@ diffattn_status diffattn_out_proj(const diffattn_problem* p, int64_t d_model, co
  *   dlq2 = -dlambda e^b lk2;  dlk2 = -dlambda e^b lq2   (lambda_init gets no gradient)
  *   inputs  q1..v, lq1..lk2 (device float32 [d]), lam, rms_weight (or NULL), saved (from
  *           diffattn_fwd in training mode on the same inputs), dout [B, H, N, 2d]
- *   outputs dq1, dq2, dk1, dk2 [B, H, N, d]; dv [B, H, N, 2d] (all p->dtype);
+ *   outputs dq1, dq2 [B, H, N, d]; dk1, dk2 [B, Hkv, N, d]; dv [B, Hkv, N, 2d] (all
+ *           p->dtype; Hkv = p->kv_heads or H, and k1, k2, v have Hkv heads too);
  *           d_attn [B, H, N, 2d] float32 = G, the gradient at the RMSNorm input;
  *           dlq1, dlk1, dlq2, dlk2 device float32 [d];
  *           d_rms_weight device float32 [H, 2d] (the RMSNorm weight gradient), or NULL to

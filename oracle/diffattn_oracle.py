@@ -452,6 +452,9 @@ def backward(q1, q2, k1, k2, v, dy, lq1, lk1, lq2, lk2, layer: int,
     lambda_init is a constant of the layer index and receives no gradient.
     d_rms_weight [H, 2d] sums each head's dw over the batch (the weight is one
     per head and channel).
+    With grouped-query attention (K1, K2, V with Hkv < H heads, query head h
+    reading K/V head h // (H / Hkv)) dk1, dk2 and dv of a K/V head sum the
+    contributions of the query heads of its group.
     ``heads`` restricts the per-head tensors to the listed (b, h) pairs (the
     others stay NaN); dlam and the vector gradients then cover only those.
     """
@@ -459,19 +462,30 @@ def backward(q1, q2, k1, k2, v, dy, lq1, lk1, lq2, lk2, layer: int,
     lam, li = st["lambda"], st["lambda_init"]
     q1 = np.asarray(q1)
     B, H, N, d = q1.shape
+    Hkv = np.asarray(k1).shape[1]
+    g = H // Hkv
     dvw = np.asarray(v).shape[-1]
-    out = {k: np.full((B, H, N, d), np.nan) for k in ("dq1", "dq2", "dk1", "dk2")}
-    out["dv"] = np.full((B, H, N, dvw), np.nan)
+    out = {k: np.full((B, H, N, d), np.nan) for k in ("dq1", "dq2")}
+    out.update({k: np.full((B, Hkv, N, d), np.nan) for k in ("dk1", "dk2")})
+    out["dv"] = np.full((B, Hkv, N, dvw), np.nan)
     out["d_attn"] = np.full((B, H, N, dvw), np.nan)
     out["d_rms_weight"] = np.zeros((H, dvw))
     dlam = 0.0
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    seen = set()       # K/V heads that already hold a contribution
     for b, h in pairs:
         w = None if weight is None else np.asarray(weight)[h]
-        r = head_backward(q1[b, h], q2[b, h], k1[b, h], k2[b, h], v[b, h], dy[b, h],
+        kh = h // g
+        r = head_backward(q1[b, h], q2[b, h], k1[b, kh], k2[b, kh], v[b, kh], dy[b, h],
                           lam, li, eps, w)
-        for k in ("dq1", "dq2", "dk1", "dk2", "dv", "d_attn"):
+        for k in ("dq1", "dq2", "d_attn"):
             out[k][b, h] = r[k]
+        for k in ("dk1", "dk2", "dv"):
+            if (b, kh) in seen:
+                out[k][b, kh] = out[k][b, kh] + r[k]
+            else:
+                out[k][b, kh] = r[k]
+        seen.add((b, kh))
         out["d_rms_weight"][h] += r["dw"]
         dlam += r["dlam"]
     lq1, lk1, lq2, lk2 = (_f64(x) for x in (lq1, lk1, lq2, lk2))

@@ -302,10 +302,10 @@ def test_grouped_query_argument_checks():
     assert fwd(da.problem(1, 8, 64, 64, da.BF16, kv_heads=3)) == da.E_ARG    # 3 does not divide 8
     assert fwd(da.problem(1, 8, 64, 64, da.BF16, kv_heads=16)) == da.E_ARG   # more K/V than Q heads
     assert fwd(da.problem(1, 8, 64, 64, da.BF16, kv_heads=-1)) == da.E_ARG
-    # the backward takes only kv_heads = heads
-    p = da.problem(2, 4, 128, 64, da.BF16, kv_heads=2)
+    # the backward also validates the grouping
+    p = da.problem(2, 4, 128, 64, da.BF16, kv_heads=3)
     sv = da.Saved(*(A * 64 * (40 + i) for i in range(5)))
     args = [addr(i * 64) for i in range(23)]
     st = lib.diffattn_bwd(ctypes.byref(p), *args[:11], ctypes.byref(sv), *args[11:23], ws,
                           1 << 30, None)
-    assert st == da.E_UNSUPPORTED
+    assert st == da.E_ARG

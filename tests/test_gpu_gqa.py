@@ -107,3 +107,35 @@ def test_qkv_proj_grouped(B, N, H, hkv, dm):
         assert tuple(g.shape) == r.shape, name
         bound = 2.0 * (np.abs(r) * 2.0 ** -9 + dm * 2.0 ** -24 * a) + 1e-30
         assert np.all(np.abs(np64(g) - r) <= bound), name
+
+
+@pytest.mark.parametrize("B,H,hkv,N", [(1, 4, 2, 200), (2, 4, 1, 129), (1, 6, 3, 64)])
+def test_backward_grouped(B, H, hkv, N):
+    """dK and dV of a shared head collect the contributions of its query heads: against
+    the oracle (normwise relative 5e-2 per tensor, as for MHA), and against the sum over
+    each group of the MHA backward on repeated K/V."""
+    from tests.test_gpu_backward import TOL, rel
+    w = synth.custom("train", B, H, N, 64, 5, "bf16", number=1900 + N + H)
+    x, _ = draw(w)
+    kv, rep = _group(x, hkv)
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    lv = (x["lq1"], x["lk1"], x["lq2"], x["lk2"])
+    sv = da.alloc_saved(B, H, N, 64, DEV)
+    da.forward(x["q1"], x["q2"], kv["k1"], kv["k2"], kv["v"], st, saved=sv)
+    g = da.backward(x["q1"], x["q2"], kv["k1"], kv["k2"], kv["v"], *lv, st, sv, x["dout"])
+    svm = da.alloc_saved(B, H, N, 64, DEV)
+    da.forward(x["q1"], x["q2"], rep["k1"], rep["k2"], rep["v"], st, saved=svm)
+    gm = da.backward(x["q1"], x["q2"], rep["k1"], rep["k2"], rep["v"], *lv, st, svm, x["dout"])
+    torch.cuda.synchronize()
+    ref = orc.backward(np64(x["q1"]), np64(x["q2"]), np64(kv["k1"]), np64(kv["k2"]),
+                       np64(kv["v"]), np64(x["dout"]), *(np64(t) for t in lv), w.layer)
+    scale = max(float(np.max(np.abs(ref["dv"]))), 1e-30)
+    for k in ("dq1", "dq2", "dk1", "dk2", "dv", "d_attn"):
+        assert tuple(g[k].shape) == ref[k].shape, k
+        assert rel(np64(g[k]), ref[k], scale) <= TOL, k
+    gsz = H // hkv
+    for k in ("dk1", "dk2", "dv"):
+        summed = np64(gm[k]).reshape(B, hkv, gsz, N, -1).sum(axis=2)
+        assert rel(np64(g[k]), summed, scale) <= TOL, k
+    for k in ("dq1", "dq2", "d_attn", "dlq1", "d_rms_weight"):
+        assert rel(np64(g[k]), np64(gm[k]), 1.0) <= 1e-6, k   # same kernels, same inputs

@@ -353,6 +353,36 @@ def _fd_check(n, d, B, H, layer, n_samples, seed, weight_on):
     assert abs(g["dlam"] + np.sum(g["d_attn"] * sv["o2"])) < 1e-9 * max(1, abs(g["dlam"]))
 
 
+def test_backward_finite_differences_grouped():
+    """Grouped-query attention: 4 query heads share 2 K/V heads, so dK and dV of a shared
+    head collect both query heads' contributions; central differences of the grouped
+    forward check every gradient entry."""
+    r = rng(23)
+    B, H, Hk, n, d = 1, 4, 2, 6, 4
+    p = {k: rand(r, B, H, n, d) for k in ("q1", "q2")}
+    p.update({k: rand(r, B, Hk, n, d) for k in ("k1", "k2")})
+    p["v"] = rand(r, B, Hk, n, 2 * d)
+    for k in ("lq1", "lk1", "lq2", "lk2"):
+        p[k] = rand(r, d, scale=0.1)
+    dy = rand(r, B, H, n, 2 * d)
+    g = orc.backward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"], dy, p["lq1"], p["lk1"],
+                     p["lq2"], p["lk2"], 3)
+    h = 1e-6
+    for name in ("q1", "k1", "k2", "v", "lq2"):
+        flat = p[name].reshape(-1)
+        fd = np.empty(flat.size)
+        for j in range(flat.size):
+            old = flat[j]
+            flat[j] = old + h
+            lp = _loss(p, dy, 3, 1e-5, None)
+            flat[j] = old - h
+            lm = _loss(p, dy, 3, 1e-5, None)
+            flat[j] = old
+            fd[j] = (lp - lm) / (2 * h)
+        an = g["d" + name].reshape(-1)
+        assert np.max(np.abs(an - fd)) / max(np.max(np.abs(an)), 1e-12) < 2e-6, name
+
+
 def test_backward_finite_differences_small_full():
     _fd_check(n=9, d=4, B=1, H=2, layer=3, n_samples=10 ** 9, seed=21, weight_on=True)
 
@@ -534,6 +564,31 @@ def _pin_failures(m):
         an = g["d" + name].reshape(-1)
         if np.max(np.abs(an - fd)) > 1e-5 * max(np.max(np.abs(fd)), 1e-9):
             fails.append("fd " + name)
+    # grouped-query backward: dV of a K/V head shared by two query heads, by central
+    # differences of the grouped forward
+    pg = {k: rand(r, 1, 2, 4, 3) for k in ("q1", "q2")}
+    pg.update({k: rand(r, 1, 1, 4, 3) for k in ("k1", "k2")})
+    pg["v"] = rand(r, 1, 1, 4, 6)
+    for k in ("lq1", "lk1", "lq2", "lk2"):
+        pg[k] = p[k][:3].copy()
+    dyg = rand(r, 1, 2, 4, 6)
+    gg = m.backward(pg["q1"], pg["q2"], pg["k1"], pg["k2"], pg["v"], dyg, pg["lq1"],
+                    pg["lk1"], pg["lq2"], pg["lk2"], 3)
+    stg = m.lambda_scalar(pg["lq1"], pg["lk1"], pg["lq2"], pg["lk2"], 3)
+    fv = pg["v"].reshape(-1)
+    fdg = np.empty(fv.size)
+    for j in range(fv.size):
+        old = fv[j]
+        fv[j] = old + h
+        lp = float(np.sum(m.forward(pg["q1"], pg["q2"], pg["k1"], pg["k2"], pg["v"],
+                                    stg["lambda"], stg["lambda_init"]) * dyg))
+        fv[j] = old - h
+        lm = float(np.sum(m.forward(pg["q1"], pg["q2"], pg["k1"], pg["k2"], pg["v"],
+                                    stg["lambda"], stg["lambda_init"]) * dyg))
+        fv[j] = old
+        fdg[j] = (lp - lm) / (2 * h)
+    if np.max(np.abs(gg["dv"].reshape(-1) - fdg)) > 1e-5 * max(np.max(np.abs(fdg)), 1e-9):
+        fails.append("fd grouped dv")
     # the RMSNorm weight gradient, by central differences of the same loss
     wgt = 1.0 + 0.3 * rand(r, H, 2 * d)
     gw = m.backward(p["q1"], p["q2"], p["k1"], p["k2"], p["v"], dy, p["lq1"], p["lk1"],
@@ -670,6 +725,8 @@ PLANTS = [
      "            kh = h % (H // g)\n            s1 = s *"),
     ("grouped keys: head and half swapped", "k = y[..., hd2:hd2 + kd2].reshape(B, N, Hkv, 2, d)",
      "k = y[..., hd2:hd2 + kd2].reshape(B, N, 2, Hkv, d).transpose(0, 1, 3, 2, 4)"),
+    ("grouped dK keeps one head", "                out[k][b, kh] = out[k][b, kh] + r[k]",
+     "                out[k][b, kh] = r[k]"),
     ("dlam sign", '"dlam": float(-np.sum(a2 * gv))', '"dlam": float(np.sum(a2 * gv))'),
 ]
 
