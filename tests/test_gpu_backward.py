@@ -174,13 +174,14 @@ def test_backward_training_workload_sampled():
 
 def test_backward_lambda_vectors_full_length():
     """Two heads at the full sequence length of the training workload: the lambda-vector
-    gradients sum over every row."""
+    gradients and the RMSNorm weight gradient sum over every row."""
     w = synth.custom("train", 1, 2, 4096, 64, 6, "bf16", number=740)
     x, h = draw(w)
     g = run_train(x, w)
     ref = orc.backward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], h["dout"], h["lq1"],
                        h["lk1"], h["lq2"], h["lk2"], w.layer)
     compare(g, ref, [(0, 0), (0, 1)], h, w.layer)
+    check_weight_grad(g, ref)
 
 
 def test_backward_deterministic():
