@@ -16,6 +16,9 @@ Also reported in the same line:
             Q1/Q2/K1/K2/V) and the output projection (token-major Y [32768, 2048] x W_O^T),
             TFLOP/s at 2 M N K each against the bf16 peak, and the whole module step
             (projection, lambda, forward with token-major output, projection).
+  ref_gemm - the box's best bf16 matrix-core rate through the vendor library (torch.matmul,
+            8192^3), and the forward's rate as a fraction of it (a measured reference next to
+            the nominal 2.5 PFLOP/s).
   copy    - a plain 2 GiB device-to-device copy: the HBM rate this machine reaches,
             and the kernel the HBM byte counters are calibrated on.
   roofline - for the dominant kernel (the forward), achieved TFLOP/s from HIP
@@ -109,9 +112,11 @@ def leg_forward(steps, warmup):
     fl = fwd_flops(w)
     kern_ms = sum(inner) / len(inner)
     achieved = fl / (kern_ms * 1e-3) / 1e12
+    srt = sorted(inner)
     return w, {
         "ms_per_step": ms, "wall_ms_per_step": wall, "tflops": fl / (ms * 1e-3) / 1e12,
-        "fwd_kernel_ms": kern_ms, "flops_per_launch": fl,
+        "fwd_kernel_ms": kern_ms, "fwd_kernel_ms_median": srt[len(srt) // 2],
+        "fwd_kernel_ms_min": srt[0], "flops_per_launch": fl,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic_from_profiles("fwd_bf16_kernel<false>", "fwd_bf16.hip", w.name)},
@@ -281,6 +286,30 @@ def leg_proj(steps, warmup):
     return res
 
 
+def leg_ref_gemm(steps, warmup):
+    """The best bf16 matrix-core rate this box shows through the vendor library
+    (torch.matmul -> hipBLASLt, 8192^3): a measured reference beside the nominal peak."""
+    import torch
+    n = 8192
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    a = torch.randn(n, n, generator=g, device="cuda:0").to(torch.bfloat16)
+    b = torch.randn(n, n, generator=g, device="cuda:0").to(torch.bfloat16)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda:0")
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev:
+            ev[0].record()
+        torch.matmul(a, b, out=c)
+        if ev:
+            ev[1].record()
+
+    _, _, inner = time_steps(step, max(5, steps // 4), warmup, inner_events=True)
+    k_ms = sorted(inner)[len(inner) // 2]
+    return {"shape": f"{n}^3 bf16 (torch.matmul, hipBLASLt)", "ms": k_ms,
+            "tflops": 2.0 * n ** 3 / (k_ms * 1e-3) / 1e12}
+
+
 def leg_copy(steps, warmup):
     """A plain 2 GiB device-to-device copy: the measured HBM reference, and the kernel the
     FETCH_SIZE / WRITE_SIZE counters are calibrated on."""
@@ -380,9 +409,9 @@ def cpu_baseline(budget_s: float = 12.0, cap_s: float = 30.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="fwd,decode,train,proj,copy")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--legs", default="fwd,decode,train,proj,refgemm,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -407,6 +436,8 @@ def main():
         "pct_bf16_mfma_peak": 100.0 * fwd["tflops"] / PEAK_BF16_TFLOPS,
         "roofline": fwd["roofline"],
         "fwd_kernel_ms": fwd["fwd_kernel_ms"],
+        "fwd_kernel_ms_median": fwd["fwd_kernel_ms_median"],
+        "fwd_kernel_ms_min": fwd["fwd_kernel_ms_min"],
         "formula_tflops_8dP": fwd["formula_tflops_8dP"],
     }
     if "decode" in legs:
@@ -415,6 +446,9 @@ def main():
         rec["train"] = leg_train(max(1, args.steps // 2), args.warmup)
     if "proj" in legs:
         rec["proj"] = leg_proj(args.steps, args.warmup)
+    if "refgemm" in legs:
+        rec["ref_gemm"] = leg_ref_gemm(args.steps, args.warmup)
+        rec["ref_gemm"]["fwd_frac_of_it"] = fwd["roofline"]["achieved"] / rec["ref_gemm"]["tflops"]
     if "copy" in legs:
         rec["copy"] = leg_copy(args.steps, args.warmup)
     if not args.no_cpu_baseline:
