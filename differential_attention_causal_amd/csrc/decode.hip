@@ -224,6 +224,42 @@ __global__ void __launch_bounds__(NT, 2) decode_split_kernel(
 // per-head quantity (queries, scores, weights, m, l, accumulators) held GW times over
 // and 32-key rounds (to keep those in registers). Writes the same per-(b, h, split)
 // partials, so decode_combine_kernel finishes both.
+// Cross-lane reductions without the LDS crossbar. Score lanes come in groups of 8 (lanes
+// 8 r .. 8 r + 7, one key per group). sum8 adds over a group (DPP: quad swaps 1 and 2,
+// then the mirror inside 8 lanes); the *_groups forms combine the 8 groups of a
+// wavefront, whose values are uniform within each group (the mirror inside 16 lanes
+// pairs groups 2k and 2k + 1, then rows are exchanged by the permlane swaps).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp<0x141>(x);   // row_half_mirror
+  return x;
+}
+template <bool MAX>
+__device__ __forceinline__ float combine(float a, float b) { return MAX ? fmaxf(a, b) : a + b; }
+// The swaps exchange rows between two registers that both start as x: afterwards each
+// lane holds its own row's value in one and the partner row's in the other (rows of 16
+// lanes paired 0-1, 2-3 by the 16-lane swap; halves of the wavefront by the 32-lane
+// swap). Issued as assembly: the compiler's model of the swap builtins folded the two
+// results into one. The s_nop wait states cover the vector-ALU write before the swap and
+// the reads after it.
+template <bool MAX>
+__device__ __forceinline__ float across_groups(float x) {
+  x = combine<MAX>(x, dpp<0x140>(x));   // row_mirror
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  x = combine<MAX>(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  a = __builtin_bit_cast(uint32_t, x);
+  b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return combine<MAX>(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
 template <int GW>
 __global__ void __launch_bounds__(NT, 2) decode_group_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
@@ -305,11 +341,8 @@ __global__ void __launch_bounds__(NT, 2) decode_group_kernel(
           d1 = __builtin_amdgcn_fdot2_f32_bf16(q1p, k1p, d1, false);
           d2 = __builtin_amdgcn_fdot2_f32_bf16(q2p, k2p, d2, false);
         }
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-          d1 += __shfl_xor(d1, o);
-          d2 += __shfl_xor(d2, o);
-        }
+        d1 = sum8(d1);
+        d2 = sum8(d2);
         const bool ok = kb + 8 * sg + r < len;
         s1[sg] = ok ? d1 * cs : -INFINITY;
         s2[sg] = ok ? d2 * cs : -INFINITY;
@@ -320,11 +353,8 @@ __global__ void __launch_bounds__(NT, 2) decode_group_kernel(
         mx1 = fmaxf(mx1, s1[sg]);
         mx2 = fmaxf(mx2, s2[sg]);
       }
-#pragma unroll
-      for (int o = 8; o < 64; o <<= 1) {
-        mx1 = fmaxf(mx1, __shfl_xor(mx1, o));
-        mx2 = fmaxf(mx2, __shfl_xor(mx2, o));
-      }
+      mx1 = across_groups<true>(mx1);
+      mx2 = across_groups<true>(mx2);
       const float mn1 = fmaxf(m1[g], mx1), mn2 = fmaxf(m2[g], mx2);
       const float al1 = fast_exp2(m1[g] - mn1), al2 = fast_exp2(m2[g] - mn2);
       float sum1 = 0.f, sum2 = 0.f;
@@ -335,11 +365,8 @@ __global__ void __launch_bounds__(NT, 2) decode_group_kernel(
         sum1 += s1[sg];
         sum2 += s2[sg];
       }
-#pragma unroll
-      for (int o = 8; o < 64; o <<= 1) {
-        sum1 += __shfl_xor(sum1, o);
-        sum2 += __shfl_xor(sum2, o);
-      }
+      sum1 = across_groups<false>(sum1);
+      sum2 = across_groups<false>(sum2);
       l1[g] = fmaf(l1[g], al1, sum1);
       l2[g] = fmaf(l2[g], al2, sum2);
       m1[g] = mn1;
