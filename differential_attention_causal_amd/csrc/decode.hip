@@ -444,38 +444,84 @@ __global__ void __launch_bounds__(NT, 2) decode_group_kernel(
   }
 }
 
-__global__ void __launch_bounds__(DV) decode_combine_kernel(
+// One thread per map and channel (map k = threadIdx.x / 128). The partials of the
+// splits are read in batches of CB independent loads, so the merge waits for memory once
+// when there are at most CB splits and a few times per map otherwise; the order of the
+// arithmetic (maximum over all splits first, then the rescaled sums in split order) does
+// not depend on the batching.
+constexpr int CB = 16;
+__global__ void __launch_bounds__(2 * DV) decode_combine_kernel(
     const float* __restrict__ partial, const int32_t* __restrict__ cache_len,
     const diffattn_lambda_state* __restrict__ lamst, const float* __restrict__ rms_w,
     bf16_t* __restrict__ out, int64_t H, int64_t L, int n_split, int64_t split_len,
     float eps) {
+  __shared__ float o2[DV];
   __shared__ float wsum[2];
-  const int ch = threadIdx.x;
+  const int mp = threadIdx.x >> 7;
+  const int ch = threadIdx.x & (DV - 1);
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / H;
   int64_t len = cache_len ? static_cast<int64_t>(cache_len[b]) : L;
   len = len < 1 ? 1 : (len > L ? L : len);
   const int nv = static_cast<int>((len + split_len - 1) / split_len);
-  const float* P = partial + bh * n_split * 2 * PART;
-  float o[2];
+  const float* P = partial + bh * n_split * 2 * PART + mp * PART;
+  float M = -INFINITY, A = 0.f, S = 0.f;
+  if (nv <= CB) {
+    float m[CB], l[CB], a[CB];
 #pragma unroll
-  for (int mp = 0; mp < 2; ++mp) {
-    float M = -INFINITY;
-    for (int s = 0; s < nv; ++s) M = fmaxf(M, P[s * 2 * PART + mp * PART]);
-    float A = 0.f, S = 0.f;
-    for (int s = 0; s < nv; ++s) {
-      const float* ps = P + s * 2 * PART + mp * PART;
-      const float sc = fast_exp2(ps[0] - M);
-      S = fmaf(ps[1], sc, S);
-      A = fmaf(ps[2 + ch], sc, A);
+    for (int i = 0; i < CB; ++i) {
+      const float* ps = P + (i < nv ? i : 0) * 2 * PART;
+      m[i] = ps[0];
+      l[i] = ps[1];
+      a[i] = ps[2 + ch];
     }
-    o[mp] = A / S;
+#pragma unroll
+    for (int i = 0; i < CB; ++i) M = fmaxf(M, m[i]);
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      if (i < nv) {
+        const float sc = fast_exp2(m[i] - M);
+        S = fmaf(l[i], sc, S);
+        A = fmaf(a[i], sc, A);
+      }
+    }
+  } else {
+    for (int s0 = 0; s0 < nv; s0 += CB) {
+      float m[CB];
+#pragma unroll
+      for (int i = 0; i < CB; ++i) m[i] = P[(s0 + i < nv ? s0 + i : s0) * 2 * PART];
+#pragma unroll
+      for (int i = 0; i < CB; ++i) M = fmaxf(M, m[i]);
+    }
+    for (int s0 = 0; s0 < nv; s0 += CB) {
+      float m[CB], l[CB], a[CB];
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const float* ps = P + (s0 + i < nv ? s0 + i : s0) * 2 * PART;
+        m[i] = ps[0];
+        l[i] = ps[1];
+        a[i] = ps[2 + ch];
+      }
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        if (s0 + i < nv) {
+          const float sc = fast_exp2(m[i] - M);
+          S = fmaf(l[i], sc, S);
+          A = fmaf(a[i], sc, A);
+        }
+      }
+    }
   }
-  const float lam = lamst->lambda_f;
-  const float y = o[0] - lam * o[1];
-  float ss = wave_sum(y * y);
-  if ((ch & 63) == 0) wsum[ch >> 6] = ss;
+  const float o = A / S;
+  if (mp == 1) o2[ch] = o;
   __syncthreads();
+  // Map 1's wavefronts stay to the last barrier but do no more work.
+  const float lam = lamst->lambda_f;
+  const float y = o - lam * o2[ch];
+  float ss = wave_sum(y * y);
+  if (mp == 0 && (ch & 63) == 0) wsum[ch >> 6] = ss;
+  __syncthreads();
+  if (mp == 1) return;
   ss = wsum[0] + wsum[1];
   const float rstd = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
   const float w = rms_w ? rms_w[(bh % H) * DV + ch] : 1.0f;
@@ -528,7 +574,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(BH)), dim3(DV), 0, s,
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(BH)), dim3(2 * DV), 0, s,
                      a.partial, a.cache_len, a.lam, a.rms_weight, static_cast<bf16_t*>(a.out),
                      a.H, a.L, a.n_split, static_cast<int64_t>(a.split_len), a.eps);
   return hipGetLastError();

@@ -14,7 +14,8 @@ BF16_TOL = 2e-2
 
 
 @pytest.mark.parametrize("b,hh,L,lens", [(1, 1, 1, None), (2, 2, 64, None), (3, 2, 300, [300, 1, 129]),
-                                       (2, 3, 1000, [513, 999]), (4, 1, 4100, [4100, 4096, 257, 2])])
+                                       (2, 3, 1000, [513, 999]), (4, 1, 4100, [4100, 4096, 257, 2]),
+                                       (2, 1, 40000, [40000, 33001])])
 def test_decode_small(b, hh, L, lens):
     w = synth.custom("decode", b, hh, L, 64, 8, "bf16", number=600 + L)
     x, h = draw(w)

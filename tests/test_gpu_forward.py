@@ -52,6 +52,18 @@ def test_lambda_bitwise(layer, d):
         ulp_diff(got["lambda_init"], orc.lambda_init(layer)) <= 1.0
 
 
+@pytest.mark.parametrize("d", [1, 65, 100, 1000])
+def test_lambda_bitwise_other_lengths(d):
+    """Vector lengths that leave a partial chunk of 64 terms (the sum stays in index order)."""
+    w = synth.custom("fwd", 1, 1, 1, d, 3, "fp32", number=260 + d)
+    x, h = draw(w)
+    st, ls = lam_pair(x, h, 3)
+    got = da.read_lambda_state(st)
+    for k in ("lambda_f32", "lambda_init_f32", "one_minus_init_f32"):
+        assert np.float32(got[k]).tobytes() == np.float32(ls[k]).tobytes(), k
+    assert lambda_f64_ok(got["lambda"], ls), (got["lambda"], ls["lambda"])
+
+
 def test_lambda_zero_vectors():
     z = torch.zeros(64, dtype=torch.float32, device=DEV)
     for layer in (1, 5, 12):
