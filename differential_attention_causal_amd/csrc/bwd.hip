@@ -11,6 +11,8 @@
 //   dV  = (A1 - lambda A2)^T G                            (bwd_dkdv_kernel)
 //   dP  = G V^T
 //   dS1 = A1 (dP - D1),  dS2 = -lambda A2 (dP - D2)
+//         (the kernels form A2 (D2 - dP) per score; lambda scales dK2 and dQ2 once, at
+//          their stores)
 //   dK_k = s dS_k^T Q_k                                   (bwd_dkdv_kernel)
 //   dQ_k = s dS_k K_k                                     (bwd_dq_kernel)
 //   dlambda = -sum over rows of D2; lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init gives
@@ -21,8 +23,9 @@
 // A_k is recomputed from the log-sum-exps the forward saved: A_k = exp(S_k - lse_k).
 //
 // Two matrix-core kernels, no atomics (deterministic). Both have the same shape:
-//  * A workgroup is 4 wavefronts, one per SIMD; each wavefront owns 32 rows (keys in
-//    bwd_dkdv_kernel, queries in bwd_dq_kernel). The operands that belong to the owned
+//  * Each wavefront owns 32 rows (keys in bwd_dkdv_kernel, queries in bwd_dq_kernel). A
+//    dK/dV workgroup is 4 wavefronts, one per SIMD; a dQ workgroup is 8, two per SIMD (the
+//    dQ kernel fits in half the register file, so each SIMD interleaves two waves). The operands that belong to the owned
 //    rows stay in the accumulation registers for the whole kernel (as the B operand of the
 //    score and dP products), next to the gradient accumulators.
 //  * The other side (query tiles for dK/dV, key tiles for dQ) streams through LDS in tiles
@@ -48,6 +51,11 @@ constexpr int DV = 128;
 constexpr int NW = 4;            // wavefronts per workgroup
 constexpr int NT = 64 * NW;
 constexpr int BW = 32 * NW;      // rows owned by a workgroup
+// The dQ kernel: 8 wavefronts (two per SIMD, so that one hides the other's latencies),
+// 32 query rows each.
+constexpr int NWQ = 8;
+constexpr int NTQ = 64 * NWQ;
+constexpr int BWQ = 32 * NWQ;
 constexpr int TB = 64;           // rows per streamed tile
 constexpr int NSLOT = 4;         // LDS ring depth
 constexpr int REG = TB * 64;     // one 32-channel region of a tile: [64 rows][64 B]
@@ -573,7 +581,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
   // later steps need.
   f32x16 S1[2], S2[2], dP[2];
   uint32_t pcw[2][8], g1w[2][8], g2w[2][8];
-  float p1[2][2], p2[2][2], y1[2][2], y2[2][2], u[2][2], tt[2][2], ww[2][2], dd2[2][2];
+  float p1[2][2], p2[2][2], y1[2][2], y2[2][2], u[2][2], ww[2][2], dd2[2][2];
   u32x4 vecr[2][2];   // per-row vectors of the pair's two rows
   u32x2 trl[16], trh[16];   // transposing reads of the C products of the half-step
   u32x4 rr[16];             // row reads of its A products
@@ -690,21 +698,16 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
         constexpr int pr = (k / 4 + 7) % 8, st = k % 4, q = pr & 1, e = 2 * pr;
         constexpr int P = (k < 4) ? PN : PA;
         if constexpr (st == 0) {
-          tt[q][0] = lam * p2[q][0];
-          tt[q][1] = lam * p2[q][1];
-          anchor(tt[q][0], tt[q][1]);
-        }
-        if constexpr (st == 1) {
           ww[q][0] = dd2[q][0] - dP[P][e];
           ww[q][1] = dd2[q][1] - dP[P][e + 1];
           anchor(ww[q][0], ww[q][1]);
         }
-        if constexpr (st == 2) {
-          g2w[P][pr] = pack_bf16x2(tt[q][0] * ww[q][0], tt[q][1] * ww[q][1]);
+        if constexpr (st == 1) {
+          g2w[P][pr] = pack_bf16x2(p2[q][0] * ww[q][0], p2[q][1] * ww[q][1]);
           anchor(g2w[P][pr]);
         }
-        if constexpr (st == 3) {
-          pcw[P][pr] = pack_bf16x2(p1[q][0] - tt[q][0], p1[q][1] - tt[q][1]);
+        if constexpr (st == 2) {
+          pcw[P][pr] = pack_bf16x2(fmaf(-lam, p2[q][0], p1[q][0]), fmaf(-lam, p2[q][1], p1[q][1]));
           anchor(pcw[P][pr]);
         }
       }
@@ -788,12 +791,10 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
     const int a0 = bl + la.tb[0], a1 = bl + la.tb[1];
     {
       constexpr int q = 1, e = 14;
-      tt[q][0] = lam * p2[q][0];
-      tt[q][1] = lam * p2[q][1];
       ww[q][0] = dd2[q][0] - dP[1][e];
       ww[q][1] = dd2[q][1] - dP[1][e + 1];
-      g2w[1][7] = pack_bf16x2(tt[q][0] * ww[q][0], tt[q][1] * ww[q][1]);
-      pcw[1][7] = pack_bf16x2(p1[q][0] - tt[q][0], p1[q][1] - tt[q][1]);
+      g2w[1][7] = pack_bf16x2(p2[q][0] * ww[q][0], p2[q][1] * ww[q][1]);
+      pcw[1][7] = pack_bf16x2(fmaf(-lam, p2[q][0], p1[q][0]), fmaf(-lam, p2[q][1], p1[q][1]));
     }
     static_for<Sc::LT, 16>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value, t = kvc_t(i), b = kvc_b(i), ks = kvc_ks(i);
@@ -815,6 +816,9 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
   // Stores: register j of block b holds channel 32 b + 8 (j / 4) + 4 h + j % 4 of the key.
   if (key < N) {
     const float s = 0.125f;  // 1 / sqrt(64)
+    // Map 2's score gradients were accumulated without their factor lambda (the same for
+    // every score): dS2 = lambda P2 (D2 - dP).
+    const float s2 = s * lamst->lambda_f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
@@ -832,8 +836,8 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
         const int col = 32 * b + 8 * jg + 4 * h;
         u32x2 pa = {pack_bf16x2(s * adk1[b][4 * jg], s * adk1[b][4 * jg + 1]),
                     pack_bf16x2(s * adk1[b][4 * jg + 2], s * adk1[b][4 * jg + 3])};
-        u32x2 pb = {pack_bf16x2(s * adk2[b][4 * jg], s * adk2[b][4 * jg + 1]),
-                    pack_bf16x2(s * adk2[b][4 * jg + 2], s * adk2[b][4 * jg + 3])};
+        u32x2 pb = {pack_bf16x2(s2 * adk2[b][4 * jg], s2 * adk2[b][4 * jg + 1]),
+                    pack_bf16x2(s2 * adk2[b][4 * jg + 2], s2 * adk2[b][4 * jg + 3])};
         *reinterpret_cast<u32x2*>(dk1 + (ho + key) * D + col) = pa;
         *reinterpret_cast<u32x2*>(dk2 + (ho + key) * D + col) = pb;
       }
@@ -854,23 +858,23 @@ struct QRsrc {
 
 // This wave's share of key tile `tile` (rows t0 ..): blocks w, w + 4 of K1 and K2, w + 4 i
 // of V (8 loads).
+// A tile is 32 blocks of 1 KiB (K1 8, K2 8, V 16); wave wv of the 8 moves K1 and K2 block
+// wv and V blocks wv and wv + 8: four loads per wave per tile.
 __device__ __forceinline__ void q_dma(const QRsrc& rs, uint32_t lds, int tile, int t0,
                                       int wv, int lane) {
   const uint32_t base = lds + (tile % NSLOT) * Q_SLOT;
   dma_rows<D>(rs.k1, base + Q_K1, t0, wv, lane);
-  dma_rows<D>(rs.k1, base + Q_K1, t0, wv + 4, lane);
   dma_rows<D>(rs.k2, base + Q_K2, t0, wv, lane);
-  dma_rows<D>(rs.k2, base + Q_K2, t0, wv + 4, lane);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dma_rows<DV>(rs.v, base + Q_V, t0, wv + 4 * i, lane);
+  dma_rows<DV>(rs.v, base + Q_V, t0, wv, lane);
+  dma_rows<DV>(rs.v, base + Q_V, t0, wv + 8, lane);
 }
 __device__ __forceinline__ void q_tile_barrier(bool next_in_flight) {
-  if (next_in_flight) vm_wait<8>();
+  if (next_in_flight) vm_wait<4>();
   else vm_wait<0>();
   barrier();
 }
 
-__global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
+__global__ void __launch_bounds__(NTQ, 1) bwd_dq_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2, const bf16_t* __restrict__ k1,
     const bf16_t* __restrict__ k2, const bf16_t* __restrict__ v, const bf16_t* __restrict__ gb,
     const f32x4* __restrict__ vec, const diffattn_lambda_state* __restrict__ lamst,
@@ -882,7 +886,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
   const int m = lane & 31, h = lane >> 5;
   const int bid = blockIdx.x;
   const int bh = bid % BH;
-  const int q0 = (nqb - 1 - bid / BH) * BW;   // late query blocks see the most keys: first
+  const int q0 = (nqb - 1 - bid / BH) * BWQ;   // late query blocks see the most keys: first
   const int q = q0 + 32 * wv + m;
   const bool qok = q < N;
   const int64_t ho = static_cast<int64_t>(bh) * N;
@@ -895,7 +899,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
   rs.v = rsrc_words(v + kvo * DV, N * DV * 2);
   // Key tiles 0 .. up to the block's last query (keys beyond N read as zero and are
   // masked: they follow every query).
-  const int kend = min(N, q0 + BW);
+  const int kend = min(N, q0 + BWQ);
   const int nT = (kend + TB - 1) / TB;
   const uint32_t ldsu = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)lds));
   const int lds0 = static_cast<int>(ldsu);
@@ -951,14 +955,13 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
 
   const LaneAddr la = lane_addr(lane);
   auto slot_of = [&](int j) { return lds0 + ((j >> 1) & (NSLOT - 1)) * Q_SLOT; };
-  const float lam = lamst->lambda_f;
   const float c = kLog2e / 8.0f;
   // Causal test: key > query for register e of sub-tile j  <=>  idx_of(e, 0) > qk - 32 j.
   const int qk = 32 * wv + m - 8 * h + q0;
 
   f32x16 S1[2], S2[2], dP[2];
   uint32_t g1w[2][8], g2w[2][8];
-  float p1[2][2], p2[2][2], y1[2][2], y2[2][2], u[2][2], tt[2][2], ww[2][2];
+  float p1[2][2], p2[2][2], y1[2][2], y2[2][2], u[2][2], ww[2][2];
   u32x2 trl[8], trh[8];
   u32x4 rr[16];
 
@@ -1050,17 +1053,12 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
         constexpr int pr = (k / 3 + 7) % 8, st = k % 3, qq = pr & 1, e = 2 * pr;
         constexpr int P = (k < 3) ? PN : PA;
         if constexpr (st == 0) {
-          tt[qq][0] = lam * p2[qq][0];
-          tt[qq][1] = lam * p2[qq][1];
-          anchor(tt[qq][0], tt[qq][1]);
-        }
-        if constexpr (st == 1) {
           ww[qq][0] = D2 - dP[P][e];
           ww[qq][1] = D2 - dP[P][e + 1];
           anchor(ww[qq][0], ww[qq][1]);
         }
-        if constexpr (st == 2) {
-          g2w[P][pr] = pack_bf16x2(tt[qq][0] * ww[qq][0], tt[qq][1] * ww[qq][1]);
+        if constexpr (st == 1) {
+          g2w[P][pr] = pack_bf16x2(p2[qq][0] * ww[qq][0], p2[qq][1] * ww[qq][1]);
           anchor(g2w[P][pr]);
         }
       }
@@ -1071,8 +1069,8 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
 
   // Prologue (as for dK/dV): tile 0 resident, A(0), P(-1) = 0, C(-1)'s first
   // transposing reads in flight.
-  if (nT > 2) vm_wait<16>();
-  else if (nT > 1) vm_wait<8>();
+  if (nT > 2) vm_wait<8>();
+  else if (nT > 1) vm_wait<4>();
   else vm_wait<0>();
   barrier();
   {
@@ -1107,7 +1105,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
     });
   }
 
-  // Trips as for dK/dV; the causal band is in the last two tiles.
+  // Trips as for dK/dV; the causal band (keys q0 .. q0 + 255) is in the last four tiles.
   auto trip = [&](auto masked, int T) __attribute__((always_inline)) {
     half(masked, Int<0>{}, 2 * T);
     if (T + 1 < nT) {
@@ -1116,7 +1114,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
     }
     half(masked, Int<1>{}, 2 * T + 1);
   };
-  const int nfree = nT > 2 ? nT - 2 : 0;
+  const int nfree = nT > 4 ? nT - 4 : 0;
   for (int T = 0; T < nfree; ++T) trip(Flag<false>{}, T);
   for (int T = nfree; T < nT; ++T) trip(Flag<true>{}, T);
   // The last half-step's score products (of a sub-tile that does not exist) are not
@@ -1130,11 +1128,9 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
     const int a0 = bl + la.tb[0], a1 = bl + la.tb[1];
     {
       constexpr int qq = 1, e = 14;
-      tt[qq][0] = lam * p2[qq][0];
-      tt[qq][1] = lam * p2[qq][1];
       ww[qq][0] = D2 - dP[1][e];
       ww[qq][1] = D2 - dP[1][e + 1];
-      g2w[1][7] = pack_bf16x2(tt[qq][0] * ww[qq][0], tt[qq][1] * ww[qq][1]);
+      g2w[1][7] = pack_bf16x2(p2[qq][0] * ww[qq][0], p2[qq][1] * ww[qq][1]);
     }
     static_for<Sc::LT, 8>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value, mp = qc_map(i), b = qc_b(i), ks = qc_ks(i);
@@ -1153,6 +1149,9 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
 
   if (qok) {
     const float s = 0.125f;  // 1 / sqrt(64)
+    // Map 2's score gradients were accumulated without their factor lambda (the same for
+    // every score): dS2 = lambda P2 (D2 - dP).
+    const float s2 = s * lamst->lambda_f;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -1160,8 +1159,8 @@ __global__ void __launch_bounds__(NT, 1) bwd_dq_kernel(
         const int col = 32 * b + 8 * jg + 4 * h;
         u32x2 pa = {pack_bf16x2(s * aq1[b][4 * jg], s * aq1[b][4 * jg + 1]),
                     pack_bf16x2(s * aq1[b][4 * jg + 2], s * aq1[b][4 * jg + 3])};
-        u32x2 pb = {pack_bf16x2(s * aq2[b][4 * jg], s * aq2[b][4 * jg + 1]),
-                    pack_bf16x2(s * aq2[b][4 * jg + 2], s * aq2[b][4 * jg + 3])};
+        u32x2 pb = {pack_bf16x2(s2 * aq2[b][4 * jg], s2 * aq2[b][4 * jg + 1]),
+                    pack_bf16x2(s2 * aq2[b][4 * jg + 2], s2 * aq2[b][4 * jg + 3])};
         *reinterpret_cast<u32x2*>(dq1 + (ho + q) * D + col) = pa;
         *reinterpret_cast<u32x2*>(dq2 + (ho + q) * D + col) = pb;
       }
@@ -1223,11 +1222,12 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
                        static_cast<bf16_t*>(a.dv), BHK, N, a.G);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(static_cast<unsigned>(BH * nb)), dim3(NT), Q_LDS, s,
+    const int nbq = static_cast<int>((a.N + BWQ - 1) / BWQ);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(static_cast<unsigned>(BH * nbq)), dim3(NTQ), Q_LDS, s,
                        static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
                        static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
                        static_cast<const bf16_t*>(a.v), gbuf, vec, a.lam,
-                       static_cast<bf16_t*>(a.dq1), static_cast<bf16_t*>(a.dq2), BH, N, nb, a.G);
+                       static_cast<bf16_t*>(a.dq1), static_cast<bf16_t*>(a.dq2), BH, N, nbq, a.G);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
