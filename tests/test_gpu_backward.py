@@ -89,7 +89,8 @@ def check_weight_grad(g, ref):
 
 
 @pytest.mark.parametrize("b,hh,n", [(1, 1, 1), (1, 1, 32), (1, 2, 33), (2, 1, 64), (1, 2, 129),
-                                    (1, 2, 200), (1, 1, 300), (1, 2, 1000)])
+                                    (1, 2, 200), (1, 1, 256), (1, 1, 257), (1, 1, 300),
+                                    (1, 1, 513), (1, 2, 1000)])
 def test_backward_small(b, hh, n):
     w = synth.custom("train", b, hh, n, 64, 6, "bf16", number=700 + n)
     x, h = draw(w)

@@ -109,7 +109,8 @@ def test_qkv_proj_grouped(B, N, H, hkv, dm):
         assert np.all(np.abs(np64(g) - r) <= bound), name
 
 
-@pytest.mark.parametrize("B,H,hkv,N", [(1, 4, 2, 200), (2, 4, 1, 129), (1, 6, 3, 64)])
+@pytest.mark.parametrize("B,H,hkv,N", [(1, 4, 2, 200), (2, 4, 1, 129), (1, 6, 3, 64),
+                                      (1, 4, 2, 600)])
 def test_backward_grouped(B, H, hkv, N):
     """dK and dV of a shared head collect the contributions of its query heads: against
     the oracle (normwise relative 5e-2 per tensor, as for MHA), and against the sum over
