@@ -22,12 +22,12 @@ namespace {
 thread_local int g_last_hip = 0;
 
 bool env_log() {
-  static int v = -1;
-  if (v < 0) {
+  // Read once; the initialisation of a local static is thread-safe.
+  static const bool on = [] {
     const char* e = getenv("DIFFATTN_LOG");
-    v = (e && e[0] == '1') ? 1 : 0;
-  }
-  return v == 1;
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
 }
 
 diffattn_status hip_status(hipError_t e, const char* what) {

@@ -1185,16 +1185,16 @@ size_t bwd_workspace_floats(int64_t B, int64_t H, int64_t N, int d) {
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   using namespace bwd;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dkdv_kernel),
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t ea = once_per_device(attr_done, [] {
+    hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dkdv_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, KV_LDS);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dq_kernel),
+    if (r == hipSuccess)
+      r = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dq_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, Q_LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return r;
+  });
+  if (ea != hipSuccess) return ea;
   const int64_t rows = a.B * a.H * a.N;
   const int64_t nchunk = (a.N + 63) / 64;
   const int64_t nparts = a.B * a.H * nchunk;

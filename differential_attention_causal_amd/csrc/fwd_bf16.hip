@@ -783,16 +783,16 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   using namespace fwdbf16;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<false>),
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t ea = once_per_device(attr_done, [] {
+    hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<true>),
+    if (r == hipSuccess)
+      r = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return r;
+  });
+  if (ea != hipSuccess) return ea;
   const int64_t BH = a.B * a.H;
   const int nqb = static_cast<int>((a.N + BR - 1) / BR);
   const int64_t nblk = BH * nqb;

@@ -273,13 +273,12 @@ __global__ void __launch_bounds__(NT, 1)
 template <bool QKV>
 hipError_t launch(const bf16_t* A, const bf16_t* B, bf16_t* C, const QkvOut& qo, int64_t M,
                   int Nc, int K, hipStream_t s) {
-  static bool attr_set = false;   // the attribute is per kernel, set once per process
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<QKV>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> attr_done{0};   // one word per instantiation
+  const hipError_t ea = once_per_device(attr_done, [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<QKV>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  });
+  if (ea != hipSuccess) return ea;
   const int64_t tiles = ((M + BM - 1) / BM) * ((Nc + BN - 1) / BN);
   hipLaunchKernelGGL(gemm_bf16_kernel<QKV>, dim3(static_cast<unsigned>(tiles)), dim3(NT),
                      LDS_BYTES, s, A, B, C, qo, M, Nc, K);

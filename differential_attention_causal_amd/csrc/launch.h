@@ -5,9 +5,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "diffattn.h"
 
 namespace diffattn {
+
+// Runs `set` (which sets kernel attributes, such as the dynamic LDS size) once for each
+// device the calling thread has current: the attributes belong to a device. The flag word
+// is atomic, so first calls from several threads at once are safe (each may set the same
+// attribute). Devices beyond the 64th are set on every call.
+template <typename F>
+inline hipError_t once_per_device(std::atomic<uint64_t>& done, F&& set) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = set();
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 // All tensors contiguous [B, H, N, feature]; shapes already validated.
 struct FwdArgs {

@@ -254,6 +254,41 @@ def test_determinism_bitwise():
     assert torch.equal(ya, yb)
 
 
+def test_concurrent_calls_from_threads():
+    """Four host threads call the forward and the decode step at once, each on a stream of
+    its own: every result equals the serial call's bitwise (the library keeps no state
+    between calls beyond the per-device kernel attributes it sets once)."""
+    import threading
+    w = synth.custom("fwd", 1, 4, 600, 64, 5, "bf16", number=530)
+    x, h = draw(w)
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    q1l, q2l = x["q1"][:, :, -1].contiguous(), x["q2"][:, :, -1].contiguous()
+    ref = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
+    refd = da.decode(q1l, q2l, x["k1"], x["k2"], x["v"], st)
+    torch.cuda.synchronize()
+    outs, errs = [None] * 4, []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
+                yd = da.decode(q1l, q2l, x["k1"], x["k2"], x["v"], st)
+            s.synchronize()
+            outs[i] = (y, yd)
+        except Exception as e:  # noqa: BLE001 - reported by the assertion below
+            errs.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errs, errs
+    for y, yd in outs:
+        assert torch.equal(y, ref) and torch.equal(yd, refd)
+
+
 def test_special_cases_lambda_zero_and_identical_maps():
     w = synth.custom("fwd", 1, 2, 260, 64, 1, "bf16", number=520)
     x, h = draw(w)
