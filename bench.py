@@ -7,6 +7,8 @@ FLOPs are counted as 12 d P per head (P = N(N+1)/2 causal pairs: two QK^T of
 width d and two PV of width 2d), the work the exact blockwise algorithm executes.
 
 Also reported in the same line:
+  prefill - the same forward on the prefill workload B4 H8 N2048 d64 (bf16, layer 4,
+            inputs scaled by 1/sqrt 2): kernel time, TFLOP/s and fraction of the peak.
   decode  - one split-KV decode step, 64 sequences x 16 heads against caches of
             8192 tokens: HBM GB/s = (cache + query + output bytes) / step time.
   train   - forward (with saves) + backward on B8 H12 N4096 when the backward
@@ -30,7 +32,7 @@ Also reported in the same line:
             ~12 s of CPU work).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--legs fwd,decode,train,proj,copy]
+                       [--legs fwd,prefill,decode,train,proj,refgemm,copy]
                        [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -89,11 +91,11 @@ def time_steps(step, steps: int, warmup: int, inner_events=None):
     return ms, wall, inner
 
 
-def leg_forward(steps, warmup):
+def leg_forward(steps, warmup, number=3):
     import torch
     from differential_attention_causal_amd import diffattn as da
     from differential_attention_causal_amd import synth
-    w = synth.WORKLOADS[3]
+    w = synth.WORKLOADS[number]
     x = synth.make_inputs(w, "cuda:0")
     out = torch.empty_like(x["v"])
     p = da.problem(w.batch, w.heads, w.seqlen, w.head_dim, da.BF16)
@@ -411,7 +413,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--legs", default="fwd,decode,train,proj,refgemm,copy")
+    ap.add_argument("--legs", default="fwd,prefill,decode,train,proj,refgemm,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -440,6 +442,10 @@ def main():
         "fwd_kernel_ms_min": fwd["fwd_kernel_ms_min"],
         "formula_tflops_8dP": fwd["formula_tflops_8dP"],
     }
+    if "prefill" in legs:
+        wp, pf = leg_forward(args.steps, args.warmup, number=2)
+        rec["prefill"] = {"workload": wp.name, "fwd_kernel_ms": pf["fwd_kernel_ms"],
+                          "tflops": pf["roofline"]["achieved"], "frac": pf["roofline"]["frac"]}
     if "decode" in legs:
         rec["decode"] = leg_decode(args.steps, args.warmup)
     if "train" in legs:
