@@ -63,6 +63,26 @@ def test_decode_workload_sampled():
     assert torch.isfinite(y.float()).all().item()
 
 
+def test_decode_maximum_cache_length():
+    """Cache capacity 2^22 (the largest supported; 16384 splits for one sequence and head,
+    so the merge reads its partials in many batches), full and ragged lengths."""
+    n = 1 << 22
+    w = synth.custom("decode", 2, 1, n, 64, 8, "bf16", number=660)
+    x = synth.make_inputs(w, DEV)
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    lens = [n, n - 1000]
+    cl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    y = da.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, cache_len=cl)
+    torch.cuda.synchronize()
+    lv = {k: np64(x[k]) for k in ("lq1", "lk1", "lq2", "lk2")}
+    ls = orc.lambda_scalar(lv["lq1"], lv["lk1"], lv["lq2"], lv["lk2"], w.layer)
+    for b in range(2):
+        sl = {k: np64(x[k][b:b + 1]) for k in ("q1", "q2", "k1", "k2", "v")}
+        ref = orc.decode(sl["q1"], sl["q2"], sl["k1"], sl["k2"], sl["v"], [lens[b]],
+                         ls["lambda"], ls["lambda_init"])
+        assert np.max(np.abs(np64(y[b:b + 1]) - ref)) <= BF16_TOL, b
+
+
 def test_decode_cache_beyond_len_is_ignored_bitwise():
     w = synth.custom("decode", 2, 2, 900, 64, 3, "bf16", number=640)
     x, h = draw(w)

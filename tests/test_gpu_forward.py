@@ -225,6 +225,30 @@ def test_bf16_long_context_sampled():
     assert torch.isfinite(y.float()).all().item()
 
 
+def test_bf16_maximum_sequence_length_sampled():
+    """The longest supported sequence, N = 2^22 (B1 H1, layer 3): V's byte offsets reach
+    2^30 and the block count 16384; sampled rows, the last one included, against the
+    oracle."""
+    n = 1 << 22
+    w = synth.custom("fwd", 1, 1, n, 64, 3, "bf16", number=540)
+    x = synth.make_inputs(w, DEV)
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
+    torch.cuda.synchronize()
+    lv = {k: np64(x[k]) for k in ("lq1", "lk1", "lq2", "lk2")}
+    ls = orc.lambda_scalar(lv["lq1"], lv["lk1"], lv["lq2"], lv["lk2"], w.layer)
+    rows = [0, 255, 256, n // 2 + 77, n - 257, n - 1]
+    hi = max(rows) + 1
+    sl = {k: np64(x[k][0, 0, :hi]) for k in ("k1", "k2", "v")}
+    q = {k: np.zeros((hi, 64)) for k in ("q1", "q2")}
+    for k in ("q1", "q2"):
+        q[k][rows] = np64(x[k][0, 0, rows])
+    r = orc.forward_rows(q["q1"], q["q2"], sl["k1"], sl["k2"], sl["v"], rows, ls["lambda"],
+                         ls["lambda_init"])
+    assert np.max(np.abs(np64(y[0, 0, rows]) - r)) <= BF16_TOL
+    assert torch.isfinite(y.float()).all().item()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_mask_bitwise(dtype):
     """Keys after row i0 changed: rows 0..i0 are bit-identical."""
