@@ -5,8 +5,9 @@
 // maps of the DiffAttn equation (pt.news.hada.io "Como a atencao diferencial funciona").
 // Generating a token re-reads the whole K1/K2/V cache from HBM (priorstack.com, "The
 // Memory Wall: Why the KV Cache Constrains LLM Serving"), so the kernel is a streaming
-// read: every cache byte is loaded exactly once, with 16-byte buffer loads, and no LDS
-// staging.
+// read: every cache byte is loaded exactly once, with 16-byte buffer loads marked
+// non-temporal (policy bit nt: the data is not kept in the caches, which no later load
+// would hit), and no LDS staging.
 //
 // Pass 1 (decode_split_kernel), grid = splits x (B*H): a workgroup of 4 wavefronts takes
 // one split of the cache; each wavefront walks 64-key rounds of its share:
@@ -93,13 +94,13 @@ __global__ void __launch_bounds__(NT, 2) decode_split_kernel(
     u32x4 kx[SG], ky[SG];
 #pragma unroll
     for (int g = 0; g < SG; ++g) {
-      kx[g] = __builtin_amdgcn_raw_buffer_load_b128(rk1, ko + g * 8 * D * 2, kbs * D * 2, 0);
-      ky[g] = __builtin_amdgcn_raw_buffer_load_b128(rk2, ko + g * 8 * D * 2, kbs * D * 2, 0);
+      kx[g] = __builtin_amdgcn_raw_buffer_load_b128(rk1, ko + g * 8 * D * 2, kbs * D * 2, 2);
+      ky[g] = __builtin_amdgcn_raw_buffer_load_b128(rk2, ko + g * 8 * D * 2, kbs * D * 2, 2);
     }
     u32x4 vv[VI];
 #pragma unroll
     for (int i = 0; i < VI; ++i)
-      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * 4 * DV * 2, kbs * DV * 2, 0);
+      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * 4 * DV * 2, kbs * DV * 2, 2);
     float s1[SG], s2[SG];
 #pragma unroll
     for (int g = 0; g < SG; ++g) {
@@ -321,12 +322,12 @@ __global__ void __launch_bounds__(NT, 2) decode_group_kernel(
     u32x4 kx[SGG], ky[SGG], vv[VIG];
 #pragma unroll
     for (int sg = 0; sg < SGG; ++sg) {
-      kx[sg] = __builtin_amdgcn_raw_buffer_load_b128(rk1, ko + sg * 8 * D * 2, kbs * D * 2, 0);
-      ky[sg] = __builtin_amdgcn_raw_buffer_load_b128(rk2, ko + sg * 8 * D * 2, kbs * D * 2, 0);
+      kx[sg] = __builtin_amdgcn_raw_buffer_load_b128(rk1, ko + sg * 8 * D * 2, kbs * D * 2, 2);
+      ky[sg] = __builtin_amdgcn_raw_buffer_load_b128(rk2, ko + sg * 8 * D * 2, kbs * D * 2, 2);
     }
 #pragma unroll
     for (int i = 0; i < VIG; ++i)
-      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * 4 * DV * 2, kbs * DV * 2, 0);
+      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * 4 * DV * 2, kbs * DV * 2, 2);
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
       float s1[SGG], s2[SGG];
