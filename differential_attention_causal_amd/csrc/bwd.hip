@@ -305,9 +305,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(
     if (n >= N) break;
     const int64_t r = bh * N + n;
     const int64_t yr = dout_bnh ? (bb * N + n) * H + hh : r;   // dout row in its layout
-    const f32x4 a = *reinterpret_cast<const f32x4*>(o1 + r * DV + 4 * t);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(o2 + r * DV + 4 * t);
-    const u32x2 dy = *reinterpret_cast<const u32x2*>(dout + yr * DV + 4 * t);
+    // O1, O2 and dY are read once: non-temporal loads keep them out of the caches.
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o1 + r * DV + 4 * t));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o2 + r * DV + 4 * t));
+    const u32x2 dy = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(dout + yr * DV + 4 * t));
     f32x4 w = {1.f, 1.f, 1.f, 1.f};
     if (rms_w) w = *reinterpret_cast<const f32x4*>(rms_w + hh * DV + 4 * t);
     const float dyv[4] = {__uint_as_float(dy[0] << 16), __uint_as_float(dy[0] & 0xffff0000u),
