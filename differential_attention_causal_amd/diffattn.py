@@ -42,7 +42,7 @@ class Saved(ctypes.Structure):
 
 
 LAMBDA_STATE_BYTES = 48  # 4 doubles + 4 floats
-_STATE_FMT = "<4d4f"
+STATE_FMT = "<4d4f"   # diffattn_lambda_state: 4 doubles, 4 floats
 
 
 class DiffAttnError(RuntimeError):
@@ -192,17 +192,9 @@ def lambda_layers(lq1s, lk1s, lq2s, lk2s, first_layer: int,
     return st
 
 
-def lambda_state_tensor(lam: float, lam_init: float, device, exp_a=1.0, exp_b=1.0) -> torch.Tensor:
-    """A hand-made device lambda state (for example lambda = 0)."""
-    import numpy as np
-    raw = struct.pack(_STATE_FMT, lam, lam_init, exp_a, exp_b, float(np.float32(lam)),
-                      float(np.float32(lam_init)), float(np.float32(1.0 - lam_init)), 0.0)
-    return torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(device)
-
-
 def read_lambda_state(st: torch.Tensor) -> Dict[str, float]:
     raw = bytes(st.cpu().numpy().tobytes())
-    v = struct.unpack(_STATE_FMT, raw)
+    v = struct.unpack(STATE_FMT, raw)
     return {"lambda": v[0], "lambda_init": v[1], "exp_a": v[2], "exp_b": v[3],
             "lambda_f32": v[4], "lambda_init_f32": v[5], "one_minus_init_f32": v[6]}
 

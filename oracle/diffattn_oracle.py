@@ -47,8 +47,11 @@ rows of each map summing to one, row 0 attending only to V row 0, mask
 perturbation invariance, RMSNorm against torch's rms_norm, a scalar brute-force
 twin on tiny shapes, decode equal to the last prefill row, grouped-query
 attention equal to the same computation with K/V repeated per head, append-then-decode
-equal to the prefill row of the extended sequence, and central finite
-differences of the forward for every gradient.
+equal to the prefill row of the extended sequence, central finite
+differences of the forward for every gradient, and, for the epilogue's own
+backward, central differences in O1, in lambda with O1 and O2 held fixed, in the
+scale of each O1 row and in the norm weight, plus equality of its dlambda with
+the full backward's (computed there from the maps instead).
 """
 from __future__ import annotations
 
@@ -439,6 +442,35 @@ def head_backward(q1, q2, k1, k2, v, dy, lam: float, lam_init: float,
         "dv": dv, "d_attn": G, "dlam": float(-np.sum(a2 * gv)),
         "dw": (1.0 - lam_init) * np.sum(dy * o * r, axis=0),
     }
+
+
+def epilogue_backward(o1, o2, dy, lam: float, lam_init: float, eps: float = DEFAULT_EPS,
+                      weight=None):
+    """Backward of the epilogue alone, rows of one head: the gradient at the RMSNorm input
+    and the per-row terms the lambda and attention gradients use, from the two maps'
+    outputs O1 = A1 V and O2 = A2 V and the upstream gradient dY.
+
+    Forward of the epilogue ([HADA] DiffAttn equation, [INTOAI] "Differential Attention
+    With Multiple Heads"): O = O1 - lam O2, r = (mean(O^2) + eps)^(-1/2),
+    Y = (1 - lam_init) w O r.  Chain rule, with g = (1 - lam_init) w dY and n the width
+    of O:
+      G  = dL/dO = r g - O r^3 rowsum(g O) / n
+      D1 = rowsum(G O1),  D2 = rowsum(G O2)
+      dlam = -sum_i D2_i              (lam enters O only as -lam O2)
+      dw = (1 - lam_init) sum over rows of dY O r
+    Returns a dict with G, D1, D2 (per row), dlam and dw.
+    """
+    o1, o2, dy = _f64(o1), _f64(o2), _f64(dy)
+    n = o1.shape[-1]
+    o = o1 - lam * o2
+    r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    w = np.ones(n) if weight is None else _f64(weight)
+    g = (1.0 - lam_init) * w * dy
+    G = r * g - (r ** 3 / n) * o * np.sum(g * o, axis=-1, keepdims=True)
+    d1 = np.sum(G * o1, axis=-1)
+    d2 = np.sum(G * o2, axis=-1)
+    return {"G": G, "D1": d1, "D2": d2, "dlam": float(-np.sum(d2)),
+            "dw": (1.0 - lam_init) * np.sum(r * o * dy, axis=0)}
 
 
 def backward(q1, q2, k1, k2, v, dy, lq1, lk1, lq2, lk2, layer: int,

@@ -1,4 +1,6 @@
-"""Shared helpers of the GPU parity tests (no method arithmetic here)."""
+"""Shared helpers of the GPU parity tests."""
+import struct
+
 import numpy as np
 import torch
 
@@ -33,3 +35,12 @@ def normwise_rel(a, ref, axes):
     num = np.max(np.abs(a - ref), axis=axes)
     den = np.max(np.abs(ref), axis=axes)
     return num / np.maximum(den, 1e-300)
+
+
+def lambda_state_tensor(lam: float, lam_init: float, device=DEV, exp_a=1.0, exp_b=1.0):
+    """A hand-made device lambda state (for example lambda = 0 or 1), laid out as the
+    library's diffattn_lambda_state: the float64 fields, then the float32 roundings of
+    lambda, lambda_init and 1 - lambda_init."""
+    raw = struct.pack(da.STATE_FMT, lam, lam_init, exp_a, exp_b, float(np.float32(lam)),
+                      float(np.float32(lam_init)), float(np.float32(1.0 - lam_init)), 0.0)
+    return torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(device)

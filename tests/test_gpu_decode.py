@@ -43,24 +43,25 @@ def test_decode_matches_last_prefill_row():
     assert np.max(np.abs(np64(yd[1, 1]) - ref[0])) <= BF16_TOL
 
 
-def test_decode_workload_sampled():
-    """64 sequences x 16 heads, cache length 8192, layer 8: 48 sampled (b, h) pairs."""
+def test_decode_workload():
+    """64 sequences x 16 heads, cache length 8192, layer 8: every (b, h) output against
+    the oracle (the cache reaches the host one sequence at a time)."""
     w = synth.WORKLOADS[4]
     x = synth.make_inputs(w, DEV)
     st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
     y = da.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
     torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all().item()
     lv = {k: np64(x[k]) for k in ("lq1", "lk1", "lq2", "lk2")}
     ls = orc.lambda_scalar(lv["lq1"], lv["lk1"], lv["lq2"], lv["lk2"], w.layer)
-    rng = np.random.default_rng(9)
-    pairs = {(0, 0), (63, 15)} | {(int(b), int(hh)) for b, hh in
-                                  zip(rng.integers(0, 64, 46), rng.integers(0, 16, 46))}
-    for b, hh in sorted(pairs):
-        sl = {k: np64(x[k][b:b + 1, hh:hh + 1]) for k in ("q1", "q2", "k1", "k2", "v")}
+    yh = np64(y)
+    worst = 0.0
+    for b in range(w.batch):
+        sl = {k: np64(x[k][b:b + 1]) for k in ("q1", "q2", "k1", "k2", "v")}
         ref = orc.decode(sl["q1"], sl["q2"], sl["k1"], sl["k2"], sl["v"], None, ls["lambda"],
                          ls["lambda_init"])
-        assert np.max(np.abs(np64(y[b, hh]) - ref[0, 0])) <= BF16_TOL, (b, hh)
-    assert torch.isfinite(y.float()).all().item()
+        worst = max(worst, float(np.max(np.abs(yh[b] - ref[0]))))
+    assert worst <= BF16_TOL, worst
 
 
 def test_decode_maximum_cache_length():

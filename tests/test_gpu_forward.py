@@ -14,7 +14,7 @@ import torch
 from differential_attention_causal_amd import diffattn as da
 from differential_attention_causal_amd import synth
 from oracle import diffattn_oracle as orc
-from tests.helpers import DEV, draw, lam_pair, normwise_rel, np64
+from tests.helpers import DEV, draw, lam_pair, lambda_state_tensor, normwise_rel, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -186,43 +186,35 @@ def test_bf16_rms_weight():
 
 
 def test_bf16_prefill_workload():
-    """B4 H8 N2048 d64, layer 4: four heads in full, every head on sampled rows."""
+    """B4 H8 N2048 d64, layer 4: the whole output tensor, all 32 heads in full."""
     w = synth.WORKLOADS[2]
     x, h, st, ls, y = _run_fwd(w)
-    yh = np64(y)
-    heads = [(0, 0), (1, 3), (2, 5), (3, 7)]
     ref = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
-                      ls["lambda_init"], heads=heads)
-    for b, hh in heads:
-        assert np.max(np.abs(yh[b, hh] - ref[b, hh])) <= BF16_TOL
-    rows = [0, 1, 127, 128, 129, 1023, 2047]
-    for b in range(w.batch):
-        for hh in range(w.heads):
-            r = orc.forward_rows(h["q1"][b, hh], h["q2"][b, hh], h["k1"][b, hh], h["k2"][b, hh],
-                                 h["v"][b, hh], rows, ls["lambda"], ls["lambda_init"])
-            assert np.max(np.abs(yh[b, hh, rows] - r)) <= BF16_TOL
+                      ls["lambda_init"])
+    err = np.max(np.abs(np64(y) - ref), axis=(2, 3))
+    assert np.all(err <= BF16_TOL), err
 
 
-def test_bf16_long_context_sampled():
-    """B1 H16 N32768 d64, layer 12: sampled rows of every head (the launch that is timed)."""
+def test_bf16_long_context_workload():
+    """B1 H16 N32768 d64, layer 12 (the launch that is timed): every head in full
+    against the blocked oracle, the heads computed concurrently on the host."""
+    from tests.test_gpu_backward import _per_head_parallel
     w = synth.WORKLOADS[3]
     x = synth.make_inputs(w, DEV)
     st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
     y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
     torch.cuda.synchronize()
-    lv = {k: np64(x[k]) for k in ("lq1", "lk1", "lq2", "lk2")}
-    ls = orc.lambda_scalar(lv["lq1"], lv["lk1"], lv["lq2"], lv["lk2"], w.layer)
-    rng = np.random.default_rng(5)
-    base = [0, 1, 31, 32, 127, 128, 4095, 16384, 32766, 32767]
-    for hh in range(w.heads):
-        rows = sorted(set(base + rng.integers(0, w.seqlen, 6).tolist()))
-        sl = {k: np64(x[k][0, hh]) for k in ("q1", "q2", "k1", "k2", "v")}
-        r = orc.forward_rows(sl["q1"], sl["q2"], sl["k1"], sl["k2"], sl["v"], rows,
-                             ls["lambda"], ls["lambda_init"])
-        got = np64(y[0, hh, rows])
-        assert np.max(np.abs(got - r)) <= BF16_TOL, hh
-    # every row is finite
     assert torch.isfinite(y.float()).all().item()
+    h = {k: np64(x[k]) for k in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")}
+    ls = orc.lambda_scalar(h["lq1"], h["lk1"], h["lq2"], h["lk2"], w.layer)
+    yh = np64(y)
+
+    def head(hh):
+        ref = orc.head_forward(h["q1"][0, hh], h["q2"][0, hh], h["k1"][0, hh], h["k2"][0, hh],
+                               h["v"][0, hh], ls["lambda"], ls["lambda_init"], block=512)
+        return float(np.max(np.abs(yh[0, hh] - ref)))
+    err = _per_head_parallel(head, list(range(w.heads)))
+    assert max(err) <= BF16_TOL, err
 
 
 def test_bf16_maximum_sequence_length_sampled():
@@ -317,12 +309,12 @@ def test_special_cases_lambda_zero_and_identical_maps():
     w = synth.custom("fwd", 1, 2, 260, 64, 1, "bf16", number=520)
     x, h = draw(w)
     # lambda = 0: plain causal softmax attention, then norm and scale
-    st0 = da.lambda_state_tensor(0.0, 0.3, DEV)
+    st0 = lambda_state_tensor(0.0, 0.3, DEV)
     y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st0)
     ref = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], 0.0, 0.3)
     assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
     # identical maps with lambda = 1: exactly zero
-    st1 = da.lambda_state_tensor(1.0, 0.2, DEV)
+    st1 = lambda_state_tensor(1.0, 0.2, DEV)
     y1 = da.forward(x["q1"], x["q1"], x["k1"], x["k1"], x["v"], st1)
     torch.cuda.synchronize()
     assert torch.count_nonzero(y1).item() == 0
@@ -349,7 +341,7 @@ def test_training_saves():
 def test_empty_sequence():
     q = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
     v = torch.empty(1, 2, 0, 128, dtype=torch.bfloat16, device=DEV)
-    st = da.lambda_state_tensor(0.5, 0.2, DEV)
+    st = lambda_state_tensor(0.5, 0.2, DEV)
     y = da.forward(q, q.clone(), q.clone(), q.clone(), v, st)
     assert y.shape == (1, 2, 0, 128)
 
@@ -357,7 +349,7 @@ def test_empty_sequence():
 def test_unsupported_head_dim_raises():
     q = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16, device=DEV)
     v = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device=DEV)
-    st = da.lambda_state_tensor(0.5, 0.2, DEV)
+    st = lambda_state_tensor(0.5, 0.2, DEV)
     with pytest.raises(da.DiffAttnError):
         da.forward(q, q.clone(), q.clone(), q.clone(), v, st)
 
@@ -385,6 +377,47 @@ def test_bf16_fixup_pass_for_large_score_jump():
     ref = orc.forward(hh["q1"], hh["q2"], hh["k1"], hh["k2"], hh["v"], ls["lambda"],
                       ls["lambda_init"])
     assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
+
+
+def test_bf16_fixup_pass_training_saves_and_backward():
+    """The score jump of the test above in training mode: the fixup pass rewrites the
+    saves (lse1, lse2, O1, O2, rstd) of the rows it flags, and the backward reads them.
+    The flag bits are set, every save matches the oracle, and so does every gradient,
+    dlambda and the lambda-vector gradients included."""
+    from tests.test_gpu_backward import TOL, compare
+    w = synth.custom("train", 1, 2, 600, 64, 5, "bf16", number=471)
+    x, h = draw(w)
+    x = {k: t.clone() for k, t in x.items()}
+    x["q1"][0, 0, 400] = 2.0
+    x["k1"][0, 0, 350] = 2.0
+    x["q2"][0, 1, 400] = 2.0
+    x["k2"][0, 1, 350] = 2.0
+    h = {k: np64(t) for k, t in x.items()}
+    st, ls = lam_pair(x, h, w.layer)
+    p = da.problem(1, 2, 600, 64, da.BF16)
+    ws = torch.zeros(da.workspace_bytes(da.OP_FWD, p), dtype=torch.uint8, device=DEV)
+    sv = da.alloc_saved(1, 2, 600, 64, DEV)
+    y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, saved=sv, workspace=ws)
+    g = da.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lq1"], x["lk1"], x["lq2"],
+                    x["lk2"], st, sv, x["dout"])
+    torch.cuda.synchronize()
+    flags = ws.view(torch.int32).cpu().numpy().reshape(2, 3, 8)
+    assert flags[0, 1, 0] & (1 << 18) and flags[1, 1, 0] & (1 << 18)
+    ref, rs = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
+                          ls["lambda_init"], want_saved=True)
+    assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
+    for k, tol in (("lse1", 2e-3), ("lse2", 2e-3), ("o1", 2e-2), ("o2", 2e-2)):
+        assert np.max(np.abs(np64(sv[k]) - rs[k])) <= tol, k
+    assert np.max(np.abs(np64(sv["rstd"]) / rs["rstd"] - 1.0)) <= 2e-2
+    # row 400 of map 1 (head 0) and of map 2 (head 1) puts all its weight on key 350
+    assert abs(np64(sv["lse1"])[0, 0, 400] - rs["lse1"][0, 0, 400]) <= 2e-3
+    gr = orc.backward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], h["dout"], h["lq1"],
+                      h["lk1"], h["lq2"], h["lk2"], w.layer)
+    compare(g, gr, [(0, 0), (0, 1)], h, w.layer)
+    for k in ("dq1", "dq2"):        # the flagged rows themselves
+        for hh in (0, 1):
+            a, r = np64(g[k][0, hh, 400]), gr[k][0, hh, 400]
+            assert np.max(np.abs(a - r)) <= TOL * np.max(np.abs(gr[k][0, hh])), (k, hh)
 
 
 @pytest.mark.parametrize("dtype,d,B,H,N", [("bf16", 64, 2, 3, 300), ("bf16", 64, 1, 2, 1),

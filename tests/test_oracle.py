@@ -392,6 +392,67 @@ def test_backward_finite_differences_one_head_n32():
     _fd_check(n=32, d=64, B=1, H=1, layer=6, n_samples=96, seed=22, weight_on=False)
 
 
+def _epilogue_fd_failures(m, r):
+    """Central differences of the epilogue's loss sum((1 - lam_init) RMSNorm(O1 - lam O2)
+    * dY), with the norm taken from torch (independent of the oracle), against
+    m.epilogue_backward: G = dL/dO1, dlam with O1 and O2 held fixed, D1_i as the
+    derivative in the scale of row i of O1, and the weight gradient. Also its dlam
+    against the full backward's (formed there from the maps as -sum A2 (G V^T)).
+    Returns the names of the checks that fail."""
+    fails = []
+    n, d2 = 6, 8
+    o1, o2, dy = rand(r, n, d2), rand(r, n, d2), rand(r, n, d2)
+    o2[2] *= 1e-3              # a row whose norm is closer to eps
+    w = 1.0 + 0.3 * rand(r, d2)
+    lam, li, eps = 0.45, 0.3, 1e-5
+    e = m.epilogue_backward(o1, o2, dy, lam, li, eps, w)
+
+    def loss(a1, a2, lm, wt):
+        t = torch.from_numpy(np.ascontiguousarray(a1 - lm * a2))
+        y = torch.nn.functional.rms_norm(t, (d2,), weight=torch.from_numpy(wt), eps=eps)
+        return float(np.sum((1.0 - li) * y.numpy() * dy))
+    h = 1e-6
+    fd = np.empty((n, d2))
+    for i in range(n):
+        for c in range(d2):
+            p_, q_ = o1.copy(), o1.copy()
+            p_[i, c] += h; q_[i, c] -= h
+            fd[i, c] = (loss(p_, o2, lam, w) - loss(q_, o2, lam, w)) / (2 * h)
+    if np.max(np.abs(e["G"] - fd)) > 1e-6 * np.max(np.abs(fd)):
+        fails.append("epilogue G")
+    fdl = (loss(o1, o2, lam + h, w) - loss(o1, o2, lam - h, w)) / (2 * h)
+    if abs(e["dlam"] - fdl) > 1e-6 * max(abs(fdl), 1e-9):
+        fails.append("epilogue dlam")
+    fd1 = np.empty(n)
+    for i in range(n):
+        p_, q_ = o1.copy(), o1.copy()
+        p_[i] *= 1 + h; q_[i] *= 1 - h
+        fd1[i] = (loss(p_, o2, lam, w) - loss(q_, o2, lam, w)) / (2 * h)
+    if np.max(np.abs(e["D1"] - fd1)) > 1e-6 * np.max(np.abs(fd1)):
+        fails.append("epilogue D1")
+    fdw = np.empty(d2)
+    for c in range(d2):
+        p_, q_ = w.copy(), w.copy()
+        p_[c] += h; q_[c] -= h
+        fdw[c] = (loss(o1, o2, lam, p_) - loss(o1, o2, lam, q_)) / (2 * h)
+    if np.max(np.abs(e["dw"] - fdw)) > 1e-6 * np.max(np.abs(fdw)):
+        fails.append("epilogue dw")
+    # the same dlam as the full backward, which forms it from the maps
+    nn_, d = 9, 4
+    q1, q2, k1, k2 = (rand(r, nn_, d) for _ in range(4))
+    v, dyy = rand(r, nn_, 2 * d), rand(r, nn_, 2 * d)
+    _, sv = m.head_forward(q1, q2, k1, k2, v, lam, li, want_saved=True)
+    full = m.head_backward(q1, q2, k1, k2, v, dyy, lam, li)
+    ep = m.epilogue_backward(sv["o1"], sv["o2"], dyy, lam, li)
+    if abs(ep["dlam"] - full["dlam"]) > 1e-10 * max(abs(full["dlam"]), 1e-9):
+        fails.append("epilogue dlam vs full backward")
+    return fails
+
+
+def test_epilogue_backward_pins():
+    assert _epilogue_fd_failures(orc, rng(31)) == []
+
+
 # ---------------------------------------------------------------- planted mistakes
 def test_pins_catch_planted_mistakes(monkeypatch):
     """Copies of the oracle with one planted mistake each fail a pin above."""
@@ -607,6 +668,7 @@ def _pin_failures(m):
         fdw[j] = (lp - lm) / (2 * h)
     if np.max(np.abs(gw.reshape(-1) - fdw)) > 1e-5 * max(np.max(np.abs(fdw)), 1e-9):
         fails.append("fd rms weight")
+    fails += _epilogue_fd_failures(m, r)
     # projections. One-hot tokens: token t of the flattened batch is unit vector
     # e_(t mod d_model), so each output entry is one weight entry; the weight is coded
     # w[row, col] = row + 1000 col, which names the weight row that fed each output.
@@ -728,6 +790,12 @@ PLANTS = [
     ("grouped dK keeps one head", "                out[k][b, kh] = out[k][b, kh] + r[k]",
      "                out[k][b, kh] = r[k]"),
     ("dlam sign", '"dlam": float(-np.sum(a2 * gv))', '"dlam": float(np.sum(a2 * gv))'),
+    ("epilogue dlam sign", '"dlam": float(-np.sum(d2))', '"dlam": float(np.sum(d2))'),
+    ("epilogue D2 from O1", "d2 = np.sum(G * o2, axis=-1)", "d2 = np.sum(G * o1, axis=-1)"),
+    ("epilogue O with +lam", "    o = o1 - lam * o2\n", "    o = o1 + lam * o2\n"),
+    ("epilogue norm term halved", "G = r * g - (r ** 3 / n) * o", "G = r * g - (r ** 3 / (2 * n)) * o"),
+    ("epilogue weight gradient without the scale", '"dw": (1.0 - lam_init) * np.sum(r * o * dy',
+     '"dw": np.sum(r * o * dy'),
 ]
 
 
