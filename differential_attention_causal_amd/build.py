@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 
 SOURCES = ["api.cpp", "lambda.hip", "fwd_fp32.hip", "fwd_bf16.hip", "decode.hip", "bwd.hip",
-           "append.hip", "gemm.hip"]
+           "append.hip", "gemm.hip", "scratch.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -112,6 +112,8 @@ const char* diffattn_status_string(diffattn_status s) {
     case DIFFATTN_E_UNSUPPORTED: return "DIFFATTN_E_UNSUPPORTED: unsupported configuration";
     case DIFFATTN_E_WORKSPACE: return "DIFFATTN_E_WORKSPACE: workspace missing or too small";
     case DIFFATTN_E_HIP: return "DIFFATTN_E_HIP: HIP runtime error";
+    case DIFFATTN_E_SCRATCH:
+      return "DIFFATTN_E_SCRATCH: problem needs more than the static decode scratch";
   }
   return "DIFFATTN_E_?: unknown status";
 }
@@ -244,17 +246,38 @@ diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const vo
   return hip_status(diffattn::launch_fwd_bf16(a, s), "fwd_bf16");
 }
 
-diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const void* q2,
-                                const void* k1c, const void* k2c, const void* vc,
-                                const int32_t* cache_len, const diffattn_lambda_state* lam,
-                                const float* rms_weight, void* out, void* workspace,
-                                size_t workspace_bytes, void* stream) {
-  bool empty = false;
-  diffattn_status st = check_problem(p, &empty);
+}  // extern "C"
+
+namespace {
+
+// The decode inputs' byte spans (for the overlap checks); returns the output's bytes.
+size_t decode_spans(const diffattn_problem* p, const void* q1, const void* q2, const void* k1c,
+                    const void* k2c, const void* vc, const int32_t* cache_len,
+                    const diffattn_lambda_state* lam, const float* rms_weight, Span* in) {
+  const int d = p->head_dim;
+  const size_t bh = static_cast<size_t>(p->batch) * p->heads;
+  const size_t bhk = static_cast<size_t>(p->batch) * kv_heads_of(p);
+  const size_t qb = bh * d * 2, kb = bhk * p->seqlen * d * 2, vb = bhk * p->seqlen * 2 * d * 2;
+  in[0] = {q1, qb}; in[1] = {q2, qb}; in[2] = {k1c, kb}; in[3] = {k2c, kb}; in[4] = {vc, vb};
+  in[5] = {cache_len, static_cast<size_t>(p->batch) * 4};
+  in[6] = {lam, sizeof(diffattn_lambda_state)};
+  in[7] = {rms_weight, static_cast<size_t>(p->heads) * 2 * d * sizeof(float)};
+  return bh * 2 * d * 2;
+}
+
+// Validation shared by the two decode entry points (all but the overlap checks, which
+// follow each one's scratch check); fills *a (except a->partial) and *need (the
+// partials' bytes). *empty: nothing to compute.
+diffattn_status decode_prepare(const diffattn_problem* p, const void* q1, const void* q2,
+                               const void* k1c, const void* k2c, const void* vc,
+                               const int32_t* cache_len, const diffattn_lambda_state* lam,
+                               const float* rms_weight, void* out, diffattn::DecodeArgs* a,
+                               size_t* need, bool* empty) {
+  diffattn_status st = check_problem(p, empty);
   if (st != DIFFATTN_OK) return st;
   if (p->dtype != DIFFATTN_BF16 || p->head_dim != 64) return DIFFATTN_E_UNSUPPORTED;
   if (p->batch * p->heads > 65535 || p->seqlen > kMaxSeqBf16) return DIFFATTN_E_UNSUPPORTED;
-  if (empty) return DIFFATTN_OK;
+  if (*empty) return DIFFATTN_OK;
   if (!q1 || !q2 || !k1c || !k2c || !vc || !lam || !out) return DIFFATTN_E_ARG;
   const void* ptrs[6] = {q1, q2, k1c, k2c, vc, out};
   for (const void* x : ptrs)
@@ -262,33 +285,68 @@ diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const
   if (!aligned(lam, 8) || (rms_weight && !aligned(rms_weight, 16)) ||
       (cache_len && !aligned(cache_len, 4)))
     return DIFFATTN_E_ARG;
-  const size_t need = decode_ws_bytes(p);
+  *need = decode_ws_bytes(p);
+  memset(a, 0, sizeof(*a));
+  a->q1 = q1; a->q2 = q2; a->k1 = k1c; a->k2 = k2c; a->v = vc;
+  a->cache_len = cache_len;
+  a->lam = lam;
+  a->rms_weight = rms_weight;
+  a->out = out;
+  a->B = p->batch; a->H = p->heads; a->L = p->seqlen;
+  a->G = static_cast<int>(p->heads / kv_heads_of(p));
+  diffattn::decode_split_geometry(a->B, a->H, a->L, &a->n_split, &a->split_len);
+  a->d = p->head_dim;
+  a->eps = p->rms_eps;
+  return DIFFATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const void* q2,
+                                const void* k1c, const void* k2c, const void* vc,
+                                const int32_t* cache_len, const diffattn_lambda_state* lam,
+                                const float* rms_weight, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  diffattn::DecodeArgs a;
+  size_t need = 0;
+  bool empty = false;
+  diffattn_status st = decode_prepare(p, q1, q2, k1c, k2c, vc, cache_len, lam, rms_weight, out,
+                                      &a, &need, &empty);
+  if (st != DIFFATTN_OK || empty) return st;
   if (!workspace || workspace_bytes < need) return DIFFATTN_E_WORKSPACE;
   if (!aligned(workspace, 16)) return DIFFATTN_E_ARG;
-  const int d = p->head_dim;
-  const size_t bh = static_cast<size_t>(p->batch) * p->heads;
-  const size_t bhk = static_cast<size_t>(p->batch) * kv_heads_of(p);
-  const size_t qb = bh * d * 2, kb = bhk * p->seqlen * d * 2, vb = bhk * p->seqlen * 2 * d * 2;
-  const Span in[8] = {{q1, qb}, {q2, qb}, {k1c, kb}, {k2c, kb}, {vc, vb},
-                      {cache_len, static_cast<size_t>(p->batch) * 4},
-                      {lam, sizeof(diffattn_lambda_state)},
-                      {rms_weight, static_cast<size_t>(p->heads) * 2 * d * sizeof(float)}};
-  const Span outs[2] = {{out, bh * 2 * d * 2}, {workspace, need}};
+  Span in[8];
+  const size_t out_bytes = decode_spans(p, q1, q2, k1c, k2c, vc, cache_len, lam, rms_weight, in);
+  const Span outs[2] = {{out, out_bytes}, {workspace, need}};
   if (any_overlap(outs, 2, in, 8)) return DIFFATTN_E_ARG;
-  diffattn::DecodeArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q1 = q1; a.q2 = q2; a.k1 = k1c; a.k2 = k2c; a.v = vc;
-  a.cache_len = cache_len;
-  a.lam = lam;
-  a.rms_weight = rms_weight;
-  a.out = out;
   a.partial = static_cast<float*>(workspace);
-  a.B = p->batch; a.H = p->heads; a.L = p->seqlen;
-  a.G = static_cast<int>(p->heads / kv_heads_of(p));
-  diffattn::decode_split_geometry(a.B, a.H, a.L, &a.n_split, &a.split_len);
-  a.d = d;
-  a.eps = p->rms_eps;
   return hip_status(diffattn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)), "decode");
+}
+
+diffattn_status diffattn_decode_noalloc(const diffattn_problem* p, const void* q1,
+                                        const void* q2, const void* k1c, const void* k2c,
+                                        const void* vc, const int32_t* cache_len,
+                                        const diffattn_lambda_state* lam,
+                                        const float* rms_weight, void* out, void* stream) {
+  diffattn::DecodeArgs a;
+  size_t need = 0;
+  bool empty = false;
+  diffattn_status st = decode_prepare(p, q1, q2, k1c, k2c, vc, cache_len, lam, rms_weight, out,
+                                      &a, &need, &empty);
+  if (st != DIFFATTN_OK || empty) return st;
+  if (need > DIFFATTN_DECODE_SCRATCH_BYTES) return DIFFATTN_E_SCRATCH;
+  Span in[8];
+  const size_t out_bytes = decode_spans(p, q1, q2, k1c, k2c, vc, cache_len, lam, rms_weight, in);
+  const Span outs[1] = {{out, out_bytes}};
+  if (any_overlap(outs, 1, in, 8)) return DIFFATTN_E_ARG;
+  float* ptr = nullptr;   // device address of the static scratch on the current device
+  st = hip_status(diffattn::decode_scratch(&ptr), "decode scratch lookup");
+  if (st != DIFFATTN_OK) return st;
+  a.partial = ptr;
+  return hip_status(diffattn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)),
+                    "decode_noalloc");
 }
 
 diffattn_status diffattn_cache_append(const diffattn_problem* p, const void* k1_new,

@@ -114,6 +114,9 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_cache_append_bf16(const AppendArgs& a, hipStream_t s);
 
+// Device address of the static decode scratch (DIFFATTN_DECODE_SCRATCH_BYTES) on the
+// current device, looked up once per device.
+hipError_t decode_scratch(float** out);
 // Decode split geometry shared by the workspace query and the launcher.
 void decode_split_geometry(int64_t B, int64_t H, int64_t L, int* n_split, int* split_len);
 // Backward workspace floats.

@@ -17,7 +17,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdiffattn.so")
 
-OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4
+OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_SCRATCH = 0, 1, 2, 3, 4, 5
+DECODE_SCRATCH_BYTES = 32 << 20   # DIFFATTN_DECODE_SCRATCH_BYTES
 FP32, BF16 = 0, 1
 OP_FWD, OP_DECODE, OP_BWD = 0, 1, 2
 LAYOUT_BHN, LAYOUT_BNH = 0, 1
@@ -25,7 +26,8 @@ _LAYOUTS = {"bhn": LAYOUT_BHN, "bnh": LAYOUT_BNH}
 
 # Every symbol declared in include/diffattn.h.
 EXPORTS = ("diffattn_lambda", "diffattn_lambda_layers", "diffattn_qkv_proj",
-           "diffattn_out_proj", "diffattn_fwd", "diffattn_decode", "diffattn_cache_append",
+           "diffattn_out_proj", "diffattn_fwd", "diffattn_decode", "diffattn_decode_noalloc",
+           "diffattn_cache_append",
            "diffattn_bwd", "diffattn_workspace_bytes", "diffattn_status_string",
            "diffattn_last_hip_error")
 
@@ -87,6 +89,8 @@ def _lib():
         lib.diffattn_decode.restype = ctypes.c_int
         lib.diffattn_decode.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
                                         ctypes.c_size_t, P]
+        lib.diffattn_decode_noalloc.restype = ctypes.c_int
+        lib.diffattn_decode_noalloc.argtypes = [ctypes.POINTER(Problem)] + [P] * 10
         lib.diffattn_cache_append.restype = ctypes.c_int
         lib.diffattn_cache_append.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P]
         lib.diffattn_bwd.restype = ctypes.c_int
@@ -317,6 +321,27 @@ def decode(q1, q2, k1c, k2c, vc, lam_state, cache_len=None, rms_weight=None, eps
         ctypes.byref(p), _ptr(q1), _ptr(q2), _ptr(k1c), _ptr(k2c), _ptr(vc), _ptr(cache_len),
         _ptr(lam_state), _ptr(rms_weight), _ptr(out), _ptr(workspace), _nbytes(workspace),
         _stream(vc.device)))
+    return out
+
+
+def decode_noalloc(q1, q2, k1c, k2c, vc, lam_state, cache_len=None, rms_weight=None,
+                   eps: float = 1e-5, out=None):
+    """decode() through the allocation-free entry point: the split partials live in the
+    library's static per-device scratch, so no workspace is passed (``out`` is still
+    allocated here when omitted). Calls that overlap on one device race."""
+    _need_cuda(q1, q2, k1c, k2c, vc, lam_state, cache_len, rms_weight, out)
+    B, Hkv, L, d = k1c.shape
+    H = q1.shape[1]
+    if tuple(q1.shape) != (B, H, d) or tuple(q2.shape) != (B, H, d):
+        raise ValueError("queries must be [B, H, d]")
+    if tuple(k2c.shape) != (B, Hkv, L, d) or tuple(vc.shape) != (B, Hkv, L, 2 * d):
+        raise ValueError("caches must be [B, Hkv, L, d] and [B, Hkv, L, 2d]")
+    p = problem(B, H, L, d, _dtype_code(k1c), eps, kv_heads=Hkv)
+    if out is None:
+        out = torch.empty(B, H, 2 * d, dtype=vc.dtype, device=vc.device)
+    _check("diffattn_decode_noalloc", _lib().diffattn_decode_noalloc(
+        ctypes.byref(p), _ptr(q1), _ptr(q2), _ptr(k1c), _ptr(k2c), _ptr(vc), _ptr(cache_len),
+        _ptr(lam_state), _ptr(rms_weight), _ptr(out), _stream(vc.device)))
     return out
 
 

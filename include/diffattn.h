@@ -39,7 +39,8 @@
  *     the contributions of its query heads).
  *   - The caller owns every buffer, including the workspace whose size is given by
  *     diffattn_workspace_bytes. The library keeps no state between calls and allocates
- *     no device memory.
+ *     no device memory; the one exception is the static scratch that
+ *     diffattn_decode_noalloc uses instead of a workspace (below).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
  *   - A call returns a status and never aborts. Argument checks run on the host before
  *     any HIP call, so they also work on a machine without a GPU. A failed launch returns
@@ -66,8 +67,13 @@ typedef enum {
   DIFFATTN_E_ARG = 1,          /* null/misaligned pointer, bad size, overlap, bad layer */
   DIFFATTN_E_UNSUPPORTED = 2,  /* dtype / head_dim / mode combination not implemented */
   DIFFATTN_E_WORKSPACE = 3,    /* workspace NULL or smaller than diffattn_workspace_bytes */
-  DIFFATTN_E_HIP = 4           /* a HIP runtime call or kernel launch failed */
+  DIFFATTN_E_HIP = 4,          /* a HIP runtime call or kernel launch failed */
+  DIFFATTN_E_SCRATCH = 5       /* the problem needs more than the static scratch of
+                                  diffattn_decode_noalloc (DIFFATTN_DECODE_SCRATCH_BYTES) */
 } diffattn_status;
+
+/* Size of the static device scratch that diffattn_decode_noalloc uses on each device. */
+#define DIFFATTN_DECODE_SCRATCH_BYTES (32u << 20)
 
 typedef enum { DIFFATTN_FP32 = 0, DIFFATTN_BF16 = 1 } diffattn_dtype;
 
@@ -202,6 +208,28 @@ diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const
                                 const int32_t* cache_len, const diffattn_lambda_state* lam,
                                 const float* rms_weight, void* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* diffattn_decode without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It allocates nothing (no hipMalloc, no hipFree, no allocating library call).
+ * The split partials go to a static device array of DIFFATTN_DECODE_SCRATCH_BYTES
+ * (32 MiB) that each device holds from this entry point's first call on it until the
+ * process ends; its device address is looked up once per device.
+ *   Arguments, layouts, ownership and results are those of diffattn_decode (same
+ *   kernels, bitwise the same output). The current device must be the one that owns
+ *   the pointers and the stream.
+ *   Limit: diffattn_workspace_bytes(DIFFATTN_OP_DECODE, p) must not exceed
+ *   DIFFATTN_DECODE_SCRATCH_BYTES, else DIFFATTN_E_SCRATCH (checked on the host before
+ *   any HIP call). That holds, for example, 64 sequences x 16 heads with a cache of 8192.
+ *   Every call on one device shares that device's array and leaves its partials there:
+ *   calls that overlap in time on one device (two streams, two host threads) race and
+ *   must be serialised by the caller. Each call writes every partial it reads, so
+ *   nothing needs clearing between calls. */
+diffattn_status diffattn_decode_noalloc(const diffattn_problem* p, const void* q1,
+                                        const void* q2, const void* k1c, const void* k2c,
+                                        const void* vc, const int32_t* cache_len,
+                                        const diffattn_lambda_state* lam,
+                                        const float* rms_weight, void* out, void* stream);
 
 /* Appends one generated token per sequence to its K1/K2/V cache, in place: the write half
  * of an autoregressive serving step, before the decode call that reads the cache whole

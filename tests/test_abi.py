@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = da.lib()
-    for s in range(5):
+    for s in range(6):
         assert lib.diffattn_status_string(s).decode().startswith("DIFFATTN_")
     assert lib.diffattn_last_hip_error() == 0
 
@@ -197,6 +197,26 @@ def test_decode_argument_checks():
     # caches beyond the kernel's 32-bit per-head buffer offsets
     long = da.problem(1, 1, (1 << 22) + 1, 64, da.BF16)
     assert call(long, ptrs, ws, need) == da.E_UNSUPPORTED
+
+
+def test_decode_noalloc_argument_checks():
+    """The allocation-free decode runs the same host checks as diffattn_decode, and
+    rejects a problem whose partials exceed the static scratch before any HIP call."""
+    lib = da.lib()
+    ptrs = [addr(i * 64) for i in range(9)]   # q1 q2 k1 k2 v len lam w out
+    call = lambda p, ptrs: lib.diffattn_decode_noalloc(ctypes.byref(p), *ptrs, None)
+    big = da.problem(64, 16, 1 << 16, 64, da.BF16)
+    assert da.workspace_bytes(da.OP_DECODE, big) > da.DECODE_SCRATCH_BYTES
+    assert call(big, ptrs) == da.E_SCRATCH
+    fits = da.problem(64, 16, 8192, 64, da.BF16)
+    assert da.workspace_bytes(da.OP_DECODE, fits) <= da.DECODE_SCRATCH_BYTES
+    assert call(da.problem(64, 16, 8192, 64, da.FP32), ptrs) == da.E_UNSUPPORTED
+    bad = list(ptrs); bad[0] = None
+    assert call(fits, bad) == da.E_ARG
+    bad = list(ptrs); bad[8] = ptrs[2]      # out aliases the K1 cache
+    assert call(fits, bad) == da.E_ARG
+    assert call(da.problem(0, 16, 8192, 64, da.BF16), ptrs) == da.OK
+    assert "scratch" in lib.diffattn_status_string(da.E_SCRATCH).decode()
 
 
 def test_cache_append_argument_checks():
