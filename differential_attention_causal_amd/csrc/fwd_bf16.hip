@@ -221,9 +221,11 @@ constexpr float kThr = 256.0f;
 constexpr float kMInit = -1e30f;
 
 // Per map and group: reference m, this lane's normaliser l (its 16 keys of each sub-tile)
-// and the sub-tile's partial sum lp (added to l once the sub-tile is settled).
+// and the sub-tile's partial sum lp (added to l once the sub-tile is settled). The fast
+// pass instead keeps two running sums, l and l2 (the first and last 8 of the lane's 16
+// keys of every sub-tile), with no per-sub-tile partial; the normaliser is l + l2.
 struct RowState {
-  float m, l, lp;
+  float m, l, lp, l2;
 };
 
 __device__ __forceinline__ float max16(const f32x16& s) {
@@ -274,11 +276,13 @@ __device__ __forceinline__ float exp_pack(const f32x16& s, float c, float m, bf1
 
 __device__ __forceinline__ bool over(float lp) { return !(lp <= kThr); }
 
-// Fast path bound: a row keeps the reference m of its first sub-tile, and its weights may
-// grow up to 2^32 (the products and sums stay far inside float range). A partial sum
-// above kBad (including +inf) flags the row for the fixup pass.
-constexpr float kBad = 4294967296.0f;
-__device__ __forceinline__ bool over_bad(float lp) { return lp > kBad; }
+// Fast path bound: a row keeps the reference m of its first sub-tile for the whole key
+// range. Its normaliser (the sum of all its weights, so also a bound on every weight) may
+// grow up to 2^48: the weights, their products with V and the accumulated sums then stay
+// far inside float range, and their relative precision does not depend on the scale. A
+// row whose normaliser ends above kBad (including +inf) is flagged for the fixup pass.
+// The check runs once per row, after the loop.
+constexpr float kBad = 281474976710656.0f;   // 2^48
 
 // Accumulator registers pass through one vector register to be scaled (read, multiply,
 // write back), so the rare slow path needs almost no vector registers of its own.
@@ -505,9 +509,9 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   // (which does not co-execute with the matrix core); each step's results are anchored
   // so the compiler cannot gather the steps of many slots in one place. The matrix core
   // thus always has a product queued while the vector unit works. CHECK (fixup pass):
-  // the row sums are tested against kThr and the rare slow path may follow; otherwise
-  // (fast pass) a row's partial sum over kBad only sets its flag, and the loop has no
-  // branch at all. IS_X: the X half-step, which
+  // the sub-tile's row sums are tested against kThr and the rare slow path may follow;
+  // otherwise (fast pass) the weights go straight into the running row sums, nothing is
+  // tested inside the loop and it has no branch at all. IS_X: the X half-step, which
   // also prefetches V^T(j) (used by Y(j) and again by X(j + 1)); the Y half-step of an
   // odd sub-tile holds the tile barrier.
   auto half = [&](auto masked, auto is_x, auto check, int j, f32x16 (&acc)[2][4],
@@ -525,7 +529,13 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     // Packed weights as separate 32-bit words: kept in a u32x4 and updated element by
     // element, the dot products below were compiled to read element 0 each time.
     uint32_t pw[2][2][4];
-    float ssum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    // Row sums: the sub-tile's partial (fixup pass), or the running sums (fast pass).
+    float ssum[2][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      ssum[g][0] = CHECK ? 0.f : st[g].l;
+      ssum[g][1] = CHECK ? 0.f : st[g].l2;
+    }
     bool slow = false;
     auto slot = [&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
@@ -589,13 +599,16 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
       if (u + 2 < n_tiles) dma_tile(rs, lds, u + 2, wv, lane);
     }
     static_for<2, 24>(slot);
-#pragma unroll
-    for (int g = 0; g < 2; ++g) st[g].lp = ssum[g][0] + ssum[g][1];
     if constexpr (CHECK) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) st[g].lp = ssum[g][0] + ssum[g][1];
       slow = __any(over(st[0].lp) || over(st[1].lp));
     } else {
-      bad[0] |= static_cast<uint32_t>(over_bad(st[0].lp));
-      bad[1] |= static_cast<uint32_t>(over_bad(st[1].lp));
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        st[g].l = ssum[g][0];
+        st[g].l2 = ssum[g][1];
+      }
     }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -621,8 +634,10 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
         }
       }
     }
+    if constexpr (CHECK) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) st[g].l += st[g].lp;
+      for (int g = 0; g < 2; ++g) st[g].l += st[g].lp;
+    }
   };
 
   auto step = [&](int j, auto masked, auto check) __attribute__((always_inline)) {
@@ -639,8 +654,8 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   auto run = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      st1[g] = RowState{kMInit, 0.f, 0.f};
-      st2[g] = RowState{kMInit, 0.f, 0.f};
+      st1[g] = RowState{kMInit, 0.f, 0.f, 0.f};
+      st2[g] = RowState{kMInit, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
 #pragma unroll
@@ -686,6 +701,15 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     vt_issue<1>(vt[1], va + v_off(0));
     for (int j = 0; j < jd; ++j) step(j, Flag<false>{}, Flag<SAFE>{});
     for (int j = jd; j < n_sub; ++j) step(j, Flag<true>{}, Flag<SAFE>{});
+    if constexpr (!SAFE) {
+      // Rows whose normaliser left the fast path's bound (either lane half of the row).
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        st1[g].l += st1[g].l2;
+        st2[g].l += st2[g].l2;
+        bad[g] = static_cast<uint32_t>(st1[g].l > kBad || st2[g].l > kBad);
+      }
+    }
     // Drain: acc2 += V^T(last) P2(last); vt holds V^T(last).
 #pragma unroll
     for (int t = 0; t < 2; ++t) {

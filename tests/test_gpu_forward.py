@@ -355,16 +355,20 @@ def test_unsupported_head_dim_raises():
 
 
 def test_bf16_fixup_pass_for_large_score_jump():
-    """A key whose score exceeds a row's first-sub-tile maximum by ~2^40 in weight: the
-    fast pass flags that row (bit 18 of word 0 of row block 1: row 400 = 256 + 8*18) and
-    the fixup pass recomputes it; every row must still match the oracle."""
+    """A key whose score exceeds a row's first-sub-tile maximum by ~2^100 in weight (query
+    and key rows of 3.0: a scaled score of 72): the fast pass flags that row (bit 18 of
+    word 0 of row block 1: row 400 = 256 + 8*18) and the fixup pass recomputes it. Row
+    300 gets a jump of ~2^43 (rows of 2.0), inside the fast pass's bound: not flagged, its
+    fast-pass result stands. Every row must match the oracle."""
     w = synth.custom("fwd", 1, 2, 600, 64, 5, "bf16", number=470)
     x, h, st, ls, _ = _run_fwd(w)
     x = {k: t.clone() for k, t in x.items()}
-    x["q1"][0, 0, 400] = 2.0
-    x["k1"][0, 0, 350] = 2.0
-    x["q2"][0, 1, 400] = 2.0
-    x["k2"][0, 1, 350] = 2.0
+    x["q1"][0, 0, 400] = 3.0
+    x["k1"][0, 0, 350] = 3.0
+    x["q2"][0, 1, 400] = 3.0
+    x["k2"][0, 1, 350] = 3.0
+    x["q1"][0, 0, 300] = 2.0
+    x["k1"][0, 0, 290] = 2.0
     p = da.problem(1, 2, 600, 64, da.BF16)
     ws = torch.zeros(da.workspace_bytes(da.OP_FWD, p), dtype=torch.uint8, device=DEV)
     y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, workspace=ws)
@@ -372,6 +376,7 @@ def test_bf16_fixup_pass_for_large_score_jump():
     torch.cuda.synchronize()
     flags = ws.view(torch.int32).cpu().numpy().reshape(2, 3, 8)   # [head, row block, word]
     assert flags[0, 1, 0] & (1 << 18) and flags[1, 1, 0] & (1 << 18)
+    assert not flags[0, 1, 4] & (1 << 5)    # row 300 = 256 + 8 * 5 + 4 (word 2 w + g = 4)
     assert torch.equal(y, y2)
     hh = {k: np64(t) for k, t in x.items()}
     ref = orc.forward(hh["q1"], hh["q2"], hh["k1"], hh["k2"], hh["v"], ls["lambda"],
@@ -380,7 +385,7 @@ def test_bf16_fixup_pass_for_large_score_jump():
 
 
 def test_bf16_fixup_pass_training_saves_and_backward():
-    """The score jump of the test above in training mode: the fixup pass rewrites the
+    """The flagged score jump of the test above in training mode: the fixup pass rewrites the
     saves (lse1, lse2, O1, O2, rstd) of the rows it flags, and the backward reads them.
     The flag bits are set, every save matches the oracle, and so does every gradient,
     dlambda and the lambda-vector gradients included."""
@@ -388,10 +393,10 @@ def test_bf16_fixup_pass_training_saves_and_backward():
     w = synth.custom("train", 1, 2, 600, 64, 5, "bf16", number=471)
     x, h = draw(w)
     x = {k: t.clone() for k, t in x.items()}
-    x["q1"][0, 0, 400] = 2.0
-    x["k1"][0, 0, 350] = 2.0
-    x["q2"][0, 1, 400] = 2.0
-    x["k2"][0, 1, 350] = 2.0
+    x["q1"][0, 0, 400] = 3.0
+    x["k1"][0, 0, 350] = 3.0
+    x["q2"][0, 1, 400] = 3.0
+    x["k2"][0, 1, 350] = 3.0
     h = {k: np64(t) for k, t in x.items()}
     st, ls = lam_pair(x, h, w.layer)
     p = da.problem(1, 2, 600, 64, da.BF16)
