@@ -724,7 +724,11 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   };
 
   // Epilogue per group: combine the lane halves' normalisers, form O, RMSNorm, scale,
-  // store. ONLY_BAD: only rows whose flag is set (after the safe re-run).
+  // store. ONLY_BAD: only rows whose flag is set (after the safe re-run). The lane holds
+  // 64 of its row's 128 channels: 32 b + 8 jg + 4 h + e for region b, chunk jg, e < 4.
+  // O = acc1 / l1 - lambda acc2 / l2 is formed once and kept in vector registers, which
+  // the loop no longer needs; Y = O times one per-row factor (1 - lambda_init) rstd,
+  // times w when given.
   const float lam = lamst->lambda_f;
   const float gsc = lamst->one_minus_init_f;
   const int hh = bh % H;
@@ -735,54 +739,72 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     float l1 = st1[g].l + __shfl_xor(st1[g].l, 32);
     float l2 = st2[g].l + __shfl_xor(st2[g].l, 32);
     const float il1 = 1.0f / l1, il2 = 1.0f / l2;
-    float ss = 0.f;
+    const float c2 = lam * il2;
+    float o[64];
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float o1 = acc1[g][b][j] * il1;
-        const float o2 = acc2[g][b][j] * il2;
-        acc1[g][b][j] = o1;
-        acc2[g][b][j] = o2;
-        const float o = o1 - lam * o2;
-        ss = fmaf(o, o, ss);
+        // Two rounded products (not contracted into one fused multiply-add), then their
+        // difference: identical maps with lambda = 1 give exactly zero, as in exact
+        // arithmetic.
+#pragma clang fp contract(off)
+        const float x = acc1[g][b][j] * il1 - acc2[g][b][j] * c2;
+        o[16 * b + j] = x;
+        ss[j & 3] = fmaf(x, x, ss[j & 3]);
       }
     }
-    ss += __shfl_xor(ss, 32);
-    const float rstd = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
+    float sst = (ss[0] + ss[1]) + (ss[2] + ss[3]);
+    sst += __shfl_xor(sst, 32);
+    const float rstd = 1.0f / sqrtf(sst * (1.0f / DV) + eps);
+    const float sc = gsc * rstd;
     const int qr = q0 + 8 * m + 2 * wv + g;
     if (qr < N && (!decltype(only_bad)::value || row_bad)) {
       // Y row of (b, h, qr): [B, H, N, 2d], or [B, N, H, 2d] with out_bnh.
       const int64_t yrow = out_bnh ? (static_cast<int64_t>(bh / H) * N + qr) * H + hh : hoff + qr;
-      bf16_t* Y = out + yrow * DV;
+      bf16_t* Y = out + yrow * DV + 4 * h;
+      if (rms_w) {
+        const float* W = rms_w + hh * DV + 4 * h;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
+        for (int i = 0; i < 16; ++i) {
+          const int b = i >> 2, jg = i & 3;
+          const float* x = o + 16 * b + 4 * jg;
+          const f32x4 wv4 = *reinterpret_cast<const f32x4*>(W + 8 * i);
+          const u32x2 pk = {pack_bf16x2(sc * (wv4[0] * x[0]), sc * (wv4[1] * x[1])),
+                            pack_bf16x2(sc * (wv4[2] * x[2]), sc * (wv4[3] * x[3]))};
+          *reinterpret_cast<u32x2*>(Y + 8 * i) = pk;
+        }
+      } else {
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const int col = 32 * b + 8 * jg + 4 * h;
-          f32x4 w = {1.f, 1.f, 1.f, 1.f};
-          if (rms_w) w = *reinterpret_cast<const f32x4*>(rms_w + hh * DV + col);
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float o = acc1[g][b][4 * jg + e] - lam * acc2[g][b][4 * jg + e];
-            y[e] = gsc * (w[e] * (o * rstd));
-          }
-          u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-          *reinterpret_cast<u32x2*>(Y + col) = pk;
-          if (sv_o1) {
-            f32x4 a = {acc1[g][b][4 * jg], acc1[g][b][4 * jg + 1], acc1[g][b][4 * jg + 2], acc1[g][b][4 * jg + 3]};
-            f32x4 bb = {acc2[g][b][4 * jg], acc2[g][b][4 * jg + 1], acc2[g][b][4 * jg + 2], acc2[g][b][4 * jg + 3]};
-            *reinterpret_cast<f32x4*>(sv_o1 + (hoff + qr) * DV + col) = a;
-            *reinterpret_cast<f32x4*>(sv_o2 + (hoff + qr) * DV + col) = bb;
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int b = i >> 2, jg = i & 3;
+          const float* x = o + 16 * b + 4 * jg;
+          const u32x2 pk = {pack_bf16x2(sc * x[0], sc * x[1]), pack_bf16x2(sc * x[2], sc * x[3])};
+          *reinterpret_cast<u32x2*>(Y + 8 * i) = pk;
         }
       }
-      if (sv_lse1 && h == 0) {
-        // lse_k = ln(sum_j exp(S_kj)) = (m_k + log2 l_k) * ln 2, m_k in the scaled log2 domain.
-        sv_lse1[hoff + qr] = (st1[g].m + __log2f(l1)) * kLn2;
-        sv_lse2[hoff + qr] = (st2[g].m + __log2f(l2)) * kLn2;
-        sv_rstd[hoff + qr] = rstd;
+      if (sv_o1) {
+        // Training saves: O1 = acc1 / l1, O2 = acc2 / l2, the log-sum-exps and rstd.
+        float* S1 = sv_o1 + (hoff + qr) * DV + 4 * h;
+        float* S2 = sv_o2 + (hoff + qr) * DV + 4 * h;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int b = i >> 2, jg = i & 3;
+          const f32x4 a = {acc1[g][b][4 * jg] * il1, acc1[g][b][4 * jg + 1] * il1,
+                           acc1[g][b][4 * jg + 2] * il1, acc1[g][b][4 * jg + 3] * il1};
+          const f32x4 bb = {acc2[g][b][4 * jg] * il2, acc2[g][b][4 * jg + 1] * il2,
+                            acc2[g][b][4 * jg + 2] * il2, acc2[g][b][4 * jg + 3] * il2};
+          *reinterpret_cast<f32x4*>(S1 + 8 * i) = a;
+          *reinterpret_cast<f32x4*>(S2 + 8 * i) = bb;
+        }
+        if (h == 0) {
+          // lse_k = ln(sum_j exp(S_kj)) = (m_k + log2 l_k) ln 2, m_k in the scaled log2
+          // domain.
+          sv_lse1[hoff + qr] = (st1[g].m + __log2f(l1)) * kLn2;
+          sv_lse2[hoff + qr] = (st2[g].m + __log2f(l2)) * kLn2;
+          sv_rstd[hoff + qr] = rstd;
+        }
       }
     }
   }
