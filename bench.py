@@ -9,6 +9,8 @@ width d and two PV of width 2d), the work the exact blockwise algorithm executes
 Also reported in the same line:
   prefill - the same forward on the prefill workload B4 H8 N2048 d64 (bf16, layer 4,
             inputs scaled by 1/sqrt 2): kernel time, TFLOP/s and fraction of the peak.
+  peaked  - the long-context forward on inputs 4x wider (N(0, 16)), whose rows often
+            outgrow the fast pass's bound: time, ratio to normal inputs, rows flagged.
   decode  - one split-KV decode step, 64 sequences x 16 heads against caches of
             8192 tokens: HBM GB/s = (cache + query + output bytes) / step time.
   train   - forward (with saves) + backward on B8 H12 N4096 when the backward
@@ -27,12 +29,12 @@ Also reported in the same line:
             events around each forward launch in the timed region, against the
             bf16 dense MFMA peak of 2500 TFLOP/s; traffic = HBM bytes per launch
             from profiles/hbm_traffic.md when it was measured on the current source.
-  cpu_baseline - the float64 oracle on the host cores, on a bounded sample of the
-            forward workload (query rows from the last one down, head by head,
-            ~12 s of CPU work).
+  cpu_baseline - the float64 oracle on the host cores (BLAS threads pinned to them), per
+            workload on a bounded sample: whole heads (forward; forward and backward
+            for training), whole decode sequences, the whole tiny workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--legs fwd,prefill,decode,train,proj,refgemm,copy]
+                       [--legs fwd,prefill,peaked,decode,train,proj,refgemm,copy]
                        [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -124,6 +126,39 @@ def leg_forward(steps, warmup, number=3):
                      "traffic": traffic_from_profiles("fwd_bf16_kernel<false>", "fwd_bf16.hip", w.name)},
         "formula_tflops_8dP": fl * 8.0 / 12.0 / (ms * 1e-3) / 1e12,
     }
+
+
+def leg_peaked(steps, warmup):
+    """The long-context forward shape with Q, K and V drawn 4x wider (N(0, 16)): scores
+    spread so far that many rows outgrow the fast pass's bound and are recomputed by the
+    fixup pass. Reports the forward time, its ratio to the normal-input forward and the
+    fraction of rows flagged."""
+    import torch
+    from differential_attention_causal_amd import diffattn as da
+    from differential_attention_causal_amd import synth
+    w = synth.custom("fwd", 1, 16, 32768, 64, 12, "bf16", scale=4.0, number=3)
+    x = synth.make_inputs(w, "cuda:0")
+    out = torch.empty_like(x["v"])
+    p = da.problem(w.batch, w.heads, w.seqlen, w.head_dim, da.BF16)
+    ws = torch.zeros(da.workspace_bytes(da.OP_FWD, p), dtype=torch.uint8, device="cuda:0")
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev:
+            ev[0].record()
+        da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, out=out, workspace=ws)
+        if ev:
+            ev[1].record()
+
+    _, _, inner = time_steps(step, max(2, steps // 5), max(1, warmup // 5), inner_events=True)
+    words = ws.view(torch.int32)
+    flagged = int(sum(bin(int(v) & 0xffffffff).count("1") for v in words.cpu().tolist()))
+    kern_ms = sum(inner) / len(inner)
+    return {"workload": "long-context bf16 forward B1 H16 N32768 d64, inputs N(0, 16)",
+            "fwd_kernel_ms": kern_ms, "tflops": fwd_flops(w) / (kern_ms * 1e-3) / 1e12,
+            "rows_flagged": flagged, "rows": w.batch * w.heads * w.seqlen,
+            "frac_rows_flagged": flagged / (w.batch * w.heads * w.seqlen)}
 
 
 def leg_decode(steps, warmup):
@@ -362,50 +397,97 @@ def traffic_from_profiles(kernel: str, source: str, workload: str):
     return None
 
 
-def cpu_baseline(budget_s: float = 12.0, cap_s: float = 30.0):
-    """The float64 oracle on the host over a time-bounded sample of the forward workload."""
+def cpu_baseline():
+    """The float64 oracle timed on the host cores, per workload, on bounded samples of the
+    same seeded inputs the GPU legs use (drawn on the GPU, copied to the host):
+      1 tiny fp32 forward   - the whole workload (oracle.forward);
+      2 prefill forward     - whole heads with the blocked oracle.head_forward;
+      3 long-context fwd    - one whole head (N = 32768) with oracle.head_forward;
+      4 decode step         - whole sequences (16 heads each) with oracle.decode;
+      5 training fwd + bwd  - whole heads with oracle.head_forward and head_backward.
+    BLAS threads are pinned to the cores this process may run on. Rates use the GPU legs'
+    conventions: 12 d P FLOP per head forward, 20 d P backward, and the cache, query and
+    output bytes of a decode step; full_s scales the sample's time to the whole workload."""
     import numpy as np
     import torch
+    from threadpoolctl import threadpool_limits
     from differential_attention_causal_amd import synth
     from oracle import diffattn_oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        blas_threads = None
-    w = synth.WORKLOADS[3]
-    x = synth.make_inputs(w, "cuda:0")
-    torch.cuda.synchronize()
-    lv = {k: x[k].cpu().double().numpy() for k in ("lq1", "lk1", "lq2", "lk2")}
-    ls = orc.lambda_scalar(lv["lq1"], lv["lk1"], lv["lq2"], lv["lk2"], w.layer)
-    n = w.seqlen
-    done_pairs, rows_done, heads_done, t0 = 0, 0, 0, time.perf_counter()
-    chunk = 256
-    for hh in range(w.heads):
-        h = {k: x[k][0, hh].float().cpu().double().numpy() for k in ("q1", "q2", "k1", "k2", "v")}
-        hi = n
-        while hi > 0:
-            lo = max(0, hi - chunk)
-            rows = list(range(lo, hi))
-            orc.forward_rows(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], rows, ls["lambda"],
+    cores = len(os.sched_getaffinity(0))
+    entries = []
+
+    def host(t):
+        return t.float().cpu().double().numpy()
+
+    def lam(x, w):
+        lv = {k: host(x[k]) for k in ("lq1", "lk1", "lq2", "lk2")}
+        return orc.lambda_scalar(lv["lq1"], lv["lk1"], lv["lq2"], lv["lk2"], w.layer)
+
+    def heads_forward(number, n_heads, backward=False):
+        w = synth.WORKLOADS[number]
+        x = synth.make_inputs(w, "cuda:0")
+        torch.cuda.synchronize()
+        ls = lam(x, w)
+        pairs = w.head_dim * w.seqlen * (w.seqlen + 1) // 2     # d P per head
+        t0 = time.perf_counter()
+        done = 0
+        for i in range(n_heads):
+            b, hh = divmod(i, w.heads)
+            h = {k: host(x[k][b, hh]) for k in x if k not in ("lq1", "lk1", "lq2", "lk2")}
+            orc.head_forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
                              ls["lambda_init"])
-            done_pairs += sum(i + 1 for i in rows)
-            rows_done += len(rows)
-            hi = lo
-            if time.perf_counter() - t0 >= min(budget_s, cap_s):
-                break
-        heads_done += 1
-        if time.perf_counter() - t0 >= min(budget_s, cap_s):
-            break
-    del x
-    el = time.perf_counter() - t0
-    fl = 12.0 * w.head_dim * done_pairs
-    cores = blas_threads or len(os.sched_getaffinity(0))
-    return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 oracle forward_rows over {rows_done} query rows (heads 0.."
-                      f"{heads_done - 1}, from the last row down) of B1 H16 N32768 d64: "
-                      f"{done_pairs} causal pairs in {el:.1f} s, 12 d P FLOP convention; "
-                      f"host cpus {len(os.sched_getaffinity(0))}"}
+            if backward:
+                orc.head_backward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], h["dout"],
+                                  ls["lambda"], ls["lambda_init"])
+            done += 1
+        el = time.perf_counter() - t0
+        del x
+        flop = (32.0 if backward else 12.0) * pairs * done
+        nh = w.batch * w.heads
+        return {"config": number, "workload": w.name, "sample": f"{done} of {nh} heads",
+                "wall_s": el, "gflops": flop / el / 1e9, "full_s": el * nh / done,
+                "flop_convention": "12 d P + 20 d P per head" if backward else "12 d P per head"}
+
+    with threadpool_limits(limits=cores):
+        # 1: the whole tiny workload
+        w = synth.WORKLOADS[1]
+        x = synth.make_inputs(w, "cuda:0")
+        h = {k: host(v) for k, v in x.items()}
+        ls = lam(x, w)
+        t0 = time.perf_counter()
+        orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"], ls["lambda_init"])
+        el = time.perf_counter() - t0
+        flop = 12.0 * w.head_dim * w.seqlen * (w.seqlen + 1) / 2 * w.batch * w.heads
+        entries.append({"config": 1, "workload": w.name, "sample": "whole workload",
+                        "wall_s": el, "gflops": flop / el / 1e9, "full_s": el,
+                        "flop_convention": "12 d P per head"})
+        entries.append(heads_forward(2, 4))
+        entries.append(heads_forward(3, 1))
+        # 4: whole sequences of the decode step
+        w = synth.WORKLOADS[4]
+        x = synth.make_inputs(w, "cuda:0")
+        torch.cuda.synchronize()
+        ls = lam(x, w)
+        n_seq = 4
+        t0 = time.perf_counter()
+        for b in range(n_seq):
+            sl = {k: host(x[k][b:b + 1]) for k in ("q1", "q2", "k1", "k2", "v")}
+            orc.decode(sl["q1"], sl["q2"], sl["k1"], sl["k2"], sl["v"], None, ls["lambda"],
+                       ls["lambda_init"])
+        el = time.perf_counter() - t0
+        del x
+        by = decode_bytes(w) * n_seq / w.batch
+        entries.append({"config": 4, "workload": w.name,
+                        "sample": f"{n_seq} of {w.batch} sequences (16 heads each)",
+                        "wall_s": el, "gb_s": by / el / 1e9, "full_s": el * w.batch / n_seq,
+                        "bytes_convention": "cache + query + output bytes"})
+        entries.append(heads_forward(5, 2, backward=True))
+    head = next(e for e in entries if e["config"] == 3)
+    return {"value": head["gflops"] / 1e3, "unit": "TFLOP/s", "cores": cores,
+            "blas_threads": cores, "kind": "oracle",
+            "sample": "float64 oracle, blocked head_forward over one whole head (N = 32768) "
+                      "of the long-context workload; per_config has every workload",
+            "per_config": entries}
 
 
 def main():
@@ -413,7 +495,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--legs", default="fwd,prefill,decode,train,proj,refgemm,copy")
+    ap.add_argument("--legs", default="fwd,prefill,peaked,decode,train,proj,refgemm,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -446,6 +528,9 @@ def main():
         wp, pf = leg_forward(args.steps, args.warmup, number=2)
         rec["prefill"] = {"workload": wp.name, "fwd_kernel_ms": pf["fwd_kernel_ms"],
                           "tflops": pf["roofline"]["achieved"], "frac": pf["roofline"]["frac"]}
+    if "peaked" in legs:
+        rec["peaked"] = leg_peaked(args.steps, args.warmup)
+        rec["peaked"]["time_vs_normal_inputs"] = rec["peaked"]["fwd_kernel_ms"] / fwd["fwd_kernel_ms"]
     if "decode" in legs:
         rec["decode"] = leg_decode(args.steps, args.warmup)
     if "train" in legs:
