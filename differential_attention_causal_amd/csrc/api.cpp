@@ -65,7 +65,7 @@ bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
 // head's K and V rows through 32-bit buffer offsets (N * 256 bytes for V).
 constexpr int64_t kMaxSeqBf16 = int64_t(1) << 22;
 
-size_t elem_bytes(diffattn_dtype t) { return t == DIFFATTN_FP32 ? 4 : 2; }
+size_t elem_bytes(int32_t t) { return t == DIFFATTN_FP32 ? 4 : 2; }
 
 // Validates the problem descriptor. Sets *empty when there is nothing to compute.
 diffattn_status check_problem(const diffattn_problem* p, bool* empty) {

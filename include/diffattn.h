@@ -93,7 +93,9 @@ typedef struct {
   int32_t head_dim;   /* d: width of Q1, Q2, K1, K2; V and outputs are 2d wide */
   int32_t causal;     /* must be 1 */
   float rms_eps;      /* eps of the per-head RMSNorm, >= 0, added inside the square root */
-  diffattn_dtype dtype; /* element type of Q/K/V, outputs and gradients */
+  int32_t dtype;      /* a diffattn_dtype: element type of Q/K/V, outputs and gradients
+                         (a plain integer, so that any value a caller stores is checked
+                         rather than read as an enumeration it does not belong to) */
   int32_t out_layout;   /* diffattn_layout of Y and dout; 0 (BHN) when zero-initialised */
   int64_t kv_heads;     /* heads of K1, K2, V (grouped-query attention: query head h reads
                            K/V head h / (heads / kv_heads)); must divide heads; 0 = heads */
