@@ -231,6 +231,7 @@ def leg_decode(steps, warmup):
                      "traffic": traffic_from_profiles("decode_split_kernel", "decode.hip", w.name)},
         "gqa": {"workload": f"{w.name}, 4 cache heads (groups of 4)", "decode_ms": gq_ms,
                 "bytes_per_step": gq_bytes, "GB_s": gq_bytes / (gq_ms * 1e-3) / 1e9,
+                "frac": gq_bytes / (gq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "speedup_vs_mha": kern_ms / gq_ms},
         "append": {"us_per_call": app_ms * 1e3, "bytes": app_bytes,
                    "GB_s": app_bytes / (app_ms * 1e-3) / 1e9, "bound": "launch latency"},

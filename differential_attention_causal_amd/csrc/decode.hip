@@ -219,63 +219,94 @@ __global__ void __launch_bounds__(NT, 2) decode_split_kernel(
   }
 }
 
-// Grouped-query decode: GW query heads that share one cache head (GW divides the group
-// size G) are served by one workgroup, so each cache byte is read once for all of them
-// instead of once per query head. Same structure as decode_split_kernel, with every
-// per-head quantity (queries, scores, weights, m, l, accumulators) held GW times over
-// and 32-key rounds (to keep those in registers). Writes the same per-(b, h, split)
-// partials, so decode_combine_kernel finishes both.
-// Cross-lane reductions without the LDS crossbar. Score lanes come in groups of 8 (lanes
-// 8 r .. 8 r + 7, one key per group). sum8 adds over a group (DPP: quad swaps 1 and 2,
-// then the mirror inside 8 lanes); the *_groups forms combine the 8 groups of a
-// wavefront, whose values are uniform within each group (the mirror inside 16 lanes
-// pairs groups 2k and 2k + 1, then rows are exchanged by the permlane swaps).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+// Grouped-query decode on the matrix cores. The gq query heads that share one cache
+// head are the columns of the B operand of v_mfma_f32_32x32x16_bf16 (32 columns, the
+// first gq real, the rest zero), so one pass over a 32-key round of the cache serves all
+// of them:
+//   * S^T = K Q^T per map: 32 keys x 32 query columns. Operand row m holds key
+//     perm_row(m) (bits 2 and 3 of the key swapped), so the 16 scores a lane holds for its
+//     column, packed to bf16, are directly the B operand of the value product: register j
+//     holds key key_of(j, h).
+//   * weights p = exp2(s log2(e) / 8 - m) per map, with a per-column reference m: the
+//     exact maximum of the wavefront's first round, moved (rescaling that column's
+//     accumulator and normaliser) only when a later round's maximum passes it by 2^20,
+//     so weights stay below 2^20.
+//   * O^T += V^T P^T per map (4 regions of 32 channels, 2 steps of 16 keys), V^T read with
+//     ds_read_b64_tr_b16.
+// The cache streams from HBM into LDS through buffer loads with LDS as the destination:
+// each wavefront has two 16 KiB buffers (a round's K1, K2 and V rows) and keeps two
+// rounds in flight while it computes a third from registers (a round's operands move to
+// registers first, which frees its buffer for the round after next). The loads are
+// assembly and their waits explicit, so the compiler neither orders LDS reads behind
+// them nor waits for later rounds. No barrier: each wavefront reads only its own
+// buffers. The four wavefronts' states are merged in LDS and written as the same
+// per-(b, h, split) partials as the other decode kernels, so decode_combine_kernel
+// finishes all of them.
+namespace gq {
+constexpr int KPR = 32;                 // keys per wavefront round
+constexpr int KT = KPR * 128;           // a round's K1 (or K2) rows: [32][128 B]
+constexpr int VREG = KPR * 64;          // a round's V rows, one 32-channel region: [32][64 B]
+constexpr int BUF = 2 * KT + 4 * VREG;  // K1 | K2 | V, 16 KiB
+constexpr int WAVE_LDS = 2 * BUF;       // two buffers per wavefront
+constexpr int DMA_PER_ROUND = 16;       // 1 KiB loads: 4 K1, 4 K2, 8 V
+static_assert(DMA_PER_ROUND == 16, "the loop's vmcnt waits count 16 loads per round");
+constexpr float kMove = 20.0f;          // a column's reference moves past 2^20 growth
+// K rows: 16-byte unit u of row r stored at u ^ k_swz(r), so the 32 operand rows read by
+// one ds_read_b128 spread over the banks; V rows: chunk c of row r at c ^ v_swz(r).
+__device__ __forceinline__ int k_swz(int row) {
+  return ((row ^ (row >> 2)) & 1) | (row & 2) | ((row >> 1) & 4);
 }
-__device__ __forceinline__ float sum8(float x) {
-  x += dpp<0xB1>(x);    // quad_perm [1, 0, 3, 2]
-  x += dpp<0x4E>(x);    // quad_perm [2, 3, 0, 1]
-  x += dpp<0x141>(x);   // row_half_mirror
+__device__ __forceinline__ int v_swz(int row) { return 2 * ((row >> 1) & 1); }
+__device__ __forceinline__ int perm_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+__device__ __forceinline__ int key_of(int j, int h) { return 16 * (j >> 3) + 8 * h + (j & 7); }
+__device__ __forceinline__ int chan_of(int j, int h) { return (j & 3) + 4 * h + 8 * (j >> 2); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef char __attribute__((address_space(3))) lds_char;
+__device__ __forceinline__ u32x2 ds_read_tr16(const lds_char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x4 ds_read_b128(const lds_char* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
+}
+// 16 bytes per lane from the buffer (offset voff) into LDS at m0 + 16 lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t m0, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rs));
+}
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// An accumulation register scaled in place through one vector register (the rare
+// reference move), so the accumulators never leave the accumulation registers.
+__device__ __forceinline__ float scale_acc(float x, float a) {
+  float t;
+  asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+               : "+a"(x), "=&v"(t)
+               : "v"(a));
   return x;
 }
-template <bool MAX>
-__device__ __forceinline__ float combine(float a, float b) { return MAX ? fmaxf(a, b) : a + b; }
-// The swaps exchange rows between two registers that both start as x: afterwards each
-// lane holds its own row's value in one and the partner row's in the other (rows of 16
-// lanes paired 0-1, 2-3 by the 16-lane swap; halves of the wavefront by the 32-lane
-// swap). Issued as assembly: the compiler's model of the swap builtins folded the two
-// results into one. The s_nop wait states cover the vector-ALU write before the swap and
-// the reads after it.
-template <bool MAX>
-__device__ __forceinline__ float across_groups(float x) {
-  x = combine<MAX>(x, dpp<0x140>(x));   // row_mirror
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  x = combine<MAX>(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-  a = __builtin_bit_cast(uint32_t, x);
-  b = a;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  return combine<MAX>(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+__device__ __forceinline__ void acc_pin(f32x16 (&a)[4]) {
+  asm volatile("" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
 }
+}  // namespace gq
 
-template <int GW>
-__global__ void __launch_bounds__(NT, 2) decode_group_kernel(
+__global__ void __launch_bounds__(NT, 1) decode_mfma_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
     const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cache_len,
-    float* __restrict__ partial, int64_t H, int64_t L, int n_split, int rounds, int G) {
-  constexpr int KPR = 32;                 // keys per wavefront round
-  constexpr int SGG = KPR / 8;            // score groups of 8 keys
-  constexpr int VIG = KPR / 4;            // value loads of 4 rows
-  __shared__ float red[4][2 * GW][PART];
+    float* __restrict__ partial, int64_t H, int64_t L, int n_split, int rounds, int G, int gq) {
+  using namespace gq;
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  lds_char* lds = (lds_char*)lds_raw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
   const int split = blockIdx.x;
-  const int64_t h0 = static_cast<int64_t>(blockIdx.y) * GW;   // first query head (b H + h)
+  const int64_t h0 = static_cast<int64_t>(blockIdx.y) * gq;   // first query head (b H + h)
   const int64_t b = h0 / H;
   int64_t len = cache_len ? static_cast<int64_t>(cache_len[b]) : L;
   len = len < 1 ? 1 : (len > L ? L : len);
@@ -283,6 +314,8 @@ __global__ void __launch_bounds__(NT, 2) decode_group_kernel(
   const int64_t s0 = static_cast<int64_t>(split) * split_len;
   if (s0 >= len) return;
 
+  // Cache rows through buffer resources bounded at len rows: keys at or beyond len read
+  // as zero (and are masked).
   const int64_t kvh = b * (H / G) + (h0 - b * H) / G;   // the shared cache head
   constexpr int kBufFlags = 0x00020000;
   const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(
@@ -292,157 +325,234 @@ __global__ void __launch_bounds__(NT, 2) decode_group_kernel(
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(v + kvh * L * DV), 0, static_cast<int>(len * DV * 2), kBufFlags);
 
-  const int r = lane >> 3, c = lane & 7;
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x8 qa[GW], qb[GW];
+  // Query columns: lane (n, h) holds channels 16 kb + 8 h .. + 7 of query head h0 + n.
+  bf16x8 qa[4], qb[4];
 #pragma unroll
-  for (int g = 0; g < GW; ++g) {
-    qa[g] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q1 + (h0 + g) * D + 8 * c));
-    qb[g] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q2 + (h0 + g) * D + 8 * c));
+  for (int kb = 0; kb < 4; ++kb) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (n < gq) {
+      x = *reinterpret_cast<const u32x4*>(q1 + (h0 + n) * D + 16 * kb + 8 * h);
+      y = *reinterpret_cast<const u32x4*>(q2 + (h0 + n) * D + 16 * kb + 8 * h);
+    }
+    qa[kb] = __builtin_bit_cast(bf16x8, x);
+    qb[kb] = __builtin_bit_cast(bf16x8, y);
   }
-  const int e = lane & 15, f = lane >> 4;
-  const int ko = r * D * 2 + 16 * c;
-  const int vo = f * DV * 2 + 16 * e;
+  // The query loads complete here, so the compiler's own waits for them stay out of the
+  // loop, where a vmcnt wait would also stall on the cache loads in flight.
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) asm volatile("" : "+v"(qa[kb]), "+v"(qb[kb]));
+  // DMA source offsets within a round (key rows from its first key): K block i holds rows
+  // 8 i .. 8 i + 7 (lane: row 8 i + lane / 8, unit lane % 8), V block (region rg, half i)
+  // rows 16 i .. 16 i + 15 of region rg (lane: row 16 i + lane / 4, chunk lane % 4).
+  int kso[4], vso[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * i + (lane >> 3), pu = lane & 7;
+    kso[i] = row * (D * 2) + 16 * (pu ^ k_swz(row));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * i + (lane >> 2), pc = lane & 3;
+    vso[i] = row * (DV * 2) + 16 * (pc ^ v_swz(row));
+  }
+  // Operand reads: K row perm_row(n), unit (2 kb + h) ^ k_swz; V^T transposing reads.
+  int kra;
+  {
+    const int kr = perm_row(n);
+    kra = kr * 128;
+  }
+  const int ks = k_swz(perm_row(n));
+  int vta;
+  {
+    const int g16 = lane >> 4, jj = (lane >> 2) & 3, a = lane & 3;
+    const int row = 8 * (g16 >> 1) + jj;
+    const int cp = 2 * (g16 & 1) + (a >> 1);
+    vta = row * 64 + 16 * (cp ^ v_swz(row)) + 8 * (a & 1);
+  }
+  const uint32_t wbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + wv * WAVE_LDS;
+  lds_char* wbuf = lds + wv * WAVE_LDS;
+
+  // The 16 loads of the round that starts at key kb into buffer c.
+  auto issue = [&](int64_t kb, int c) __attribute__((always_inline)) {
+    const int kbi = static_cast<int>(kb);
+    const uint32_t dst = wbase + c * BUF;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dma16(rk1, dst + 1024 * i, kbi * (D * 2) + kso[i]);
+      dma16(rk2, dst + KT + 1024 * i, kbi * (D * 2) + kso[i]);
+    }
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dma16(rv, dst + 2 * KT + VREG * rg + 1024 * i, kbi * (DV * 2) + vso[i] + 64 * rg);
+    }
+  };
 
   const float cs = kLog2e / 8.0f;
-  float m1[GW], m2[GW], l1[GW], l2[GW], acc1[GW][8], acc2[GW][8];
+  f32x16 acc1[4], acc2[4];
 #pragma unroll
-  for (int g = 0; g < GW; ++g) {
-    m1[g] = m2[g] = -INFINITY;
-    l1[g] = l2[g] = 0.f;
+  for (int rg = 0; rg < 4; ++rg) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc1[g][t] = acc2[g][t] = 0.f;
+    for (int j = 0; j < 16; ++j) acc1[rg][j] = acc2[rg][j] = 0.f;
   }
+  float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
 
-#pragma clang loop unroll(disable)
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int64_t kb = s0 + (static_cast<int64_t>(wv) * rounds + rd) * KPR;
-    if (kb >= len) break;
-    const int kbs = __builtin_amdgcn_readfirstlane(static_cast<int>(kb));
-    u32x4 kx[SGG], ky[SGG], vv[VIG];
+  const int64_t kfirst = s0 + static_cast<int64_t>(wv) * rounds * KPR;
+  int nr = 0;   // rounds of this wavefront that start below len
+  for (int rd = 0; rd < rounds; ++rd)
+    if (kfirst + static_cast<int64_t>(rd) * KPR < len) nr = rd + 1;
+  if (nr > 0) issue(kfirst, 0);
+  if (nr > 1) issue(kfirst + KPR, 1);
+
+  // One round of map k: scores, weights (with the rare move of a column's reference) and
+  // the packed B operands of the value product.
+  auto softmax = [&](f32x16 S, int64_t kb, bool first, float& m, float& l, f32x16 (&acc)[4],
+                     bf16x8& pa, bf16x8& pb) __attribute__((always_inline)) {
+    if (kb + KPR > len) {
+      const int kl = static_cast<int>(len - kb);   // keys of this round below len
 #pragma unroll
-    for (int sg = 0; sg < SGG; ++sg) {
-      kx[sg] = __builtin_amdgcn_raw_buffer_load_b128(rk1, ko + sg * 8 * D * 2, kbs * D * 2, 2);
-      ky[sg] = __builtin_amdgcn_raw_buffer_load_b128(rk2, ko + sg * 8 * D * 2, kbs * D * 2, 2);
+      for (int j = 0; j < 16; ++j)
+        if (key_of(j, h) >= kl) S[j] = -INFINITY;
     }
+    float mx = S[0];
 #pragma unroll
-    for (int i = 0; i < VIG; ++i)
-      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * 4 * DV * 2, kbs * DV * 2, 2);
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, S[j]);
+    mx = max_halves(mx) * cs;
+    if (first) {
+      m = mx;
+    } else {
+      const bool mv = mx > m + kMove;
+      if (__builtin_expect(__any(mv), 0)) {
+        const float mn = mv ? mx : m;
+        const float al = fast_exp2(m - mn);
+        m = mn;
+        l *= al;
 #pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      float s1[SGG], s2[SGG];
+        for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
-      for (int sg = 0; sg < SGG; ++sg) {
-        float d1 = 0.f, d2 = 0.f;
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, kx[sg]), kc = __builtin_bit_cast(bf16x8, ky[sg]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x2 q1p = {qa[g][2 * t], qa[g][2 * t + 1]}, k1p = {ka[2 * t], ka[2 * t + 1]};
-          const bf16x2 q2p = {qb[g][2 * t], qb[g][2 * t + 1]}, k2p = {kc[2 * t], kc[2 * t + 1]};
-          d1 = __builtin_amdgcn_fdot2_f32_bf16(q1p, k1p, d1, false);
-          d2 = __builtin_amdgcn_fdot2_f32_bf16(q2p, k2p, d2, false);
-        }
-        d1 = sum8(d1);
-        d2 = sum8(d2);
-        const bool ok = kb + 8 * sg + r < len;
-        s1[sg] = ok ? d1 * cs : -INFINITY;
-        s2[sg] = ok ? d2 * cs : -INFINITY;
+          for (int j = 0; j < 16; ++j) acc[rg][j] = scale_acc(acc[rg][j], al);
       }
-      float mx1 = s1[0], mx2 = s2[0];
+    }
+    f32x8 x, y;
+    float sum = 0.f;
 #pragma unroll
-      for (int sg = 1; sg < SGG; ++sg) {
-        mx1 = fmaxf(mx1, s1[sg]);
-        mx2 = fmaxf(mx2, s2[sg]);
+    for (int e = 0; e < 8; ++e) {
+      x[e] = fast_exp2(fmaf(S[e], cs, -m));
+      y[e] = fast_exp2(fmaf(S[8 + e], cs, -m));
+      sum += x[e] + y[e];
+    }
+    l += sum;
+    pa = __builtin_convertvector(x, bf16x8);
+    pb = __builtin_convertvector(y, bf16x8);
+  };
+
+  acc_pin(acc1);
+  acc_pin(acc2);
+  for (int rd = 0; rd < nr; ++rd) {
+    const int c = rd & 1;
+    const int64_t kb = kfirst + static_cast<int64_t>(rd) * KPR;
+    acc_pin(acc1);
+    acc_pin(acc2);
+    // This round's 16 loads are done; the next round's may still be in flight.
+    if (rd + 1 < nr) {
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    const lds_char* bk = wbuf + c * BUF;
+    u32x4 kx[4], ky[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int off = kra + 16 * ((2 * kk + h) ^ ks);
+      kx[kk] = ds_read_b128(bk + off);
+      ky[kk] = ds_read_b128(bk + KT + off);
+    }
+    u32x4 vt[2][4];
+    const lds_char* vb = bk + 2 * KT + vta;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const u32x2 lo = ds_read_tr16(vb + VREG * rg + 1024 * t);
+        const u32x2 hi = ds_read_tr16(vb + VREG * rg + 1024 * t + 4 * 64);
+        vt[t][rg] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
-      mx1 = across_groups<true>(mx1);
-      mx2 = across_groups<true>(mx2);
-      const float mn1 = fmaxf(m1[g], mx1), mn2 = fmaxf(m2[g], mx2);
-      const float al1 = fast_exp2(m1[g] - mn1), al2 = fast_exp2(m2[g] - mn2);
-      float sum1 = 0.f, sum2 = 0.f;
+    }
+    // Every read of buffer c is done before the round after next is loaded into it.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (rd + 2 < nr) issue(kb + 2 * KPR, c);
+    f32x16 S1 = {}, S2 = {};
 #pragma unroll
-      for (int sg = 0; sg < SGG; ++sg) {
-        s1[sg] = fast_exp2(s1[sg] - mn1);   // now the weights p
-        s2[sg] = fast_exp2(s2[sg] - mn2);
-        sum1 += s1[sg];
-        sum2 += s2[sg];
-      }
-      sum1 = across_groups<false>(sum1);
-      sum2 = across_groups<false>(sum2);
-      l1[g] = fmaf(l1[g], al1, sum1);
-      l2[g] = fmaf(l2[g], al2, sum2);
-      m1[g] = mn1;
-      m2[g] = mn2;
+    for (int kk = 0; kk < 4; ++kk) {
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx[kk]), qa[kk], S1, 0, 0, 0);
+      S2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ky[kk]), qb[kk], S2, 0, 0, 0);
+    }
+    bf16x8 p1a, p1b, p2a, p2b;
+    softmax(S1, kb, rd == 0, m1, l1, acc1, p1a, p1b);
+    softmax(S2, kb, rd == 0, m2, l2, acc2, p2a, p2b);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        acc1[g][t] *= al1;
-        acc2[g][t] *= al2;
-      }
-      // values: key 4 i + f, whose weight sits in register i / 2 of lanes 8 (key % 8)
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int i = 0; i < VIG; ++i) {
-        const int src = 32 * (i & 1) + 8 * f;
-        const float w1 = __shfl(s1[i >> 1], src);
-        const float w2 = __shfl(s2[i >> 1], src);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float lo = __uint_as_float(vv[i][t] << 16);
-          const float hi = __uint_as_float(vv[i][t] & 0xffff0000u);
-          acc1[g][2 * t] = fmaf(w1, lo, acc1[g][2 * t]);
-          acc1[g][2 * t + 1] = fmaf(w1, hi, acc1[g][2 * t + 1]);
-          acc2[g][2 * t] = fmaf(w2, lo, acc2[g][2 * t]);
-          acc2[g][2 * t + 1] = fmaf(w2, hi, acc2[g][2 * t + 1]);
-        }
+      for (int rg = 0; rg < 4; ++rg) {
+        const bf16x8 va = __builtin_bit_cast(bf16x8, vt[t][rg]);
+        acc1[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, t ? p1b : p1a, acc1[rg], 0, 0, 0);
+        acc2[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, t ? p2b : p2a, acc2[rg], 0, 0, 0);
       }
     }
   }
-#pragma unroll
-  for (int g = 0; g < GW; ++g) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      acc1[g][t] += __shfl_xor(acc1[g][t], 16);
-      acc1[g][t] += __shfl_xor(acc1[g][t], 32);
-      acc2[g][t] += __shfl_xor(acc2[g][t], 16);
-      acc2[g][t] += __shfl_xor(acc2[g][t], 32);
+  l1 += __shfl_xor(l1, 32);
+  l2 += __shfl_xor(l2, 32);
+
+  // Merge the four wavefronts per query head: red[w][q][map] = (m, l, acc[128]).
+  __syncthreads();   // every wavefront is done with its buffers
+  float* red = reinterpret_cast<float*>(lds_raw);
+  auto slot = [&](int w, int q, int mp) { return red + ((w * gq + q) * 2 + mp) * PART; };
+  if (n < gq) {
+    float* r1 = slot(wv, n, 0);
+    float* r2 = slot(wv, n, 1);
+    if (h == 0) {
+      r1[0] = m1; r1[1] = l1;
+      r2[0] = m2; r2[1] = l2;
     }
-    if (lane == 0) {
-      red[wv][2 * g][0] = m1[g];
-      red[wv][2 * g][1] = l1[g];
-      red[wv][2 * g + 1][0] = m2[g];
-      red[wv][2 * g + 1][1] = l2[g];
-    }
-    if (f == 0) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        red[wv][2 * g][2 + 8 * e + t] = acc1[g][t];
-        red[wv][2 * g + 1][2 + 8 * e + t] = acc2[g][t];
+    for (int rg = 0; rg < 4; ++rg) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        r1[2 + 32 * rg + chan_of(j, h)] = acc1[rg][j];
+        r2[2 + 32 * rg + chan_of(j, h)] = acc2[rg][j];
       }
     }
   }
   __syncthreads();
-  // Merge the 4 wavefront states per head: thread = (map, channel), looping over heads.
-  if (tid < 2 * DV) {
-    const int mp = tid / DV, ch = tid % DV;
+  for (int it = tid; it < gq * 2 * DV; it += NT) {
+    const int q = it / (2 * DV), mp = (it / DV) & 1, ch = it % DV;
+    float M = slot(0, q, mp)[0];
 #pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      float* out = partial + ((h0 + g) * n_split + split) * 2 * PART;
-      const int row = 2 * g + mp;
-      float M = red[0][row][0];
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, slot(w, q, mp)[0]);
+    float A = 0.f, Ssum = 0.f;
 #pragma unroll
-      for (int w = 1; w < 4; ++w) M = fmaxf(M, red[w][row][0]);
-      float A = 0.f, S = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float sc = fast_exp2(red[w][row][0] - M);
-        A = fmaf(red[w][row][2 + ch], sc, A);
-        S = fmaf(red[w][row][1], sc, S);
-      }
-      out[mp * PART + 2 + ch] = A;
-      if (ch == 0) {
-        out[mp * PART + 0] = M;
-        out[mp * PART + 1] = S;
-      }
+    for (int w = 0; w < 4; ++w) {
+      const float* r = slot(w, q, mp);
+      const float sc = fast_exp2(r[0] - M);   // 0 for a wavefront without keys (m = -inf)
+      A = fmaf(r[2 + ch], sc, A);
+      Ssum = fmaf(r[1], sc, Ssum);
+    }
+    float* out = partial + ((h0 + q) * n_split + split) * 2 * PART + mp * PART;
+    out[2 + ch] = A;
+    if (ch == 0) {
+      out[0] = M;
+      out[1] = Ssum;
     }
   }
+}
+
+// LDS bytes of decode_mfma_kernel for gq query heads per workgroup: the V buffers during
+// the rounds, then the merge of the four wavefront states.
+size_t decode_mfma_lds_bytes(int gq) {
+  const size_t merge = static_cast<size_t>(4) * gq * 2 * PART * sizeof(float);
+  const size_t bufs = static_cast<size_t>(4) * gq::WAVE_LDS;
+  return merge > bufs ? merge : bufs;
 }
 
 // One thread per map and channel (map k = threadIdx.x / 128). The partials of the
@@ -548,25 +658,40 @@ void decode_split_geometry(int64_t B, int64_t H, int64_t L, int* n_split, int* s
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   using namespace dec;
-  const int rounds = a.split_len / (KEYS_PER_ROUND * 4);
   const int64_t BH = a.B * a.H;
-  // Query heads served per workgroup: the largest of 4, 3, 2 dividing the group size.
-  const int gw = a.G % 4 == 0 ? 4 : (a.G % 3 == 0 ? 3 : (a.G % 2 == 0 ? 2 : 1));
-  auto group = [&](auto kern, int heads_per_wg) {
-    // 32-key rounds: twice as many per split as the 64-key rounds of the single-head kernel.
-    hipLaunchKernelGGL(kern, dim3(a.n_split, static_cast<unsigned>(BH / heads_per_wg)),
-                       dim3(NT), 0, s, static_cast<const bf16_t*>(a.q1),
-                       static_cast<const bf16_t*>(a.q2), static_cast<const bf16_t*>(a.k1),
-                       static_cast<const bf16_t*>(a.k2), static_cast<const bf16_t*>(a.v),
-                       a.cache_len, a.partial, a.H, a.L, a.n_split, 2 * rounds, a.G);
-  };
-  if (gw == 4) {
-    group(decode_group_kernel<4>, 4);
-  } else if (gw == 3) {
-    group(decode_group_kernel<3>, 3);
-  } else if (gw == 2) {
-    group(decode_group_kernel<2>, 2);
+  int n_split = a.n_split;
+  int64_t split_len = a.split_len;
+  if (a.G > 1) {
+    // Grouped-query attention: the query heads of a group on the matrix cores, gq at a
+    // time (the largest divisor of the group size up to 32, the B operand's columns).
+    int gq = 1;
+    for (int c = 1; c <= 32 && c <= a.G; ++c)
+      if (a.G % c == 0) gq = c;
+    const int64_t groups = BH / gq;
+    // 32-key rounds per wavefront, splits of 128 x rounds keys: as long as possible (up to
+    // 8192 keys) while there is a workgroup for every compute unit, since a workgroup
+    // fills its unit's LDS and each one that ends drains the unit's load pipeline; at
+    // least 512 keys, so there are no more splits than the workspace holds partials for.
+    int rounds_g = 64;
+    while (rounds_g > 4 && groups * ((a.L + 128 * rounds_g - 1) / (128 * rounds_g)) < 256)
+      rounds_g >>= 1;
+    split_len = static_cast<int64_t>(gq::KPR) * 4 * rounds_g;
+    n_split = static_cast<int>((a.L + split_len - 1) / split_len);
+    const size_t lds = decode_mfma_lds_bytes(gq);
+    static std::atomic<uint64_t> attr_done{0};
+    const hipError_t ea = once_per_device(attr_done, [] {
+      return hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 static_cast<int>(decode_mfma_lds_bytes(32)));
+    });
+    if (ea != hipSuccess) return ea;
+    hipLaunchKernelGGL(decode_mfma_kernel, dim3(n_split, static_cast<unsigned>(groups)), dim3(NT),
+                       lds, s, static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
+                       static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
+                       static_cast<const bf16_t*>(a.v), a.cache_len, a.partial, a.H, a.L,
+                       n_split, rounds_g, a.G, gq);
   } else {
+    const int rounds = a.split_len / (KEYS_PER_ROUND * 4);
     hipLaunchKernelGGL(decode_split_kernel, dim3(a.n_split, static_cast<unsigned>(BH)),
                        dim3(NT), 0, s, static_cast<const bf16_t*>(a.q1),
                        static_cast<const bf16_t*>(a.q2), static_cast<const bf16_t*>(a.k1),
@@ -577,7 +702,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(BH)), dim3(2 * DV), 0, s,
                      a.partial, a.cache_len, a.lam, a.rms_weight, static_cast<bf16_t*>(a.out),
-                     a.H, a.L, a.n_split, static_cast<int64_t>(a.split_len), a.eps);
+                     a.H, a.L, n_split, split_len, a.eps);
   return hipGetLastError();
 }
 

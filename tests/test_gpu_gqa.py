@@ -52,11 +52,22 @@ def test_forward_grouped(dtype, B, H, hkv, N):
         assert np.all(normwise_rel(np64(y), ref, axes=(2, 3)) <= FP32_TOL)
 
 
+# Groups of 2, 3, 4, 6, 8, 16 and 32 query heads (the matrix-core kernel's column counts,
+# 32 being the most it takes), cache lengths that end inside a round, a length of 1,
+# caches longer than one split, and a length just past a split boundary.
 @pytest.mark.parametrize("B,H,hkv,L,lens", [(3, 4, 2, 700, [700, 1, 333]),
                                             (2, 8, 1, 1500, [1500, 1024]),
-                                            (1, 16, 4, 4100, None)])
+                                            (1, 16, 4, 4100, None),
+                                            (1, 6, 2, 333, None),
+                                            (2, 6, 1, 20000, [20000, 8193]),
+                                            (2, 16, 1, 9000, [9000, 4500]),
+                                            (1, 32, 1, 2000, None)])
 def test_decode_grouped(B, H, hkv, L, lens):
-    w = synth.custom("decode", B, H, L, 64, 8, "bf16", number=1700 + L)
+    _decode_grouped_case(B, H, hkv, L, lens)
+
+
+def _decode_grouped_case(B, H, hkv, L, lens):
+    w = synth.custom("decode", B, H, L, 64, 8, "bf16", number=1700 + L + H)
     x, _ = draw(w)
     kv, rep = _group(x, hkv)
     st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
@@ -71,22 +82,32 @@ def test_decode_grouped(B, H, hkv, L, lens):
     assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
 
 
-def test_decode_grouped_serving_workload_sampled():
-    """64 sequences x 16 query heads sharing 4 cache heads, cache length 8192."""
+def test_decode_grouped_long_splits():
+    """Enough groups for the longest splits (8192 keys) with caches of three splits, and
+    cache lengths at and around the split and round boundaries."""
+    B, H, hkv, L = 32, 16, 4, 16385
+    lens = np.random.default_rng(1717).integers(1, L + 1, B)
+    lens[:8] = [L, 8192, 8193, 1, 16384, 31, 32, 8191]
+    _decode_grouped_case(B, H, hkv, L, [int(v) for v in lens])
+
+
+def test_decode_grouped_serving_workload():
+    """64 sequences x 16 query heads sharing 4 cache heads, cache length 8192: every
+    output against the oracle, one sequence at a time."""
     w = synth.WORKLOADS[4]
     x = synth.make_inputs(w, DEV)
     kv, _ = _group(x, 4)
     st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
     y = da.decode(x["q1"], x["q2"], kv["k1"], kv["k2"], kv["v"], st)
     torch.cuda.synchronize()
+    y = np64(y)
     ls = orc.lambda_scalar(*(np64(x[k]) for k in ("lq1", "lk1", "lq2", "lk2")), w.layer)
-    for b, hh in [(0, 0), (0, 3), (17, 4), (63, 15), (40, 9)]:
-        kh = hh // 4
-        ref = orc.decode(np64(x["q1"][b:b + 1, hh:hh + 1]), np64(x["q2"][b:b + 1, hh:hh + 1]),
-                         np64(kv["k1"][b:b + 1, kh:kh + 1]), np64(kv["k2"][b:b + 1, kh:kh + 1]),
-                         np64(kv["v"][b:b + 1, kh:kh + 1]), None, ls["lambda"],
+    for b in range(w.batch):
+        s = slice(b, b + 1)
+        ref = orc.decode(np64(x["q1"][s]), np64(x["q2"][s]), np64(kv["k1"][s]),
+                         np64(kv["k2"][s]), np64(kv["v"][s]), None, ls["lambda"],
                          ls["lambda_init"])
-        assert np.max(np.abs(np64(y[b, hh]) - ref[0, 0])) <= BF16_TOL, (b, hh)
+        assert np.max(np.abs(y[s] - ref)) <= BF16_TOL, b
 
 
 @pytest.mark.parametrize("B,N,H,hkv,dm", [(1, 300, 4, 2, 128), (2, 77, 8, 1, 256)])
