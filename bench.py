@@ -228,7 +228,7 @@ def leg_decode(steps, warmup):
         "ms_per_step": ms, "decode_ms": kern_ms, "bytes_per_step": nb,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS,
-                     "traffic": traffic_from_profiles("decode_split_kernel", "decode.hip", w.name)},
+                     "traffic": traffic_from_profiles("decode_mfma_kernel", "decode.hip", w.name)},
         "gqa": {"workload": f"{w.name}, 4 cache heads (groups of 4)", "decode_ms": gq_ms,
                 "bytes_per_step": gq_bytes, "GB_s": gq_bytes / (gq_ms * 1e-3) / 1e9,
                 "frac": gq_bytes / (gq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,

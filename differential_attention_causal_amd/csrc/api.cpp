@@ -94,8 +94,9 @@ diffattn_status check_problem(const diffattn_problem* p, bool* empty) {
 int64_t kv_heads_of(const diffattn_problem* p) { return p->kv_heads > 0 ? p->kv_heads : p->heads; }
 
 size_t decode_ws_bytes(const diffattn_problem* p) {
-  int ns = 0, sl = 0;
-  diffattn::decode_split_geometry(p->batch, p->heads, p->seqlen, &ns, &sl);
+  int gq = 0, ns = 0, sl = 0;
+  diffattn::decode_geometry(p->batch, p->heads, p->heads / kv_heads_of(p), p->seqlen, &gq, &ns,
+                            &sl);
   // per (b, h, split): two maps x (m, l, 2d accumulators)
   return static_cast<size_t>(p->batch) * p->heads * ns * 2 * (2 + 2 * p->head_dim) *
          sizeof(float);
@@ -294,7 +295,7 @@ diffattn_status decode_prepare(const diffattn_problem* p, const void* q1, const 
   a->out = out;
   a->B = p->batch; a->H = p->heads; a->L = p->seqlen;
   a->G = static_cast<int>(p->heads / kv_heads_of(p));
-  diffattn::decode_split_geometry(a->B, a->H, a->L, &a->n_split, &a->split_len);
+  diffattn::decode_geometry(a->B, a->H, a->G, a->L, &a->gq, &a->n_split, &a->split_len);
   a->d = p->head_dim;
   a->eps = p->rms_eps;
   return DIFFATTN_OK;

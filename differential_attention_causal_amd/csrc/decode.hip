@@ -5,20 +5,13 @@
 // maps of the DiffAttn equation (pt.news.hada.io "Como a atencao diferencial funciona").
 // Generating a token re-reads the whole K1/K2/V cache from HBM (priorstack.com, "The
 // Memory Wall: Why the KV Cache Constrains LLM Serving"), so the kernel is a streaming
-// read: every cache byte is loaded exactly once, with 16-byte buffer loads marked
-// non-temporal (policy bit nt: the data is not kept in the caches, which no later load
-// would hit), and no LDS staging.
+// read: every cache byte is loaded once per step, for all the query heads that share it,
+// with loads marked non-temporal (policy bit nt: no later load would hit the caches).
 //
-// Pass 1 (decode_split_kernel), grid = splits x (B*H): a workgroup of 4 wavefronts takes
-// one split of the cache; each wavefront walks 64-key rounds of its share:
-//   * scores: 8 lanes per key, each lane a 16-byte slice of the K1 and K2 rows, so one
-//     wave instruction reads 8 whole rows (1 KiB contiguous); each lane's slice is dotted
-//     with the query by v_dot2_f32_bf16 and the 8 partial sums are added across lanes;
-//   * per map: running max m, normaliser l, and p_j = exp2(s_j log2(e)/sqrt(d) - m);
-//   * values: 16 lanes per V row (16 bytes each), 4 rows per instruction; each lane keeps
-//     8 output channels of both accumulators.
-// The four wavefront states are merged in LDS and written as one partial
-// (m, l, acc[128]) per map and split.
+// Pass 1 (decode_mfma_kernel), grid = splits x (query-head groups): a workgroup of 4
+// wavefronts takes one split of one cache head for up to 32 of the query heads that
+// share it (one, without grouped-query attention), on the matrix cores; it writes one
+// partial (m, l, acc[128]) per query head, map and split.
 // Pass 2 (decode_combine_kernel), grid = B*H: exact log-sum-exp merge of the splits,
 // O = acc1/l1 - lambda acc2/l2, RMSNorm over the 128 channels, x (1 - lambda_init).
 #include "common.h"
@@ -30,197 +23,10 @@ namespace dec {
 constexpr int D = 64;
 constexpr int DV = 128;
 constexpr int NT = 256;
-constexpr int KEYS_PER_ROUND = 64;          // per wavefront
-constexpr int SG = KEYS_PER_ROUND / 8;      // score groups of 8 keys (8 lanes per key)
-constexpr int VI = KEYS_PER_ROUND / 4;      // value loads (16 lanes per row, 4 rows each)
 constexpr int PART = 2 + DV;                // m, l, acc[DV]
 
-__global__ void __launch_bounds__(NT, 2) decode_split_kernel(
-    const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
-    const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
-    const bf16_t* __restrict__ v, const int32_t* __restrict__ cache_len,
-    float* __restrict__ partial, int64_t H, int64_t L, int n_split, int rounds, int G) {
-  __shared__ float red[4][2][PART];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int split = blockIdx.x;
-  const int64_t bh = blockIdx.y;
-  const int64_t b = bh / H;
-  int64_t len = cache_len ? static_cast<int64_t>(cache_len[b]) : L;
-  len = len < 1 ? 1 : (len > L ? L : len);
-  const int64_t split_len = static_cast<int64_t>(KEYS_PER_ROUND) * 4 * rounds;
-  const int64_t s0 = static_cast<int64_t>(split) * split_len;
-  if (s0 >= len) return;  // the combine pass reads only splits that start below len
-
-  // Cache rows through buffer resources bounded at len rows: keys at or beyond len read
-  // as zero, and each load needs only a 32-bit lane offset plus the round's scalar offset.
-  constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer, no swizzle
-  // Cache head of this query head (grouped-query attention: G query heads per cache head).
-  const int64_t kvh = b * (H / G) + (bh - b * H) / G;
-  const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(k1 + kvh * L * D), 0, static_cast<int>(len * D * 2), kBufFlags);
-  const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(k2 + kvh * L * D), 0, static_cast<int>(len * D * 2), kBufFlags);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(v + kvh * L * DV), 0, static_cast<int>(len * DV * 2), kBufFlags);
-
-  // Score lanes: key r = lane / 8 of each group of 8, channel slice c = lane % 8.
-  const int r = lane >> 3, c = lane & 7;
-  // This lane's 8 query channels of each map, as bf16 pairs for v_dot2 (each product of
-  // two bf16 values is exact in float32; the sums are float32).
-  // (Pairs are built element by element from bf16x8 vectors: bit-casting 32-bit lanes of
-  // a u32x4 to bf16x2 here was compiled to feed the same pair to every dot product.)
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q1 + bh * D + 8 * c));
-  const bf16x8 qb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q2 + bh * D + 8 * c));
-  // Value lanes: channel slice e = lane % 16 (channels 8e..8e+7), key phase f = lane / 16.
-  const int e = lane & 15, f = lane >> 4;
-  const int ko = r * D * 2 + 16 * c;    // byte offset of this lane's K slice in a round
-  const int vo = f * DV * 2 + 16 * e;   // byte offset of this lane's V slice in a round
-
-  const float cs = kLog2e / 8.0f;  // log2(e) / sqrt(64)
-  float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
-  float acc1[8], acc2[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) acc1[t] = acc2[t] = 0.f;
-
-#pragma clang loop unroll(disable)
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int64_t kb = s0 + (static_cast<int64_t>(wv) * rounds + rd) * KEYS_PER_ROUND;
-    if (kb >= len) break;
-    const int kbs = __builtin_amdgcn_readfirstlane(static_cast<int>(kb));
-    // ---- scores of the keys kb + 8 g + r
-    u32x4 kx[SG], ky[SG];
-#pragma unroll
-    for (int g = 0; g < SG; ++g) {
-      kx[g] = __builtin_amdgcn_raw_buffer_load_b128(rk1, ko + g * 8 * D * 2, kbs * D * 2, 2);
-      ky[g] = __builtin_amdgcn_raw_buffer_load_b128(rk2, ko + g * 8 * D * 2, kbs * D * 2, 2);
-    }
-    u32x4 vv[VI];
-#pragma unroll
-    for (int i = 0; i < VI; ++i)
-      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * 4 * DV * 2, kbs * DV * 2, 2);
-    float s1[SG], s2[SG];
-#pragma unroll
-    for (int g = 0; g < SG; ++g) {
-      float d1 = 0.f, d2 = 0.f;
-      const bf16x8 ka = __builtin_bit_cast(bf16x8, kx[g]), kc = __builtin_bit_cast(bf16x8, ky[g]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x2 q1p = {qa[2 * t], qa[2 * t + 1]}, k1p = {ka[2 * t], ka[2 * t + 1]};
-        const bf16x2 q2p = {qb[2 * t], qb[2 * t + 1]}, k2p = {kc[2 * t], kc[2 * t + 1]};
-        d1 = __builtin_amdgcn_fdot2_f32_bf16(q1p, k1p, d1, false);
-        d2 = __builtin_amdgcn_fdot2_f32_bf16(q2p, k2p, d2, false);
-      }
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        d1 += __shfl_xor(d1, o);
-        d2 += __shfl_xor(d2, o);
-      }
-      const bool ok = kb + 8 * g + r < len;
-      s1[g] = ok ? d1 * cs : -INFINITY;
-      s2[g] = ok ? d2 * cs : -INFINITY;
-    }
-    float mx1 = s1[0], mx2 = s2[0];
-#pragma unroll
-    for (int g = 1; g < SG; ++g) {
-      mx1 = fmaxf(mx1, s1[g]);
-      mx2 = fmaxf(mx2, s2[g]);
-    }
-#pragma unroll
-    for (int o = 8; o < 64; o <<= 1) {
-      mx1 = fmaxf(mx1, __shfl_xor(mx1, o));
-      mx2 = fmaxf(mx2, __shfl_xor(mx2, o));
-    }
-    const float mn1 = fmaxf(m1, mx1), mn2 = fmaxf(m2, mx2);
-    const float al1 = fast_exp2(m1 - mn1), al2 = fast_exp2(m2 - mn2);
-    float p1[SG], p2[SG], sum1 = 0.f, sum2 = 0.f;
-#pragma unroll
-    for (int g = 0; g < SG; ++g) {
-      p1[g] = fast_exp2(s1[g] - mn1);
-      p2[g] = fast_exp2(s2[g] - mn2);
-      sum1 += p1[g];
-      sum2 += p2[g];
-    }
-#pragma unroll
-    for (int o = 8; o < 64; o <<= 1) {
-      sum1 += __shfl_xor(sum1, o);
-      sum2 += __shfl_xor(sum2, o);
-    }
-    l1 = fmaf(l1, al1, sum1);
-    l2 = fmaf(l2, al2, sum2);
-    m1 = mn1;
-    m2 = mn2;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      acc1[t] *= al1;
-      acc2[t] *= al2;
-    }
-    // ---- values: key 4 i + f, whose weight sits in register i/2 of lanes 8 * (key % 8)
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int src = 32 * (i & 1) + 8 * f;
-      const float w1 = __shfl(p1[i >> 1], src);
-      const float w2 = __shfl(p2[i >> 1], src);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float lo = __uint_as_float(vv[i][t] << 16);
-        const float hi = __uint_as_float(vv[i][t] & 0xffff0000u);
-        acc1[2 * t] = fmaf(w1, lo, acc1[2 * t]);
-        acc1[2 * t + 1] = fmaf(w1, hi, acc1[2 * t + 1]);
-        acc2[2 * t] = fmaf(w2, lo, acc2[2 * t]);
-        acc2[2 * t + 1] = fmaf(w2, hi, acc2[2 * t + 1]);
-      }
-    }
-  }
-  // Sum the four key phases (lanes e, e+16, e+32, e+48 hold the same channels).
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    acc1[t] += __shfl_xor(acc1[t], 16);
-    acc1[t] += __shfl_xor(acc1[t], 32);
-    acc2[t] += __shfl_xor(acc2[t], 16);
-    acc2[t] += __shfl_xor(acc2[t], 32);
-  }
-  if (lane == 0) {
-    red[wv][0][0] = m1;
-    red[wv][0][1] = l1;
-    red[wv][1][0] = m2;
-    red[wv][1][1] = l2;
-  }
-  if (f == 0) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      red[wv][0][2 + 8 * e + t] = acc1[t];
-      red[wv][1][2 + 8 * e + t] = acc2[t];
-    }
-  }
-  __syncthreads();
-  // Merge the 4 wavefront states: thread = (map, channel). Waves with no valid key have
-  // m = -inf and weight 0; wave 0 always has a valid key.
-  float* out = partial + (bh * n_split + split) * 2 * PART;
-  if (tid < 2 * DV) {
-    const int mp = tid / DV, ch = tid % DV;
-    float M = red[0][mp][0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, red[w][mp][0]);
-    float A = 0.f, S = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float sc = fast_exp2(red[w][mp][0] - M);
-      A = fmaf(red[w][mp][2 + ch], sc, A);
-      S = fmaf(red[w][mp][1], sc, S);
-    }
-    out[mp * PART + 2 + ch] = A;
-    if (ch == 0) {
-      out[mp * PART + 0] = M;
-      out[mp * PART + 1] = S;
-    }
-  }
-}
-
-// Grouped-query decode on the matrix cores. The gq query heads that share one cache
-// head are the columns of the B operand of v_mfma_f32_32x32x16_bf16 (32 columns, the
+// Decode on the matrix cores. The gq query heads that share one cache head (gq = 1
+// without grouped-query attention) are the columns of the B operand of v_mfma_f32_32x32x16_bf16 (32 columns, the
 // first gq real, the rest zero), so one pass over a 32-key round of the cache serves all
 // of them:
 //   * S^T = K Q^T per map: 32 keys x 32 query columns. Operand row m holds key
@@ -239,9 +45,8 @@ __global__ void __launch_bounds__(NT, 2) decode_split_kernel(
 // registers first, which frees its buffer for the round after next). The loads are
 // assembly and their waits explicit, so the compiler neither orders LDS reads behind
 // them nor waits for later rounds. No barrier: each wavefront reads only its own
-// buffers. The four wavefronts' states are merged in LDS and written as the same
-// per-(b, h, split) partials as the other decode kernels, so decode_combine_kernel
-// finishes all of them.
+// buffers. The four wavefronts' states are merged in LDS and written as per-(b, h, split)
+// partials for decode_combine_kernel.
 namespace gq {
 constexpr int KPR = 32;                 // keys per wavefront round
 constexpr int KT = KPR * 128;           // a round's K1 (or K2) rows: [32][128 B]
@@ -641,17 +446,21 @@ __global__ void __launch_bounds__(2 * DV) decode_combine_kernel(
 
 }  // namespace dec
 
-void decode_split_geometry(int64_t B, int64_t H, int64_t L, int* n_split, int* split_len) {
-  // Rounds of 64 keys per wavefront, at most 2 per wavefront: many small workgroups, so
-  // that the last partial wave of workgroups leaves little of the chip idle.
-  const int64_t BH = B * H;
-  int rounds = 2;
-  while (rounds > 1) {
-    const int64_t sl = static_cast<int64_t>(dec::KEYS_PER_ROUND) * 4 * rounds;
-    if (BH * ((L + sl - 1) / sl) >= 4096) break;
-    rounds >>= 1;
-  }
-  const int64_t sl = static_cast<int64_t>(dec::KEYS_PER_ROUND) * 4 * rounds;
+void decode_geometry(int64_t B, int64_t H, int64_t G, int64_t L, int* gq, int* n_split,
+                     int* split_len) {
+  // The query heads of a group on the matrix cores, gq at a time: the largest divisor of
+  // the group size up to 32 (the B operand's columns).
+  int c = 1;
+  for (int t = 1; t <= 32 && t <= G; ++t)
+    if (G % t == 0) c = t;
+  const int64_t groups = B * H / c;
+  // 32-key rounds per wavefront, splits of 128 x rounds keys: as long as possible (up to
+  // 8192 keys) while there is a workgroup for every compute unit, since a workgroup fills
+  // its unit's LDS and each one that ends drains the unit's load pipeline; at least 512.
+  int rounds = 64;
+  while (rounds > 4 && groups * ((L + 128 * rounds - 1) / (128 * rounds)) < 256) rounds >>= 1;
+  const int64_t sl = static_cast<int64_t>(dec::gq::KPR) * 4 * rounds;
+  *gq = c;
   *split_len = static_cast<int>(sl);
   *n_split = static_cast<int>((L + sl - 1) / sl);
 }
@@ -659,50 +468,25 @@ void decode_split_geometry(int64_t B, int64_t H, int64_t L, int* n_split, int* s
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   using namespace dec;
   const int64_t BH = a.B * a.H;
-  int n_split = a.n_split;
-  int64_t split_len = a.split_len;
-  if (a.G > 1) {
-    // Grouped-query attention: the query heads of a group on the matrix cores, gq at a
-    // time (the largest divisor of the group size up to 32, the B operand's columns).
-    int gq = 1;
-    for (int c = 1; c <= 32 && c <= a.G; ++c)
-      if (a.G % c == 0) gq = c;
-    const int64_t groups = BH / gq;
-    // 32-key rounds per wavefront, splits of 128 x rounds keys: as long as possible (up to
-    // 8192 keys) while there is a workgroup for every compute unit, since a workgroup
-    // fills its unit's LDS and each one that ends drains the unit's load pipeline; at
-    // least 512 keys, so there are no more splits than the workspace holds partials for.
-    int rounds_g = 64;
-    while (rounds_g > 4 && groups * ((a.L + 128 * rounds_g - 1) / (128 * rounds_g)) < 256)
-      rounds_g >>= 1;
-    split_len = static_cast<int64_t>(gq::KPR) * 4 * rounds_g;
-    n_split = static_cast<int>((a.L + split_len - 1) / split_len);
-    const size_t lds = decode_mfma_lds_bytes(gq);
-    static std::atomic<uint64_t> attr_done{0};
-    const hipError_t ea = once_per_device(attr_done, [] {
-      return hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 static_cast<int>(decode_mfma_lds_bytes(32)));
-    });
-    if (ea != hipSuccess) return ea;
-    hipLaunchKernelGGL(decode_mfma_kernel, dim3(n_split, static_cast<unsigned>(groups)), dim3(NT),
-                       lds, s, static_cast<const bf16_t*>(a.q1), static_cast<const bf16_t*>(a.q2),
-                       static_cast<const bf16_t*>(a.k1), static_cast<const bf16_t*>(a.k2),
-                       static_cast<const bf16_t*>(a.v), a.cache_len, a.partial, a.H, a.L,
-                       n_split, rounds_g, a.G, gq);
-  } else {
-    const int rounds = a.split_len / (KEYS_PER_ROUND * 4);
-    hipLaunchKernelGGL(decode_split_kernel, dim3(a.n_split, static_cast<unsigned>(BH)),
-                       dim3(NT), 0, s, static_cast<const bf16_t*>(a.q1),
-                       static_cast<const bf16_t*>(a.q2), static_cast<const bf16_t*>(a.k1),
-                       static_cast<const bf16_t*>(a.k2), static_cast<const bf16_t*>(a.v),
-                       a.cache_len, a.partial, a.H, a.L, a.n_split, rounds, a.G);
-  }
+  const int gq = a.gq;
+  const int rounds = a.split_len / (gq::KPR * 4);
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t ea = once_per_device(attr_done, [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(decode_mfma_lds_bytes(32)));
+  });
+  if (ea != hipSuccess) return ea;
+  hipLaunchKernelGGL(decode_mfma_kernel, dim3(a.n_split, static_cast<unsigned>(BH / gq)),
+                     dim3(NT), decode_mfma_lds_bytes(gq), s, static_cast<const bf16_t*>(a.q1),
+                     static_cast<const bf16_t*>(a.q2), static_cast<const bf16_t*>(a.k1),
+                     static_cast<const bf16_t*>(a.k2), static_cast<const bf16_t*>(a.v),
+                     a.cache_len, a.partial, a.H, a.L, a.n_split, rounds, a.G, gq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(BH)), dim3(2 * DV), 0, s,
                      a.partial, a.cache_len, a.lam, a.rms_weight, static_cast<bf16_t*>(a.out),
-                     a.H, a.L, n_split, split_len, a.eps);
+                     a.H, a.L, a.n_split, static_cast<int64_t>(a.split_len), a.eps);
   return hipGetLastError();
 }
 

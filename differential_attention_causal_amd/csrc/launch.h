@@ -52,6 +52,7 @@ struct DecodeArgs {
   float* partial;            // workspace
   int64_t B, H, L;
   int G;                     // query heads per cache head (caches have H / G heads)
+  int gq;                    // query heads per workgroup (divides G)
   int n_split, split_len;
   int d;
   float eps;
@@ -117,8 +118,10 @@ hipError_t launch_cache_append_bf16(const AppendArgs& a, hipStream_t s);
 // Device address of the static decode scratch (DIFFATTN_DECODE_SCRATCH_BYTES) on the
 // current device, looked up once per device.
 hipError_t decode_scratch(float** out);
-// Decode split geometry shared by the workspace query and the launcher.
-void decode_split_geometry(int64_t B, int64_t H, int64_t L, int* n_split, int* split_len);
+// Decode geometry shared by the workspace query and the launcher: query heads per
+// workgroup, and the splits of the cache.
+void decode_geometry(int64_t B, int64_t H, int64_t G, int64_t L, int* gq, int* n_split,
+                     int* split_len);
 // Backward workspace floats.
 size_t bwd_workspace_floats(int64_t B, int64_t H, int64_t N, int d);
 

@@ -126,7 +126,7 @@ int main() {
   EXPECT(dec(&pd, dq, nullptr, dneed), DIFFATTN_E_WORKSPACE);
   EXPECT(dec(&pd, dq, addr(64 * 40), dneed - 4), DIFFATTN_E_WORKSPACE);
   { void* y[9]; std::memcpy(y, dq, sizeof(y)); y[8] = dq[2]; EXPECT(dec(&pd, y, addr(64 * 40), dneed), DIFFATTN_E_ARG); }
-  { diffattn_problem big = prob(64, 16, int64_t(1) << 16, 64, DIFFATTN_BF16);
+  { diffattn_problem big = prob(64, 16, int64_t(1) << 20, 64, DIFFATTN_BF16);
     EXPECT(dna(&big, dq), DIFFATTN_E_SCRATCH); }
   { void* y[9]; std::memcpy(y, dq, sizeof(y)); y[0] = nullptr; EXPECT(dna(&pd, y), DIFFATTN_E_ARG); }
 

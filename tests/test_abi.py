@@ -205,7 +205,7 @@ def test_decode_noalloc_argument_checks():
     lib = da.lib()
     ptrs = [addr(i * 64) for i in range(9)]   # q1 q2 k1 k2 v len lam w out
     call = lambda p, ptrs: lib.diffattn_decode_noalloc(ctypes.byref(p), *ptrs, None)
-    big = da.problem(64, 16, 1 << 16, 64, da.BF16)
+    big = da.problem(64, 16, 1 << 20, 64, da.BF16)
     assert da.workspace_bytes(da.OP_DECODE, big) > da.DECODE_SCRATCH_BYTES
     assert call(big, ptrs) == da.E_SCRATCH
     fits = da.problem(64, 16, 8192, 64, da.BF16)
