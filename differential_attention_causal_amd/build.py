@@ -2,6 +2,9 @@
 
 Every HIP translation unit under csrc/ is compiled to an object file in
 ``_build/`` (in parallel) and linked into ``libdiffattn.so`` next to this file.
+``build(debug=True)`` builds the same sources with DIFFATTN_DEBUG_BARRIERS (an extra
+workgroup barrier at every step of the kernels' main loops) into ``_build/debug/`` and
+``libdiffattn_debug.so``; its results must equal the normal build's bit for bit.
 """
 from __future__ import annotations
 
@@ -17,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
+LIB_DEBUG = os.path.join(PKG, "libdiffattn_debug.so")
+# Marker ranges around the entry points (rocprofiler-sdk's roctx).
+LINK_LIBS = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
 
 SOURCES = ["api.cpp", "lambda.hip", "fwd_fp32.hip", "fwd_bf16.hip", "decode.hip", "bwd.hip",
            "append.hip", "gemm.hip", "scratch.hip"]
@@ -44,8 +50,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: install ROCm or set HIPCC")
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra, outdir: str) -> str:
+    obj = os.path.join(outdir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     cmd = [hipcc()] + HIPCC_FLAGS + FILE_FLAGS.get(src, []) + list(extra) + \
         ["-I", INCLUDE, "-I", CSRC] + lang + \
@@ -60,19 +66,25 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=()) -> str:
-    """Compile every source and link libdiffattn.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(extra_flags=(), debug: bool = False) -> str:
+    """Compile every source and link libdiffattn.so (or, with debug, the debug-barrier
+    build libdiffattn_debug.so); returns the library path."""
+    outdir = os.path.join(BUILD, "debug") if debug else BUILD
+    lib = LIB_DEBUG if debug else LIB
+    flags = list(extra_flags) + (["-DDIFFATTN_DEBUG_BARRIERS"] if debug else [])
+    os.makedirs(outdir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, flags, outdir), SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + LINK_LIBS
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(sys.argv[1:]))
+    args = sys.argv[1:]
+    debug = "--debug" in args
+    print(build([a for a in args if a != "--debug"], debug=debug))

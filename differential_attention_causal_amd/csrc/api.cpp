@@ -13,6 +13,7 @@
 #include <cmath>
 
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include "diffattn.h"
 #include "launch.h"
@@ -29,6 +30,27 @@ bool env_log() {
   }();
   return on;
 }
+
+// One marker range per entry-point call, named after the entry point (shown by
+// rocprofv3 --marker-trace; a no-op when no tool is attached). With DIFFATTN_LOG=1 the
+// call and its problem shape are also written to stderr.
+struct CallRange {
+  CallRange(const char* name, const diffattn_problem* p) {
+    roctxRangePushA(name);
+    if (!env_log()) return;
+    if (p) {
+      fprintf(stderr, "[diffattn] %s B=%lld H=%lld N=%lld d=%d kv_heads=%lld dtype=%d\n", name,
+              static_cast<long long>(p->batch), static_cast<long long>(p->heads),
+              static_cast<long long>(p->seqlen), p->head_dim,
+              static_cast<long long>(p->kv_heads), static_cast<int>(p->dtype));
+    } else {
+      fprintf(stderr, "[diffattn] %s\n", name);
+    }
+  }
+  ~CallRange() { roctxRangePop(); }
+  CallRange(const CallRange&) = delete;
+  CallRange& operator=(const CallRange&) = delete;
+};
 
 diffattn_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return DIFFATTN_OK;
@@ -140,6 +162,7 @@ size_t diffattn_workspace_bytes(diffattn_op op, const diffattn_problem* p) {
 diffattn_status diffattn_lambda(int32_t dim, int32_t layer_idx, const float* lq1,
                                 const float* lk1, const float* lq2, const float* lk2,
                                 diffattn_lambda_state* state_out, void* stream) {
+  const CallRange range("diffattn_lambda", nullptr);
   if (dim < 1 || dim > 1024 || layer_idx < 1) return DIFFATTN_E_ARG;
   if (!lq1 || !lk1 || !lq2 || !lk2 || !state_out) return DIFFATTN_E_ARG;
   if (!aligned(lq1, 4) || !aligned(lk1, 4) || !aligned(lq2, 4) || !aligned(lk2, 4) ||
@@ -159,6 +182,7 @@ diffattn_status diffattn_lambda_layers(int32_t dim, int32_t n_layers, int32_t fi
                                        const float* lq1, const float* lk1, const float* lq2,
                                        const float* lk2, diffattn_lambda_state* states_out,
                                        void* stream) {
+  const CallRange range("diffattn_lambda_layers", nullptr);
   if (dim < 1 || dim > 1024 || n_layers < 0 || n_layers > 65535 || first_layer < 1)
     return DIFFATTN_E_ARG;
   if (first_layer > INT32_MAX - n_layers) return DIFFATTN_E_ARG;
@@ -185,6 +209,7 @@ diffattn_status diffattn_fwd(const diffattn_problem* p, const void* q1, const vo
                              const diffattn_lambda_state* lam, const float* rms_weight,
                              void* out, const diffattn_saved* saved, void* workspace,
                              size_t workspace_bytes, void* stream) {
+  const CallRange range("diffattn_fwd", p);
   bool empty = false;
   diffattn_status st = check_problem(p, &empty);
   if (st != DIFFATTN_OK) return st;
@@ -310,6 +335,7 @@ diffattn_status diffattn_decode(const diffattn_problem* p, const void* q1, const
                                 const int32_t* cache_len, const diffattn_lambda_state* lam,
                                 const float* rms_weight, void* out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
+  const CallRange range("diffattn_decode", p);
   diffattn::DecodeArgs a;
   size_t need = 0;
   bool empty = false;
@@ -331,6 +357,7 @@ diffattn_status diffattn_decode_noalloc(const diffattn_problem* p, const void* q
                                         const void* vc, const int32_t* cache_len,
                                         const diffattn_lambda_state* lam,
                                         const float* rms_weight, void* out, void* stream) {
+  const CallRange range("diffattn_decode_noalloc", p);
   diffattn::DecodeArgs a;
   size_t need = 0;
   bool empty = false;
@@ -353,6 +380,7 @@ diffattn_status diffattn_decode_noalloc(const diffattn_problem* p, const void* q
 diffattn_status diffattn_cache_append(const diffattn_problem* p, const void* k1_new,
                                       const void* k2_new, const void* v_new, void* k1c,
                                       void* k2c, void* vc, int32_t* cache_len, void* stream) {
+  const CallRange range("diffattn_cache_append", p);
   bool empty = false;
   diffattn_status st = check_problem(p, &empty);
   if (st != DIFFATTN_OK) return st;
@@ -403,6 +431,7 @@ diffattn_status check_proj(const diffattn_problem* p, int64_t d_model, bool* emp
 diffattn_status diffattn_qkv_proj(const diffattn_problem* p, int64_t d_model, const void* x,
                                   const void* w_qkv, void* q1, void* q2, void* k1, void* k2,
                                   void* v, void* stream) {
+  const CallRange range("diffattn_qkv_proj", p);
   bool empty = false;
   diffattn_status st = check_proj(p, d_model, &empty);
   if (st != DIFFATTN_OK) return st;
@@ -429,6 +458,7 @@ diffattn_status diffattn_qkv_proj(const diffattn_problem* p, int64_t d_model, co
 
 diffattn_status diffattn_out_proj(const diffattn_problem* p, int64_t d_model, const void* attn,
                                   const void* w_o, void* y, void* stream) {
+  const CallRange range("diffattn_out_proj", p);
   bool empty = false;
   diffattn_status st = check_proj(p, d_model, &empty);
   if (st != DIFFATTN_OK) return st;
@@ -457,6 +487,7 @@ diffattn_status diffattn_bwd(const diffattn_problem* p, const void* q1, const vo
                              float* dlq1, float* dlk1, float* dlq2, float* dlk2,
                              float* d_rms_weight, void* workspace, size_t workspace_bytes,
                              void* stream) {
+  const CallRange range("diffattn_bwd", p);
   bool empty = false;
   diffattn_status st = check_problem(p, &empty);
   if (st != DIFFATTN_OK) return st;

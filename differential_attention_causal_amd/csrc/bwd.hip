@@ -771,6 +771,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
   // its barrier, which also frees tile T-1's slot for tile T+3). Sub-tiles 0..3 (the
   // first two tiles) hold the causal diagonal band of this block's keys.
   auto trip = [&](auto masked, int T) __attribute__((always_inline)) {
+    DIFFATTN_DEBUG_BARRIER();   // every wave runs the same trips
     half(masked, Int<0>{}, 2 * T);
     if (T + 1 < nT) {
       kv_tile_barrier(T + 2 < nT, wv == 0);
@@ -1108,6 +1109,7 @@ __global__ void __launch_bounds__(NTQ, 1) bwd_dq_kernel(
 
   // Trips as for dK/dV; the causal band (keys q0 .. q0 + 255) is in the last four tiles.
   auto trip = [&](auto masked, int T) __attribute__((always_inline)) {
+    DIFFATTN_DEBUG_BARRIER();   // every wave runs the same trips
     half(masked, Int<0>{}, 2 * T);
     if (T + 1 < nT) {
       q_tile_barrier(T + 2 < nT);

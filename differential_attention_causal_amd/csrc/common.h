@@ -16,6 +16,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Builds with DIFFATTN_DEBUG_BARRIERS put a full workgroup barrier (with its waits for
+// outstanding memory operations) at every step of the kernels' main loops, at points that
+// every wavefront of a workgroup reaches equally often. Results must not change: a
+// difference from the normal build is a race between wavefronts.
+#ifdef DIFFATTN_DEBUG_BARRIERS
+#define DIFFATTN_DEBUG_BARRIER() __syncthreads()
+#else
+#define DIFFATTN_DEBUG_BARRIER() \
+  do {                            \
+  } while (0)
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

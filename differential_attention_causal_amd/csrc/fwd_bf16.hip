@@ -641,6 +641,7 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   };
 
   auto step = [&](int j, auto masked, auto check) __attribute__((always_inline)) {
+    DIFFATTN_DEBUG_BARRIER();   // every wave runs the same sub-tiles
     // X(j): acc2 += V^T(j-1) P2(j-1); S2(j); softmax of S1(j) -> P1.
     half(masked, Flag<true>{}, check, j, acc2, P2, S2, qf2, j, S1, qf1, st1, P1, acc1);
     // Y(j): acc1 += V^T(j) P1(j); S1(j+1); softmax of S2(j) -> P2.

@@ -198,6 +198,7 @@ __global__ void __launch_bounds__(NT, 1)
   bf16x8 fa[2][4], fb[2][4];
   read_ops(fa[0], fb[0], lds0, 0);
   for (int kt = 0; kt < KT; ++kt) {
+    DIFFATTN_DEBUG_BARRIER();   // every wave runs the same K-steps
     const uint32_t cur = lds0 + (kt & 1) * STAGE;
     read_ops(fa[1], fb[1], cur, 1);
     products(fa[0], fb[0], 0, 16);

@@ -329,3 +329,25 @@ def test_grouped_query_argument_checks():
     st = lib.diffattn_bwd(ctypes.byref(p), *args[:11], ctypes.byref(sv), *args[11:23], ws,
                           1 << 30, None)
     assert st == da.E_ARG
+
+
+def test_call_logging_with_diffattn_log(tmp_path):
+    """DIFFATTN_LOG=1 writes one line per entry-point call, with the problem shape, to
+    stderr (here for calls the argument checks reject, so no GPU is touched)."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes\n"
+        "from differential_attention_causal_amd import diffattn as da\n"
+        "lib = da.lib()\n"
+        "p = da.problem(2, 3, 17, 64, da.BF16)\n"
+        "r = lib.diffattn_fwd(ctypes.byref(p), *([None] * 10), 0, None)\n"
+        "assert r == da.E_ARG, r\n"
+        "r = lib.diffattn_lambda(64, 1, *([None] * 6))\n"
+        "assert r == da.E_ARG, r\n")
+    env = dict(os.environ, DIFFATTN_LOG="1", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=ROOT, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "[diffattn] diffattn_fwd B=2 H=3 N=17 d=64 kv_heads=0 dtype=1" in r.stderr, r.stderr
+    assert "[diffattn] diffattn_lambda\n" in r.stderr, r.stderr

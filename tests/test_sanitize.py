@@ -44,7 +44,8 @@ def test_abi_validation_under_asan_and_ubsan(tmp_path):
                            capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
     r = subprocess.run(["g++"] + san + [drv_o, api_o] + objs +
-                       ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", exe],
+                       ["-L/opt/rocm/lib", "-lamdhip64", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib",
+                        "-o", exe],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
