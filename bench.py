@@ -417,6 +417,11 @@ def cpu_baseline():
     cores = len(os.sched_getaffinity(0))
     entries = []
 
+    def add(e):
+        entries.append(e)
+        print(f"[bench] cpu_baseline config {e['config']}: {e['wall_s']:.1f} s", file=sys.stderr,
+              flush=True)
+
     def host(t):
         return t.float().cpu().double().numpy()
 
@@ -459,11 +464,11 @@ def cpu_baseline():
         orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"], ls["lambda_init"])
         el = time.perf_counter() - t0
         flop = 12.0 * w.head_dim * w.seqlen * (w.seqlen + 1) / 2 * w.batch * w.heads
-        entries.append({"config": 1, "workload": w.name, "sample": "whole workload",
+        add({"config": 1, "workload": w.name, "sample": "whole workload",
                         "wall_s": el, "gflops": flop / el / 1e9, "full_s": el,
                         "flop_convention": "12 d P per head"})
-        entries.append(heads_forward(2, 4))
-        entries.append(heads_forward(3, 1))
+        add(heads_forward(2, 4))
+        add(heads_forward(3, 1))
         # 4: whole sequences of the decode step
         w = synth.WORKLOADS[4]
         x = synth.make_inputs(w, "cuda:0")
@@ -478,17 +483,22 @@ def cpu_baseline():
         el = time.perf_counter() - t0
         del x
         by = decode_bytes(w) * n_seq / w.batch
-        entries.append({"config": 4, "workload": w.name,
+        add({"config": 4, "workload": w.name,
                         "sample": f"{n_seq} of {w.batch} sequences (16 heads each)",
                         "wall_s": el, "gb_s": by / el / 1e9, "full_s": el * w.batch / n_seq,
                         "bytes_convention": "cache + query + output bytes"})
-        entries.append(heads_forward(5, 2, backward=True))
+        add(heads_forward(5, 2, backward=True))
     head = next(e for e in entries if e["config"] == 3)
     return {"value": head["gflops"] / 1e3, "unit": "TFLOP/s", "cores": cores,
             "blas_threads": cores, "kind": "oracle",
             "sample": "float64 oracle, blocked head_forward over one whole head (N = 32768) "
                       "of the long-context workload; per_config has every workload",
             "per_config": entries}
+
+
+def _progress(msg: str, t0: float) -> None:
+    """One line on stderr as each leg ends (the JSON record stays the only stdout line)."""
+    print(f"[bench] {msg} ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
 
 
 def main():
@@ -509,7 +519,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     legs = set(args.legs.split(","))
+    t0 = time.perf_counter()
     w, fwd = leg_forward(args.steps, args.warmup)
+    _progress("forward", t0)
     rec = {
         "metric": METRIC, "value": fwd["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": fwd["ms_per_step"],
@@ -529,22 +541,30 @@ def main():
         wp, pf = leg_forward(args.steps, args.warmup, number=2)
         rec["prefill"] = {"workload": wp.name, "fwd_kernel_ms": pf["fwd_kernel_ms"],
                           "tflops": pf["roofline"]["achieved"], "frac": pf["roofline"]["frac"]}
+        _progress("prefill", t0)
     if "peaked" in legs:
         rec["peaked"] = leg_peaked(args.steps, args.warmup)
         rec["peaked"]["time_vs_normal_inputs"] = rec["peaked"]["fwd_kernel_ms"] / fwd["fwd_kernel_ms"]
+        _progress("peaked", t0)
     if "decode" in legs:
         rec["decode"] = leg_decode(args.steps, args.warmup)
+        _progress("decode", t0)
     if "train" in legs:
         rec["train"] = leg_train(max(1, args.steps // 2), args.warmup)
+        _progress("train", t0)
     if "proj" in legs:
         rec["proj"] = leg_proj(args.steps, args.warmup)
+        _progress("proj", t0)
     if "refgemm" in legs:
         rec["ref_gemm"] = leg_ref_gemm(args.steps, args.warmup)
         rec["ref_gemm"]["fwd_frac_of_it"] = fwd["roofline"]["achieved"] / rec["ref_gemm"]["tflops"]
+        _progress("refgemm", t0)
     if "copy" in legs:
         rec["copy"] = leg_copy(args.steps, args.warmup)
+        _progress("copy", t0)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
+        _progress("cpu_baseline", t0)
     print(json.dumps(rec))
 
 
