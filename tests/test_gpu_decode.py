@@ -65,8 +65,8 @@ def test_decode_workload():
 
 
 def test_decode_maximum_cache_length():
-    """Cache capacity 2^22 (the largest supported; 16384 splits for one sequence and head,
-    so the merge reads its partials in many batches), full and ragged lengths."""
+    """Cache capacity 2^22 (the largest supported; 8192 splits of 512 keys for one sequence
+    and head, so the merge reads its partials in many batches), full and ragged lengths."""
     n = 1 << 22
     w = synth.custom("decode", 2, 1, n, 64, 8, "bf16", number=660)
     x = synth.make_inputs(w, DEV)
