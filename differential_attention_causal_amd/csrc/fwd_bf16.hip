@@ -730,10 +730,16 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   // O = acc1 / l1 - lambda acc2 / l2 is formed once and kept in vector registers, which
   // the loop no longer needs; Y = O times one per-row factor (1 - lambda_init) rstd,
   // times w when given.
+  // The fast pass stages its Y rows in LDS and stores them as whole rows. Each wave has
+  // 16 KiB there (64 rows of 256 B) in the two ring slots after the last tile's slot: once
+  // a wave has passed the last tile barrier, every wave is past its last read of any slot
+  // but the last tile's, and no tile load is in flight.
+  const int stage = lds_base + ((n_tiles + (wv >> 1)) % NSLOT) * SLOT + (wv & 1) * (64 * DV * 2);
   const float lam = lamst->lambda_f;
   const float gsc = lamst->one_minus_init_f;
   const int hh = bh % H;
   auto epilogue = [&](auto only_bad) __attribute__((always_inline)) {
+  constexpr bool STAGED = !decltype(only_bad)::value;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const bool row_bad = (bad[g] | static_cast<uint32_t>(__shfl_xor(static_cast<int>(bad[g]), 32))) != 0;
@@ -761,11 +767,31 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     const float rstd = 1.0f / sqrtf(sst * (1.0f / DV) + eps);
     const float sc = gsc * rstd;
     const int qr = q0 + 8 * m + 2 * wv + g;
-    if (qr < N && (!decltype(only_bad)::value || row_bad)) {
+    if constexpr (STAGED) {
+      // Row 2 m + g of the wave's staging area; its 16-byte unit u (channels 8 u .. 8 u + 7)
+      // sits at u ^ (m % 16), so the 32 rows one write touches spread over the banks.
+      const int sr = stage + (2 * m + g) * (DV * 2) + 8 * h;
+      const float* W = rms_w ? rms_w + hh * DV + 4 * h : nullptr;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int b = i >> 2, jg = i & 3;
+        const float* x = o + 16 * b + 4 * jg;
+        f32x4 y = {sc * x[0], sc * x[1], sc * x[2], sc * x[3]};
+        if (W) {
+          const f32x4 wv4 = *reinterpret_cast<const f32x4*>(W + 8 * i);
+          y = f32x4{sc * (wv4[0] * x[0]), sc * (wv4[1] * x[1]), sc * (wv4[2] * x[2]),
+                    sc * (wv4[3] * x[3])};
+        }
+        const u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        *reinterpret_cast<LDS_AS u32x2*>((LDS_AS char*)nullptr + sr + 16 * ((4 * b + jg) ^ (m & 15))) = pk;
+      }
+    }
+    if (qr < N && (STAGED || row_bad)) {
       // Y row of (b, h, qr): [B, H, N, 2d], or [B, N, H, 2d] with out_bnh.
       const int64_t yrow = out_bnh ? (static_cast<int64_t>(bh / H) * N + qr) * H + hh : hoff + qr;
       bf16_t* Y = out + yrow * DV + 4 * h;
-      if (rms_w) {
+      if (STAGED) {
+      } else if (rms_w) {
         const float* W = rms_w + hh * DV + 4 * h;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -806,6 +832,20 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
           sv_lse2[hoff + qr] = (st2[g].m + __log2f(l2)) * kLn2;
           sv_rstd[hoff + qr] = rstd;
         }
+      }
+    }
+  }
+  if constexpr (STAGED) {
+    // The wave's 64 rows as whole rows: 4 rows of 256 B per instruction, 16 B per lane.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 4 * i + (lane >> 4), c = lane & 15;
+      const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(
+          (LDS_AS char*)nullptr + stage + r * (DV * 2) + 16 * (c ^ ((r >> 1) & 15)));
+      const int qr = q0 + 8 * (r >> 1) + 2 * wv + (r & 1);
+      if (qr < N) {
+        const int64_t yrow = out_bnh ? (static_cast<int64_t>(bh / H) * N + qr) * H + hh : hoff + qr;
+        *reinterpret_cast<u32x4*>(out + yrow * DV + 8 * c) = v;
       }
     }
   }
