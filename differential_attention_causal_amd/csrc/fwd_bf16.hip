@@ -355,6 +355,37 @@ __device__ __forceinline__ void s_guard(f32x16 (&S)[2]) {
   asm volatile("s_nop 7\n\ts_nop 4" : "+v"(S[0]), "+v"(S[1]));
 }
 
+// Orders the consumers of S after its products without waiting (the products are known
+// to be complete).
+__device__ __forceinline__ void s_anchor(f32x16 (&S)[2]) {
+  asm volatile("" : "+v"(S[0]), "+v"(S[1]));
+}
+
+// Product order of a half-step's 24 slots: 16 accumulator products and 8 score products.
+// The score products sit in the middle (X: slots 8..15; Y: the even slots 6..20), so the
+// next half-step reads their results without wait states; they start 4 slots or more
+// after their K operands are read (slot 2). qk_slot: the score product at slot k
+// (kb = q / 2, group q % 2), or -1; pv_index: the accumulator product at slot k, in issue
+// order (k-step t = pv / 8).
+template <bool IS_X>
+__host__ __device__ constexpr int qk_slot(int k) {
+  if (IS_X) return (k >= 8 && k < 16) ? k - 8 : -1;
+  return (k >= 6 && k <= 20 && (k & 1) == 0) ? (k - 6) / 2 : -1;
+}
+// X half-steps refill V^T region b of k-step t behind the slot of the last accumulator
+// product that reads it: t = 0 behind slots 8..11 (its products are slots 0..7), t = 1
+// behind slots 18, 20, 22 and 23 (its products are slots 16..23, two per region).
+__host__ __device__ constexpr int vt_read_slot(int t, int b) {
+  return t == 0 ? 8 + b : (b < 3 ? 18 + 2 * b : 23);
+}
+template <bool IS_X>
+__host__ __device__ constexpr int pv_index(int k) {
+  int n = 0;
+  for (int i = 0; i < k; ++i) n += qk_slot<IS_X>(i) < 0 ? 1 : 0;
+  return n;
+}
+static_assert(pv_index<false>(24) == 16 && pv_index<true>(24) == 16, "16 accumulator products");
+
 // O^T += V^T P^T for one map, both groups and one k-step (8 MFMAs sharing the V^T
 // operands).
 __device__ __forceinline__ void pv(f32x16 (&acc)[2][4], const VtHalf& vt,
@@ -501,8 +532,9 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     for (int g = 0; g < 2; ++g) bad[g] = (f[2 * wv + g] >> m) & 1u;
   }
 
-  // One half-step, in a fixed order: 24 products (16 accumulator products acc += V^T P^T,
-  // then 8 score products S_next = K Q^T), each followed by a slice of the softmax of
+  // One half-step, in a fixed order: 24 products (16 accumulator products acc += V^T P^T
+  // and 8 score products S_next = K Q^T in the middle, see qk_slot), each followed by a
+  // slice of the softmax of
   // S_cur (sub-tile j, for accumulator acc_cur), software-pipelined over pairs of scores
   // started every 1.25 slots: fma (scale, subtract m), one exp2, the other exp2, pack to
   // bf16, row sum. At most two transcendentals fall behind one product, and no v_dot2
@@ -539,18 +571,22 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     bool slow = false;
     auto slot = [&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
-      // ---- the k-th product
-      if constexpr (k < 16) {
-        constexpr int t = k >> 3, b = (k & 7) >> 1, g = k & 1;
+      // ---- the k-th product (score product q or accumulator product pv, see qk_slot)
+      constexpr int q = qk_slot<IS_X>(k);
+      if constexpr (q < 0) {
+        constexpr int pv = pv_index<IS_X>(k);
+        constexpr int t = pv >> 3, b = (pv & 7) >> 1, g = pv & 1;
         acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_operand(vt[t], b), Pin[g][t],
                                                              acc[g][b], 0, 0, 0);
       } else {
-        constexpr int kb = (k - 16) >> 1, g = k & 1;
+        constexpr int kb = q >> 1, g = q & 1;
         qk_one(S_next[g], k_operand(kop, kb), qf[g][kb], kb == 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- work placed behind it
-      if constexpr (k == 0) s_guard(S_cur);
+      // S_cur came from the previous half-step's score products, the last of them 3 or
+      // more slots before that half-step ended: more than the result latency.
+      if constexpr (k == 0) s_anchor(S_cur);
       if constexpr (k == 2) k_issue<KN_OFF>(kop, ka, k_off(k_sub));
       static_for<0, 16>([&](auto pc) __attribute__((always_inline)) {
         constexpr int pr = decltype(pc)::value;
@@ -583,10 +619,13 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
         }
       });
       // V^T(j) for Y(j) and X(j + 1): two transposing reads per slot (they do not overlap
-      // the matrix core well when bunched).
-      if constexpr (IS_X && k >= 16) {
-        constexpr int t = (k - 16) >> 2, b = (k - 16) & 3;
-        vt_issue_b<b, t>(vt[t], va + v_off(j));
+      // the matrix core well when bunched), each behind the last accumulator product that
+      // reads the registers it refills (vt_read_slot).
+      if constexpr (IS_X) {
+        static_for<0, 8>([&](auto ic) __attribute__((always_inline)) {
+          constexpr int t = decltype(ic)::value >> 2, b = decltype(ic)::value & 3;
+          if constexpr (k == vt_read_slot(t, b)) vt_issue_b<b, t>(vt[t], va + v_off(j));
+        });
       }
       __builtin_amdgcn_sched_barrier(0);
     };
