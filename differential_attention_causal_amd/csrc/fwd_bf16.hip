@@ -18,7 +18,9 @@
 // Work decomposition: one workgroup = 4 wavefronts = 256 query rows of one (b, h), one
 // workgroup per CU and one wavefront per SIMD. A wavefront owns 64 query rows as two
 // groups of 32; its four accumulators (2 maps x 2 groups, 128 x 32 fp32 each) live in
-// the accumulation registers, everything else in the vector registers.
+// the accumulation registers, everything else in the vector registers. When the blocks
+// are few (short sequences), a workgroup takes 128 rows instead, one group of 32 per
+// wavefront, which halves the longest key walk of a wavefront.
 //  * Transposed score tiles S^T = K Q^T (32 keys x 32 queries per group) with
 //    v_mfma_f32_32x32x16_bf16: each lane holds 16 scores of one query of each group, and
 //    the key rows fed to the MFMA are permuted (bits 2 and 3 swapped) so that the score
@@ -33,10 +35,11 @@
 //            VALU  softmax of S2(j) -> P2(j)
 //    A map's rescale (when its running max moved) happens between its half-steps, after
 //    the last product into that accumulator and before the next.
-//  * Query rows are dealt to lanes with stride 8 (row 8 m + 2 w + g of the workgroup's
-//    256 for lane column m, wavefront w, group g), so every wavefront and group sees the
-//    same key range: sub-tiles below the workgroup's first row run without mask code and
-//    the 8 sub-tiles of the diagonal block apply the integer predicate key <= query.
+//  * Query rows are dealt to lanes with stride 4 NG (row 4 NG m + NG w + g of the
+//    workgroup's for lane column m, wavefront w, group g), so every wavefront and group
+//    sees the same key range: sub-tiles below the workgroup's first row run without mask
+//    code and the 4 NG sub-tiles of the diagonal block apply the integer predicate
+//    key <= query.
 //  * K1, K2 and V tiles of 64 keys go from HBM straight into LDS (buffer loads with the
 //    LDS as destination) in a ring of 4 slots, two tiles ahead, one barrier per tile.
 //    Rows at or beyond N read as zero. V^T comes out of the row-major V tile with the
@@ -61,7 +64,7 @@ constexpr int D = 64;
 constexpr int DV = 128;
 constexpr int NW = 4;          // wavefronts per workgroup (one per SIMD)
 constexpr int NT = 64 * NW;    // threads per workgroup
-constexpr int BR = 64 * NW;    // query rows per workgroup
+constexpr int BR = 64 * NW;    // query rows per workgroup with two query groups per wave
 constexpr int BC = 64;         // keys per LDS tile
 constexpr int NSLOT = 4;       // LDS ring depth (tiles)
 
@@ -323,20 +326,23 @@ __device__ __forceinline__ void settle_row(const f32x16& s, float c, RowState& s
   }
 }
 
-// S^T = K Q^T for one map and both groups (8 MFMAs sharing the K operands). The score
-// products are written as assembly so that their results stay in vector registers while
-// the accumulator products (compiler-visible, below) keep theirs in the accumulation
-// registers. Their consumers are fenced by s_guard. Destinations are early-clobber
-// outputs: a product may not overwrite its own operands.
-__device__ __forceinline__ void qk(f32x16 (&S)[2], const KOps& k, const bf16x8 (&q)[2][4]) {
+// S^T = K Q^T for one map and the NG query groups of a wave (4 NG MFMAs sharing the K
+// operands). The score products are written as assembly so that their results stay in
+// vector registers while the accumulator products (compiler-visible, below) keep theirs
+// in the accumulation registers. Their consumers are fenced by s_guard. Destinations are
+// early-clobber outputs: a product may not overwrite its own operands.
+template <int NG>
+__device__ __forceinline__ void qk(f32x16 (&S)[NG], const KOps& k, const bf16x8 (&q)[NG][4]) {
   const bf16x8 a0 = k_operand(k, 0);
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S[0]) : "v"(a0), "v"(q[0][0]));
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S[1]) : "v"(a0), "v"(q[1][0]));
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S[g]) : "v"(a0), "v"(q[g][0]));
 #pragma unroll
   for (int kb = 1; kb < 4; ++kb) {
     const bf16x8 a = k_operand(k, kb);
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S[0]) : "v"(a), "v"(q[0][kb]));
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S[1]) : "v"(a), "v"(q[1][kb]));
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S[g]) : "v"(a), "v"(q[g][kb]));
   }
 }
 // One score product; FIRST starts the accumulation from zero. The destination must not
@@ -354,68 +360,62 @@ __device__ __forceinline__ void qk_one(f32x16& S, const bf16x8& a, const bf16x8&
 __device__ __forceinline__ void s_guard(f32x16 (&S)[2]) {
   asm volatile("s_nop 7\n\ts_nop 4" : "+v"(S[0]), "+v"(S[1]));
 }
-
+__device__ __forceinline__ void s_guard(f32x16 (&S)[1]) {
+  asm volatile("s_nop 7\n\ts_nop 4" : "+v"(S[0]));
+}
 // Orders the consumers of S after its products without waiting (the products are known
 // to be complete).
 __device__ __forceinline__ void s_anchor(f32x16 (&S)[2]) {
   asm volatile("" : "+v"(S[0]), "+v"(S[1]));
 }
 
-// Product order of a half-step's 24 slots: 16 accumulator products and 8 score products.
-// The score products sit in the middle (X: slots 8..15; Y: the even slots 6..20), so the
-// next half-step reads their results without wait states; they start 4 slots or more
-// after their K operands are read (slot 2). qk_slot: the score product at slot k
-// (kb = q / 2, group q % 2), or -1; pv_index: the accumulator product at slot k, in issue
-// order (k-step t = pv / 8).
-template <bool IS_X>
+// Product order of a half-step's 12 NG slots: 8 NG accumulator products and 4 NG score
+// products. With two query groups (NG = 2) the score products sit in the middle (X: slots
+// 8..15; Y: the even slots 6..20), so the next half-step reads their results without
+// wait states; they start 4 slots or more after their K operands are read (slot 2). With
+// one group (NG = 1) they take the even slots 4..10, one accumulator product between two
+// of them (each depends on the one before), and the next half-step waits for them
+// (s_guard). qk_slot: the score product at slot k (kb = q / NG, group q % NG), or -1;
+// pv_index: the accumulator product at slot k, in issue order (k-step t = pv / (4 NG),
+// region (pv % (4 NG)) / NG, group pv % NG).
+template <int NG, bool IS_X>
 __host__ __device__ constexpr int qk_slot(int k) {
+  if (NG == 1) return (k >= 4 && k <= 10 && (k & 1) == 0) ? (k - 4) / 2 : -1;
   if (IS_X) return (k >= 8 && k < 16) ? k - 8 : -1;
   return (k >= 6 && k <= 20 && (k & 1) == 0) ? (k - 6) / 2 : -1;
 }
-// X half-steps refill V^T region b of k-step t behind the slot of the last accumulator
-// product that reads it: t = 0 behind slots 8..11 (its products are slots 0..7), t = 1
-// behind slots 18, 20, 22 and 23 (its products are slots 16..23, two per region).
-__host__ __device__ constexpr int vt_read_slot(int t, int b) {
-  return t == 0 ? 8 + b : (b < 3 ? 18 + 2 * b : 23);
-}
-template <bool IS_X>
+template <int NG, bool IS_X>
 __host__ __device__ constexpr int pv_index(int k) {
   int n = 0;
-  for (int i = 0; i < k; ++i) n += qk_slot<IS_X>(i) < 0 ? 1 : 0;
+  for (int i = 0; i < k; ++i) n += qk_slot<NG, IS_X>(i) < 0 ? 1 : 0;
   return n;
 }
-static_assert(pv_index<false>(24) == 16 && pv_index<true>(24) == 16, "16 accumulator products");
-
-// O^T += V^T P^T for one map, both groups and one k-step (8 MFMAs sharing the V^T
-// operands).
-__device__ __forceinline__ void pv(f32x16 (&acc)[2][4], const VtHalf& vt,
-                                   const bf16x8 (&p)[2][2], int t) {
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const bf16x8 va = vt_operand(vt, b);
-    acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[0][t], acc[0][b], 0, 0, 0);
-    acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[1][t], acc[1][b], 0, 0, 0);
-  }
+static_assert(pv_index<2, false>(24) == 16 && pv_index<2, true>(24) == 16, "16 products");
+static_assert(pv_index<1, false>(12) == 8 && pv_index<1, true>(12) == 8, "8 products");
+// X half-steps refill V^T region b of k-step t behind the slot of the last accumulator
+// product that reads it. NG = 2: t = 0 behind slots 8..11 (its products are slots 0..7),
+// t = 1 behind slots 18, 20, 22 and 23 (its products are slots 16..23, two per region).
+// NG = 1: t = 0 behind slots 4..7 (its products are slots 0..3), t = 1 behind slots 6, 8,
+// 10 and 11 (its products are slots 5, 7, 9 and 11).
+template <int NG>
+__host__ __device__ constexpr int vt_read_slot(int t, int b) {
+  if (NG == 1) return t == 0 ? 4 + b : (b < 3 ? 6 + 2 * b : 11);
+  return t == 0 ? 8 + b : (b < 3 ? 18 + 2 * b : 23);
 }
+// Slot of the first step of softmax pair pr (16 pairs over 24 slots with two groups, 8
+// over 12 with one); its five steps take that slot and the four after it.
+template <int NG>
+__host__ __device__ constexpr int pair_start(int pr) { return NG == 2 ? (pr * 5) / 4 : pr; }
+static_assert(pair_start<2>(15) + 4 < 24 && pair_start<1>(7) + 4 < 12, "pairs end in time");
+
 // Keeps the accumulators in the accumulation registers across the loop.
 __device__ __forceinline__ void acc_pin(f32x16 (&acc)[2][4]) {
   asm volatile(""
                : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
                  "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
 }
-// The softmax results are complete here (keeps them from being sunk past the rescale).
-__device__ __forceinline__ void p_anchor(bf16x8 (&P)[2][2]) {
-  asm volatile("" : "+v"(P[0][0]), "+v"(P[0][1]), "+v"(P[1][0]), "+v"(P[1][1]));
-}
-// MFMA / vector-ALU interleave for the 16 accumulator products of a half-step: each is
-// followed by a few softmax instructions.
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-  }
+__device__ __forceinline__ void acc_pin(f32x16 (&acc)[1][4]) {
+  asm volatile("" : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]));
 }
 
 template <bool B>
@@ -440,11 +440,12 @@ __device__ __forceinline__ int k_off(int j) { return ((j >> 1) % NSLOT) * SLOT +
 __device__ __forceinline__ int v_off(int j) { return ((j >> 1) % NSLOT) * SLOT + (j & 1) * (32 * 64); }
 
 // SAFE = false: the fast pass (every row block). SAFE = true: the fixup pass, which
-// returns at once unless the fast pass flagged a row of its block in `flags` (8 words per
-// block, block (b h, qb) at words 8 (bh nqb + qb) ..: bit m of word 2 w + g is row
-// 8 m + 2 w + g of the block), and then redoes the block on the checked path and rewrites
-// exactly the flagged rows.
-template <bool SAFE>
+// returns at once unless the fast pass flagged a row of its block in `flags` (4 NG words
+// per block, block (b h, qb) at words 4 NG (bh nqb + qb) ..: bit m of word NG w + g is the
+// row of lane column m, group g of wave w), and then redoes the block on the checked path
+// and rewrites exactly the flagged rows. NG: query groups of 32 rows per wave (2: 256-row
+// blocks; 1: 128-row blocks, see fwd_bf16_groups).
+template <bool SAFE, int NG>
 __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
     const bf16_t* __restrict__ k1, const bf16_t* __restrict__ k2,
@@ -465,7 +466,12 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   const int bid = blockIdx.x;
   const int bh = bid % BH;
   const int qb = nqb - 1 - bid / BH;
-  const int q0 = qb * BR;
+  constexpr int RB = 32 * NW * NG;   // query rows per workgroup
+  constexpr int FW = NW * NG;        // row-flag words per block
+  const int q0 = qb * RB;
+  // Workgroup row of lane column m, group g of this wave: rows are dealt with stride
+  // NW NG, so every wave and group sees the same key range.
+  auto row_of = [&](int g) __attribute__((always_inline)) { return q0 + FW * m + NG * wv + g; };
   const int64_t hoff = static_cast<int64_t>(bh) * N;
 
   // K/V head of this query head (grouped-query attention: G query heads per K/V head).
@@ -475,17 +481,17 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   rs.k2 = rsrc_words(k2 + kvoff * D, N * D * 2);
   rs.v = rsrc_words(v + kvoff * DV, N * DV * 2);
 
-  // Every wave walks the same sub-tiles: keys 0 .. q0 + BR - 1 (rows beyond N are
+  // Every wave walks the same sub-tiles: keys 0 .. q0 + RB - 1 (rows beyond N are
   // zero-filled and masked). The first jd are wholly below the block's first row.
-  const int n_sub = (q0 + BR) / 32;
+  const int n_sub = (q0 + RB) / 32;
   const int n_tiles = n_sub / 2;
   const int jd = q0 / 32;
 
   // Queries of this lane: group g holds workgroup row 8 m + 2 wv + g.
-  bf16x8 qf1[2][4], qf2[2][4];
+  bf16x8 qf1[NG][4], qf2[NG][4];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int q = min(q0 + 8 * m + 2 * wv + g, N - 1);
+  for (int g = 0; g < NG; ++g) {
+    const int q = min(row_of(g), N - 1);
     const bf16_t* Q1 = q1 + (hoff + q) * D;
     const bf16_t* Q2 = q2 + (hoff + q) * D;
 #pragma unroll
@@ -513,23 +519,23 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   }
 
   const float c = kLog2e / 8.0f;  // log2(e) / sqrt(64)
-  RowState st1[2], st2[2];
-  f32x16 acc1[2][4], acc2[2][4];
-  f32x16 S1[2], S2[2];
-  bf16x8 P1[2][2], P2[2][2];
+  RowState st1[NG], st2[NG];
+  f32x16 acc1[NG][4], acc2[NG][4];
+  f32x16 S1[NG], S2[NG];
+  bf16x8 P1[NG][2], P2[NG][2];
   // V^T operands of the sub-tile the next PV products use.
   VtHalf vt[2];
   // Per group: this lane's row left the fast path's bound on some sub-tile (fast pass),
   // or was flagged by it (fixup pass).
-  uint32_t bad[2] = {0u, 0u};
+  uint32_t bad[NG] = {};
   if constexpr (SAFE) {
-    const uint32_t* f = flags + 8 * (static_cast<int64_t>(bh) * nqb + qb);
+    const uint32_t* f = flags + FW * (static_cast<int64_t>(bh) * nqb + qb);
     uint32_t any = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) any |= f[i];
+    for (int i = 0; i < FW; ++i) any |= f[i];
     if (__builtin_amdgcn_readfirstlane(any) == 0) return;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) bad[g] = (f[2 * wv + g] >> m) & 1u;
+    for (int g = 0; g < NG; ++g) bad[g] = (f[NG * wv + g] >> m) & 1u;
   }
 
   // One half-step, in a fixed order: 24 products (16 accumulator products acc += V^T P^T
@@ -546,10 +552,10 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   // tested inside the loop and it has no branch at all. IS_X: the X half-step, which
   // also prefetches V^T(j) (used by Y(j) and again by X(j + 1)); the Y half-step of an
   // odd sub-tile holds the tile barrier.
-  auto half = [&](auto masked, auto is_x, auto check, int j, f32x16 (&acc)[2][4],
-                  const bf16x8 (&Pin)[2][2], f32x16 (&S_next)[2], const bf16x8 (&qf)[2][4],
-                  int k_sub, f32x16 (&S_cur)[2], const bf16x8 (&qf_cur)[2][4],
-                  RowState (&st)[2], bf16x8 (&Pout)[2][2], f32x16 (&acc_cur)[2][4])
+  auto half = [&](auto masked, auto is_x, auto check, int j, f32x16 (&acc)[NG][4],
+                  const bf16x8 (&Pin)[NG][2], f32x16 (&S_next)[NG], const bf16x8 (&qf)[NG][4],
+                  int k_sub, f32x16 (&S_cur)[NG], const bf16x8 (&qf_cur)[NG][4],
+                  RowState (&st)[NG], bf16x8 (&Pout)[NG][2], f32x16 (&acc_cur)[NG][4])
       __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     constexpr bool IS_X = decltype(is_x)::value;
@@ -560,11 +566,11 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     float y[32];
     // Packed weights as separate 32-bit words: kept in a u32x4 and updated element by
     // element, the dot products below were compiled to read element 0 each time.
-    uint32_t pw[2][2][4];
+    uint32_t pw[NG][2][4];
     // Row sums: the sub-tile's partial (fixup pass), or the running sums (fast pass).
-    float ssum[2][2];
+    float ssum[NG][2];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
       ssum[g][0] = CHECK ? 0.f : st[g].l;
       ssum[g][1] = CHECK ? 0.f : st[g].l2;
     }
@@ -572,31 +578,37 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     auto slot = [&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
       // ---- the k-th product (score product q or accumulator product pv, see qk_slot)
-      constexpr int q = qk_slot<IS_X>(k);
+      constexpr int q = qk_slot<NG, IS_X>(k);
       if constexpr (q < 0) {
-        constexpr int pv = pv_index<IS_X>(k);
-        constexpr int t = pv >> 3, b = (pv & 7) >> 1, g = pv & 1;
+        constexpr int pv = pv_index<NG, IS_X>(k);
+        constexpr int t = pv / (4 * NG), b = (pv % (4 * NG)) / NG, g = pv % NG;
         acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_operand(vt[t], b), Pin[g][t],
                                                              acc[g][b], 0, 0, 0);
       } else {
-        constexpr int kb = q >> 1, g = q & 1;
+        constexpr int kb = q / NG, g = q % NG;
         qk_one(S_next[g], k_operand(kop, kb), qf[g][kb], kb == 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- work placed behind it
       // S_cur came from the previous half-step's score products, the last of them 3 or
       // more slots before that half-step ended: more than the result latency.
-      if constexpr (k == 0) s_anchor(S_cur);
+      if constexpr (k == 0) {
+        if constexpr (NG == 2) {
+          s_anchor(S_cur);
+        } else {
+          s_guard(S_cur);
+        }
+      }
       if constexpr (k == 2) k_issue<KN_OFF>(kop, ka, k_off(k_sub));
-      static_for<0, 16>([&](auto pc) __attribute__((always_inline)) {
+      static_for<0, 8 * NG>([&](auto pc) __attribute__((always_inline)) {
         constexpr int pr = decltype(pc)::value;
-        constexpr int sa = (pr * 5) / 4;   // 16 pairs over slots 0 .. 22
+        constexpr int sa = pair_start<NG>(pr);
         constexpr int g = pr >> 3, e = 2 * (pr & 7);
         if constexpr (k == sa) {          // scale and subtract the reference
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             float sv = S_cur[g][e + i];
-            if (MASKED && 32 * j + key_of(e + i, h) > q0 + 8 * m + 2 * wv + g) sv = -INFINITY;
+            if (MASKED && 32 * j + key_of(e + i, h) > row_of(g)) sv = -INFINITY;
             y[16 * g + e + i] = fmaf(sv, c, -st[g].m);
           }
           asm volatile("" : "+v"(y[16 * g + e]), "+v"(y[16 * g + e + 1]));
@@ -624,7 +636,7 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
       if constexpr (IS_X) {
         static_for<0, 8>([&](auto ic) __attribute__((always_inline)) {
           constexpr int t = decltype(ic)::value >> 2, b = decltype(ic)::value & 3;
-          if constexpr (k == vt_read_slot(t, b)) vt_issue_b<b, t>(vt[t], va + v_off(j));
+          if constexpr (k == vt_read_slot<NG>(t, b)) vt_issue_b<b, t>(vt[t], va + v_off(j));
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -637,20 +649,23 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
       tile_barrier(u + 1 < n_tiles);
       if (u + 2 < n_tiles) dma_tile(rs, lds, u + 2, wv, lane);
     }
-    static_for<2, 24>(slot);
+    static_for<2, 12 * NG>(slot);
     if constexpr (CHECK) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) st[g].lp = ssum[g][0] + ssum[g][1];
-      slow = __any(over(st[0].lp) || over(st[1].lp));
+      for (int g = 0; g < NG; ++g) st[g].lp = ssum[g][0] + ssum[g][1];
+      bool o = false;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) o = o || over(st[g].lp);
+      slow = __any(o);
     } else {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         st[g].l = ssum[g][0];
         st[g].l2 = ssum[g][1];
       }
     }
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const u32x4 w4 = {pw[g][hf][0], pw[g][hf][1], pw[g][hf][2], pw[g][hf][3]};
@@ -663,19 +678,19 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         KOps kc;
         k_issue<KC_OFF>(kc, ka, k_off(j));
-        f32x16 Sr[2];
+        f32x16 Sr[NG];
         qk(Sr, kc, qf_cur);
         s_guard(Sr);
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          if (MASKED) mask_scores(Sr[g], 32 * j, q0 + 8 * m + 2 * wv + g, h);
+        for (int g = 0; g < NG; ++g) {
+          if (MASKED) mask_scores(Sr[g], 32 * j, row_of(g), h);
           settle_row(Sr[g], c, st[g], Pout[g][0], Pout[g][1], acc_cur[g]);
         }
       }
     }
     if constexpr (CHECK) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) st[g].l += st[g].lp;
+      for (int g = 0; g < NG; ++g) st[g].l += st[g].lp;
     }
   };
 
@@ -693,7 +708,7 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   // pass checks every sub-tile.
   auto run = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
       st1[g] = RowState{kMInit, 0.f, 0.f, 0.f};
       st2[g] = RowState{kMInit, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -719,23 +734,23 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
       // starts at key 0).
       KOps kop;
       k_issue<K2_OFF>(kop, ka, k_off(0));
-      f32x16 T2[2];
+      f32x16 T2[NG];
       qk(T2, kop, qf2);
       s_guard(S1);
       s_guard(T2);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         f32x16 a = S1[g], b = T2[g];
         if (jd == 0) {
-          mask_scores(a, 0, q0 + 8 * m + 2 * wv + g, h);
-          mask_scores(b, 0, q0 + 8 * m + 2 * wv + g, h);
+          mask_scores(a, 0, row_of(g), h);
+          mask_scores(b, 0, row_of(g), h);
         }
         st1[g].m = max_halves(max16(a)) * c;
         st2[g].m = max_halves(max16(b)) * c;
       }
     }
 #pragma unroll
-    for (int g = 0; g < 2; ++g) P2[g][0] = P2[g][1] = bf16x8{};
+    for (int g = 0; g < NG; ++g) P2[g][0] = P2[g][1] = bf16x8{};
     // X(0) multiplies tile 0's V (finite) by P2 = 0.
     vt_issue<0>(vt[0], va + v_off(0));
     vt_issue<1>(vt[1], va + v_off(0));
@@ -744,7 +759,7 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     if constexpr (!SAFE) {
       // Rows whose normaliser left the fast path's bound (either lane half of the row).
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         st1[g].l += st1[g].l2;
         st2[g].l += st2[g].l2;
         bad[g] = static_cast<uint32_t>(st1[g].l > kBad || st2[g].l > kBad);
@@ -756,7 +771,7 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < NG; ++g)
           acc2[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_operand(vt[t], b), P2[g][t],
                                                                acc2[g][b], 0, 0, 0);
       }
@@ -770,17 +785,20 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   // the loop no longer needs; Y = O times one per-row factor (1 - lambda_init) rstd,
   // times w when given.
   // The fast pass stages its Y rows in LDS and stores them as whole rows. Each wave has
-  // 16 KiB there (64 rows of 256 B) in the two ring slots after the last tile's slot: once
-  // a wave has passed the last tile barrier, every wave is past its last read of any slot
-  // but the last tile's, and no tile load is in flight.
-  const int stage = lds_base + ((n_tiles + (wv >> 1)) % NSLOT) * SLOT + (wv & 1) * (64 * DV * 2);
+  // 8 NG KiB there (32 NG rows of 256 B) in the two ring slots after the last tile's slot:
+  // once a wave has passed the last tile barrier, every wave is past its last read of any
+  // slot but the last tile's, and no tile load is in flight.
+  constexpr int STAGE_W = 32 * NG * DV * 2;   // bytes per wave
+  constexpr int WPS = SLOT / STAGE_W;         // waves per slot
+  static_assert(NW <= 2 * WPS, "the staging areas fit two ring slots");
+  const int stage = lds_base + ((n_tiles + wv / WPS) % NSLOT) * SLOT + (wv % WPS) * STAGE_W;
   const float lam = lamst->lambda_f;
   const float gsc = lamst->one_minus_init_f;
   const int hh = bh % H;
   auto epilogue = [&](auto only_bad) __attribute__((always_inline)) {
   constexpr bool STAGED = !decltype(only_bad)::value;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
+  for (int g = 0; g < NG; ++g) {
     const bool row_bad = (bad[g] | static_cast<uint32_t>(__shfl_xor(static_cast<int>(bad[g]), 32))) != 0;
     float l1 = st1[g].l + __shfl_xor(st1[g].l, 32);
     float l2 = st2[g].l + __shfl_xor(st2[g].l, 32);
@@ -805,11 +823,11 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     sst += __shfl_xor(sst, 32);
     const float rstd = 1.0f / sqrtf(sst * (1.0f / DV) + eps);
     const float sc = gsc * rstd;
-    const int qr = q0 + 8 * m + 2 * wv + g;
+    const int qr = row_of(g);
     if constexpr (STAGED) {
       // Row 2 m + g of the wave's staging area; its 16-byte unit u (channels 8 u .. 8 u + 7)
       // sits at u ^ (m % 16), so the 32 rows one write touches spread over the banks.
-      const int sr = stage + (2 * m + g) * (DV * 2) + 8 * h;
+      const int sr = stage + (NG * m + g) * (DV * 2) + 8 * h;
       const float* W = rms_w ? rms_w + hh * DV + 4 * h : nullptr;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -875,13 +893,14 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     }
   }
   if constexpr (STAGED) {
-    // The wave's 64 rows as whole rows: 4 rows of 256 B per instruction, 16 B per lane.
+    // The wave's 32 NG rows as whole rows: 4 rows of 256 B per instruction, 16 B per lane.
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8 * NG; ++i) {
       const int r = 4 * i + (lane >> 4), c = lane & 15;
+      const int rm = r / NG, rg = r % NG;   // lane column and group of staged row r
       const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(
-          (LDS_AS char*)nullptr + stage + r * (DV * 2) + 16 * (c ^ ((r >> 1) & 15)));
-      const int qr = q0 + 8 * (r >> 1) + 2 * wv + (r & 1);
+          (LDS_AS char*)nullptr + stage + r * (DV * 2) + 16 * (c ^ (rm & 15)));
+      const int qr = q0 + FW * rm + NG * wv + rg;
       if (qr < N) {
         const int64_t yrow = out_bnh ? (static_cast<int64_t>(bh / H) * N + qr) * H + hh : hoff + qr;
         *reinterpret_cast<u32x4*>(out + yrow * DV + 8 * c) = v;
@@ -893,12 +912,13 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   run();
   if constexpr (!SAFE) {
     epilogue(Flag<false>{});
-    // Row flags of this block: bit m of word 2 wv + g for row 8 m + 2 wv + g.
+    // Row flags of this block: bit m of word NG wv + g for the row of lane column m and
+    // group g.
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
       const uint64_t bal = __ballot(bad[g] != 0);
       const uint32_t mask = static_cast<uint32_t>(bal) | static_cast<uint32_t>(bal >> 32);
-      if (lane == 0) flags[8 * (static_cast<int64_t>(bh) * nqb + qb) + 2 * wv + g] = mask;
+      if (lane == 0) flags[FW * (static_cast<int64_t>(bh) * nqb + qb) + NG * wv + g] = mask;
     }
   } else {
     epilogue(Flag<true>{});
@@ -907,20 +927,34 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
 
 }  // namespace fwdbf16
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+// Query groups per wave: one (128-row blocks) when the 256-row blocks would not fill
+// the chip twice over. Every wave of a block walks all keys up to the block's end, so a
+// wave's longest walk is half as long with 32 rows per wave; with few blocks per compute
+// unit that walk, not the total work, sets the time. With more blocks the hardware's
+// longest-first dispatch already balances the compute units, and two groups per wave
+// share every K and V^T operand read.
+constexpr int64_t kFwdOneGroupMaxBlocks = 384;
+int fwd_bf16_groups(int64_t B, int64_t H, int64_t N) {
+  const int64_t blocks256 = B * H * ((N + fwdbf16::BR - 1) / fwdbf16::BR);
+  return blocks256 <= kFwdOneGroupMaxBlocks ? 1 : 2;
+}
+
+template <int NG>
+static hipError_t launch_fwd_bf16_ng(const FwdArgs& a, hipStream_t s) {
   using namespace fwdbf16;
   static std::atomic<uint64_t> attr_done{0};
   const hipError_t ea = once_per_device(attr_done, [] {
-    hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<false>),
+    hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<false, NG>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (r == hipSuccess)
-      r = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<true>),
+      r = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<true, NG>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     return r;
   });
   if (ea != hipSuccess) return ea;
+  constexpr int RB = 32 * NW * NG;
   const int64_t BH = a.B * a.H;
-  const int nqb = static_cast<int>((a.N + BR - 1) / BR);
+  const int nqb = static_cast<int>((a.N + RB - 1) / RB);
   const int64_t nblk = BH * nqb;
   const diffattn_saved& sv = a.saved;
   uint32_t* flags = static_cast<uint32_t*>(a.workspace);
@@ -936,12 +970,18 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
                        a.eps, a.out_bnh ? 1 : 0, a.G);
     return hipGetLastError();
   };
-  hipError_t e = launch(fwd_bf16_kernel<false>);
+  hipError_t e = launch(fwd_bf16_kernel<false, NG>);
   if (e != hipSuccess) return e;
-  return launch(fwd_bf16_kernel<true>);
+  return launch(fwd_bf16_kernel<true, NG>);
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+  return fwd_bf16_groups(a.B, a.H, a.N) == 1 ? launch_fwd_bf16_ng<1>(a, s)
+                                             : launch_fwd_bf16_ng<2>(a, s);
 }
 
 size_t fwd_bf16_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+  // Row flags: 8 words per 256-row block, or 4 per 128-row block (no more words in all).
   const int64_t nqb = (N + fwdbf16::BR - 1) / fwdbf16::BR;
   return static_cast<size_t>(B * H * nqb) * 8 * sizeof(uint32_t);
 }

@@ -44,3 +44,23 @@ def lambda_state_tensor(lam: float, lam_init: float, device=DEV, exp_a=1.0, exp_
     raw = struct.pack(da.STATE_FMT, lam, lam_init, exp_a, exp_b, float(np.float32(lam)),
                       float(np.float32(lam_init)), float(np.float32(1.0 - lam_init)), 0.0)
     return torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(device)
+
+
+def forward_groups(B, H, N):
+    """Query groups per wave the bf16 forward uses: one (128-row blocks) when the problem
+    has at most 384 blocks of 256 rows, else two (256-row blocks)."""
+    return 1 if B * H * ((N + 255) // 256) <= 384 else 2
+
+
+def row_flagged(ws, B, H, N, bh, row):
+    """Whether the forward's fast pass flagged query row `row` of head bh (b H + h) for the
+    fixup pass, from the row flags it leaves in its workspace: per block of 128 NG rows,
+    4 NG words; bit m of word NG w + g is the row 4 NG m + NG w + g of the block."""
+    ng = forward_groups(B, H, N)
+    rb, fw = 128 * ng, 4 * ng
+    nqb = (N + rb - 1) // rb
+    qb, r = divmod(row, rb)
+    m, rest = divmod(r, fw)
+    word = rest            # NG w + g
+    flags = ws.view(torch.int32).cpu().numpy()
+    return bool((int(flags[fw * (bh * nqb + qb) + word]) >> m) & 1)

@@ -14,7 +14,8 @@ import torch
 from differential_attention_causal_amd import diffattn as da
 from differential_attention_causal_amd import synth
 from oracle import diffattn_oracle as orc
-from tests.helpers import DEV, draw, lam_pair, lambda_state_tensor, normwise_rel, np64
+from tests.helpers import (DEV, draw, forward_groups, lam_pair, lambda_state_tensor, normwise_rel,
+                           np64, row_flagged)
 
 pytestmark = pytest.mark.gpu
 
@@ -356,10 +357,10 @@ def test_unsupported_head_dim_raises():
 
 def test_bf16_fixup_pass_for_large_score_jump():
     """A key whose score exceeds a row's first-sub-tile maximum by ~2^100 in weight (query
-    and key rows of 3.0: a scaled score of 72): the fast pass flags that row (bit 18 of
-    word 0 of row block 1: row 400 = 256 + 8*18) and the fixup pass recomputes it. Row
-    300 gets a jump of ~2^43 (rows of 2.0), inside the fast pass's bound: not flagged, its
-    fast-pass result stands. Every row must match the oracle."""
+    and key rows of 3.0: a scaled score of 72): the fast pass flags that row (400) and the
+    fixup pass recomputes it. Row 300 gets a jump of ~2^43 (rows of 2.0), inside the fast
+    pass's bound: not flagged, its fast-pass result stands. Every row must match the
+    oracle. (Few blocks: the forward takes 128-row blocks here.)"""
     w = synth.custom("fwd", 1, 2, 600, 64, 5, "bf16", number=470)
     x, h, st, ls, _ = _run_fwd(w)
     x = {k: t.clone() for k, t in x.items()}
@@ -374,14 +375,41 @@ def test_bf16_fixup_pass_for_large_score_jump():
     y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, workspace=ws)
     y2 = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st)
     torch.cuda.synchronize()
-    flags = ws.view(torch.int32).cpu().numpy().reshape(2, 3, 8)   # [head, row block, word]
-    assert flags[0, 1, 0] & (1 << 18) and flags[1, 1, 0] & (1 << 18)
-    assert not flags[0, 1, 4] & (1 << 5)    # row 300 = 256 + 8 * 5 + 4 (word 2 w + g = 4)
+    assert row_flagged(ws, 1, 2, 600, 0, 400) and row_flagged(ws, 1, 2, 600, 1, 400)
+    assert not row_flagged(ws, 1, 2, 600, 0, 300)
     assert torch.equal(y, y2)
     hh = {k: np64(t) for k, t in x.items()}
     ref = orc.forward(hh["q1"], hh["q2"], hh["k1"], hh["k2"], hh["v"], ls["lambda"],
                       ls["lambda_init"])
     assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
+
+
+def test_bf16_fixup_pass_two_groups_per_wave():
+    """The same planted score jump with 512 blocks of 256 rows (B1 H128 N1024), where the
+    forward takes two query groups per wave: rows 400 (head 0, map 1) and 700 (head 77,
+    map 2) are flagged and recomputed; those heads and two others match the oracle."""
+    B, H, N = 1, 128, 1024
+    assert forward_groups(B, H, N) == 2
+    w = synth.custom("fwd", B, H, N, 64, 5, "bf16", number=473)
+    x, _ = draw(w)
+    x = {k: t.clone() for k, t in x.items()}
+    x["q1"][0, 0, 400] = 3.0
+    x["k1"][0, 0, 350] = 3.0
+    x["q2"][0, 77, 700] = 3.0
+    x["k2"][0, 77, 650] = 3.0
+    h = {k: np64(t) for k, t in x.items()}
+    st, ls = lam_pair(x, h, w.layer)
+    p = da.problem(B, H, N, 64, da.BF16)
+    ws = torch.zeros(da.workspace_bytes(da.OP_FWD, p), dtype=torch.uint8, device=DEV)
+    y = da.forward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], st, workspace=ws)
+    torch.cuda.synchronize()
+    assert row_flagged(ws, B, H, N, 0, 400) and row_flagged(ws, B, H, N, 77, 700)
+    assert not row_flagged(ws, B, H, N, 0, 399)
+    for hd in (0, 1, 77, 127):
+        sl = {k: h[k][:, hd:hd + 1] for k in ("q1", "q2", "k1", "k2", "v")}
+        ref = orc.forward(sl["q1"], sl["q2"], sl["k1"], sl["k2"], sl["v"], ls["lambda"],
+                          ls["lambda_init"])
+        assert np.max(np.abs(np64(y[:, hd:hd + 1]) - ref)) <= BF16_TOL, hd
 
 
 def test_bf16_peaked_scores():
@@ -424,8 +452,7 @@ def test_bf16_fixup_pass_training_saves_and_backward():
     g = da.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lq1"], x["lk1"], x["lq2"],
                     x["lk2"], st, sv, x["dout"])
     torch.cuda.synchronize()
-    flags = ws.view(torch.int32).cpu().numpy().reshape(2, 3, 8)
-    assert flags[0, 1, 0] & (1 << 18) and flags[1, 1, 0] & (1 << 18)
+    assert row_flagged(ws, 1, 2, 600, 0, 400) and row_flagged(ws, 1, 2, 600, 1, 400)
     ref, rs = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
                           ls["lambda_init"], want_saved=True)
     assert np.max(np.abs(np64(y) - ref)) <= BF16_TOL
