@@ -36,19 +36,21 @@
 //    A map's rescale (when its running max moved) happens between its half-steps, after
 //    the last product into that accumulator and before the next.
 //  * Query rows are dealt to lanes with stride 4 NG (row 4 NG m + NG w + g of the
-//    workgroup's for lane column m, wavefront w, group g), so every wavefront and group
-//    sees the same key range: sub-tiles below the workgroup's first row run without mask
-//    code and the 4 NG sub-tiles of the diagonal block apply the integer predicate
-//    key <= query.
+//    workgroup's rows for lane column m, wavefront w, group g; NG groups per wavefront),
+//    so every wavefront and group sees the same key range: sub-tiles below the
+//    workgroup's first row run without mask code and the 4 NG sub-tiles of the diagonal
+//    block apply the integer predicate key <= query.
 //  * K1, K2 and V tiles of 64 keys go from HBM straight into LDS (buffer loads with the
 //    LDS as destination) in a ring of 4 slots, two tiles ahead, one barrier per tile.
 //    Rows at or beyond N read as zero. V^T comes out of the row-major V tile with the
 //    transposing read ds_read_b64_tr_b16; LDS swizzles keep every operand read free of
 //    bank conflicts.
-//  * No row maximum on the fast path: weights use the row's current reference m, and a
-//    row only takes the slow path (exact maximum, rescale) when its partial sum leaves
-//    the bound (see kThr); the decision is per row, so every row's result depends on its
-//    own scores only.
+//  * No running row maximum on the fast path: each row's reference m is the exact maximum
+//    of its first sub-tile, and the loop never branches. A row whose normaliser ends above
+//    2^48 (kBad) is flagged; a second launch (the fixup pass) redoes only flagged blocks
+//    on the checked path, where a row's partial sum above kThr moves its m to the exact
+//    maximum and rescales. The decisions are per row, so every row's result depends on
+//    its own scores only.
 //  * Workgroups run longest-first, and consecutive workgroup ids take different heads so
 //    that the tiles of one head land on the same XCD (ids are dealt to the 8 XCDs
 //    round-robin) and share its L2.
