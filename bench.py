@@ -123,7 +123,7 @@ def leg_forward(steps, warmup, number=3):
         "fwd_kernel_ms_min": srt[0], "flops_per_launch": fl,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_from_profiles("fwd_bf16_kernel<false>", "fwd_bf16.hip", w.name)},
+                     "traffic": traffic_from_profiles("fwd_bf16_kernel<false, 2>", "fwd_bf16.hip", w.name)},
         "formula_tflops_8dP": fl * 8.0 / 12.0 / (ms * 1e-3) / 1e12,
     }
 
