@@ -446,7 +446,8 @@ __device__ __forceinline__ int v_off(int j) { return ((j >> 1) % NSLOT) * SLOT +
 // per block, block (b h, qb) at words 4 NG (bh nqb + qb) ..: bit m of word NG w + g is the
 // row of lane column m, group g of wave w), and then redoes the block on the checked path
 // and rewrites exactly the flagged rows. NG: query groups of 32 rows per wave (2: 256-row
-// blocks; 1: 128-row blocks, see fwd_bf16_groups).
+// blocks; 1: 128-row blocks, see fwd_bf16_groups). With one group the fast pass does that
+// fixup itself, in the same launch, and the SAFE instance is not used.
 template <bool SAFE, int NG>
 __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     const bf16_t* __restrict__ q1, const bf16_t* __restrict__ q2,
@@ -707,8 +708,9 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   // The key loop over every sub-tile, from loading tile 0 to the last product. The fast
   // pass takes each row's reference m from the exact maximum of its first sub-tile (both
   // maps' first score tiles are formed here once for that) and never branches; the fixup
-  // pass checks every sub-tile.
-  auto run = [&]() __attribute__((always_inline)) {
+  // (CHECK) checks every sub-tile.
+  auto run = [&](auto check) __attribute__((always_inline)) {
+    constexpr bool CHECK = decltype(check)::value;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       st1[g] = RowState{kMInit, 0.f, 0.f, 0.f};
@@ -731,7 +733,7 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
       k_issue<K1_OFF>(kop, ka, k_off(0));
       qk(S1, kop, qf1);
     }
-    if constexpr (!SAFE) {
+    if constexpr (!CHECK) {
       // Reference m of both maps: exact row maxima of sub-tile 0 (masked where the block
       // starts at key 0).
       KOps kop;
@@ -756,9 +758,9 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     // X(0) multiplies tile 0's V (finite) by P2 = 0.
     vt_issue<0>(vt[0], va + v_off(0));
     vt_issue<1>(vt[1], va + v_off(0));
-    for (int j = 0; j < jd; ++j) step(j, Flag<false>{}, Flag<SAFE>{});
-    for (int j = jd; j < n_sub; ++j) step(j, Flag<true>{}, Flag<SAFE>{});
-    if constexpr (!SAFE) {
+    for (int j = 0; j < jd; ++j) step(j, Flag<false>{}, check);
+    for (int j = jd; j < n_sub; ++j) step(j, Flag<true>{}, check);
+    if constexpr (!CHECK) {
       // Rows whose normaliser left the fast path's bound (either lane half of the row).
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -911,18 +913,40 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   }
   };
 
-  run();
   if constexpr (!SAFE) {
+    run(Flag<false>{});
     epilogue(Flag<false>{});
     // Row flags of this block: bit m of word NG wv + g for the row of lane column m and
     // group g.
+    uint32_t mask[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const uint64_t bal = __ballot(bad[g] != 0);
-      const uint32_t mask = static_cast<uint32_t>(bal) | static_cast<uint32_t>(bal >> 32);
-      if (lane == 0) flags[FW * (static_cast<int64_t>(bh) * nqb + qb) + NG * wv + g] = mask;
+      mask[g] = static_cast<uint32_t>(bal) | static_cast<uint32_t>(bal >> 32);
+      if (lane == 0) flags[FW * (static_cast<int64_t>(bh) * nqb + qb) + NG * wv + g] = mask[g];
+    }
+    if constexpr (NG == 1) {
+      // One-group blocks redo a flagged block here rather than in a second launch, which
+      // costs more than the rare fixup itself on the small problems that use them. The
+      // waves share their flags through LDS; the barrier also ends every wave's reads of
+      // the staging slots.
+      __shared__ uint32_t wave_flags[NW];
+      if (lane == 0) wave_flags[wv] = mask[0];
+      __syncthreads();
+      uint32_t any = 0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) any |= wave_flags[i];
+      if (__builtin_amdgcn_readfirstlane(any) != 0) {
+        bad[0] = (mask[0] >> m) & 1u;
+        // The fast pass's stores of the flagged rows land before the rewrite.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        run(Flag<true>{});
+        epilogue(Flag<true>{});
+      }
     }
   } else {
+    run(Flag<true>{});
     epilogue(Flag<true>{});
   }
 }
@@ -948,8 +972,8 @@ static hipError_t launch_fwd_bf16_ng(const FwdArgs& a, hipStream_t s) {
   const hipError_t ea = once_per_device(attr_done, [] {
     hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<false, NG>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (r == hipSuccess)
-      r = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<true, NG>),
+    if (NG == 2 && r == hipSuccess)
+      r = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<true, 2>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     return r;
   });
@@ -973,8 +997,9 @@ static hipError_t launch_fwd_bf16_ng(const FwdArgs& a, hipStream_t s) {
     return hipGetLastError();
   };
   hipError_t e = launch(fwd_bf16_kernel<false, NG>);
-  if (e != hipSuccess) return e;
-  return launch(fwd_bf16_kernel<true, NG>);
+  // One-group blocks fix their flagged rows in the same launch.
+  if (e != hipSuccess || NG == 1) return e;
+  return launch(fwd_bf16_kernel<true, 2>);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {

@@ -178,8 +178,8 @@ diffattn_status diffattn_lambda_layers(int32_t dim, int32_t n_layers, int32_t fi
  *                   Non-NULL: every field must be a valid device buffer (bf16 only).
  *   workspace       device buffer of at least diffattn_workspace_bytes(OP_FWD) bytes
  *                   (bf16: 32 bytes per block of 256 query rows, B * H * ceil(N / 256)
- *                   blocks; it holds the row flags that pass the fast pass's result to a
- *                   fixup pass; contents are scratch, nothing needs to be cleared). May
+ *                   blocks; it holds the fast pass's row flags, which select the rows a
+ *                   fixup recomputes; contents are scratch, nothing needs to be cleared). May
  *                   be NULL when that size is 0 (float32). Too small or NULL when needed:
  *                   DIFFATTN_E_WORKSPACE. It must not overlap any other argument.
  * Pointers must be 16-byte aligned. */

@@ -360,7 +360,8 @@ def test_bf16_fixup_pass_for_large_score_jump():
     and key rows of 3.0: a scaled score of 72): the fast pass flags that row (400) and the
     fixup pass recomputes it. Row 300 gets a jump of ~2^43 (rows of 2.0), inside the fast
     pass's bound: not flagged, its fast-pass result stands. Every row must match the
-    oracle. (Few blocks: the forward takes 128-row blocks here.)"""
+    oracle. (Few blocks: the forward takes 128-row blocks here, and the fast pass redoes the
+    flagged block in the same launch.)"""
     w = synth.custom("fwd", 1, 2, 600, 64, 5, "bf16", number=470)
     x, h, st, ls, _ = _run_fwd(w)
     x = {k: t.clone() for k, t in x.items()}
