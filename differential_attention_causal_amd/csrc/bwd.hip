@@ -73,6 +73,10 @@ constexpr int Q_K2 = 2 * REG;
 constexpr int Q_V = 4 * REG;
 constexpr int Q_SLOT = 8 * REG;
 constexpr int Q_LDS = NSLOT * Q_SLOT;
+// Per-wave regions of the result staging (the stores through LDS), inside the ring.
+constexpr int KV_STAGE = 32 * (2 * DV + 16) + 2 * 32 * (2 * D + 16);
+constexpr int Q_STAGE = 2 * 32 * (2 * D + 16);
+static_assert(NW * KV_STAGE <= KV_LDS && NWQ * Q_STAGE <= Q_LDS, "staging exceeds the ring");
 
 // Tile layout: a W-channel bf16 tensor is stored as W/32 regions of [64 rows][64 B]; the
 // 16-byte chunk c of row r sits at position c ^ sw(r). With sw, the 16 operand rows that a
@@ -131,6 +135,38 @@ __device__ __forceinline__ void dma_rows(const u32x4& rs, uint32_t dst, int t0, 
 }
 // Workgroup barrier that also keeps the compiler from moving LDS reads across it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Result rows leave through LDS. A lane's accumulator holds 4 consecutive channels of
+// one row (8 bytes), and 32 rows per store instruction cost the memory pipeline about as
+// much per row as a whole line: the wave instead writes its 32 rows of a W-channel result
+// into LDS, row pitch 2 W + 16 bytes (the 8-byte writes of 32 rows and the 16-byte reads
+// along rows both meet no bank conflict), and copies them out as 16-byte pieces of
+// contiguous rows, 1 KiB per instruction.
+template <int W>
+constexpr int stage_pitch() { return 2 * W + 16; }
+template <int W>
+constexpr int stage_bytes() { return 32 * stage_pitch<W>(); }
+// Lane (m, h): channels 32 b + 8 jg + 4 h .. + 3 of row m.
+template <int W>
+__device__ __forceinline__ void stage_put(int base, int m, int h, int b, int jg, u32x2 v) {
+  *reinterpret_cast<LDS_AS u32x2*>((LDS_AS char*)nullptr + base + m * stage_pitch<W>() +
+                                   2 * (32 * b + 8 * jg + 4 * h)) = v;
+}
+// The 32 staged rows to dst (row pitch W elements); rows from `valid` on are not written.
+// Every lane of the wave has put its values (the wave's LDS accesses complete in order).
+template <int W>
+__device__ __forceinline__ void stage_flush(int base, bf16_t* dst, int valid, int lane) {
+  constexpr int LPR = 2 * W / 16;   // lanes per row
+  constexpr int RPI = 64 / LPR;     // rows per instruction
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + lane / LPR, cb = 16 * (lane % LPR);
+    const u32x4 x = *reinterpret_cast<const LDS_AS u32x4*>(
+        (LDS_AS char*)nullptr + base + r * stage_pitch<W>() + cb);
+    if (r < valid) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst + r * W) + cb) = x;
+  }
+}
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -513,6 +549,20 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
   const uint32_t ldsu = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)lds));
   const int lds0 = static_cast<int>(ldsu);
 
+  // Tiles 0..2 of query head g on their way into the ring.
+  auto start_head = [&](int g) {
+    const int64_t qo = (static_cast<int64_t>(bhk) * G + g) * N;   // query head bhk G + g
+    rs.q1 = rsrc_words(q1 + qo * D, N * D * 2);
+    rs.q2 = rsrc_words(q2 + qo * D, N * D * 2);
+    rs.g = rsrc_words(gb + qo * DV, N * DV * 2);
+    rs.vec = rsrc_words(vec + qo, N * 16);
+    kv_dma(rs, ldsu, 0, qt0 * TB, wv, lane);
+    if (nT > 1) kv_dma(rs, ldsu, 1, (qt0 + 1) * TB, wv, lane);
+    if (nT > 2) kv_dma(rs, ldsu, 2, (qt0 + 2) * TB, wv, lane);
+  };
+  // The first head's tiles travel together with the resident loads below.
+  start_head(0);
+
   // Resident B operands (K^T and V^T columns of this lane's key), in the accumulation
   // registers.
   bf16x8 kr1[4], kr2[4], vr[8];
@@ -561,17 +611,11 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
   auto slot_of = [&](int j) { return lds0 + ((j >> 1) & (NSLOT - 1)) * KV_SLOT; };
 #pragma clang loop unroll(disable)
   for (int g = 0; g < G; ++g) {
-  const int64_t qo = (static_cast<int64_t>(bhk) * G + g) * N;   // query head bhk G + g
-  rs.q1 = rsrc_words(q1 + qo * D, N * D * 2);
-  rs.q2 = rsrc_words(q2 + qo * D, N * D * 2);
-  rs.g = rsrc_words(gb + qo * DV, N * DV * 2);
-  rs.vec = rsrc_words(vec + qo, N * 16);
   // Every wave is done with the previous query head's tiles before the ring refills.
-  if (g > 0) barrier();
-  // Tiles 0..2 on their way (for g = 0 the resident loads above complete before tile 0's).
-  kv_dma(rs, ldsu, 0, qt0 * TB, wv, lane);
-  if (nT > 1) kv_dma(rs, ldsu, 1, (qt0 + 1) * TB, wv, lane);
-  if (nT > 2) kv_dma(rs, ldsu, 2, (qt0 + 2) * TB, wv, lane);
+  if (g > 0) {
+    barrier();
+    start_head(g);
+  }
   const float lam = lamst->lambda_f;
   const float c = kLog2e / 8.0f;   // log2(e) / sqrt(64)
   // Causal test: key > query for register e of sub-tile j  <=>  idx_of(e, 0) > kq - 32 j.
@@ -816,34 +860,40 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(
   }   // query heads of the group
 
   // Stores: register j of block b holds channel 32 b + 8 (j / 4) + 4 h + j % 4 of the key.
-  if (key < N) {
+  // Stores through LDS, in this wave's region of the ring once every wave is done with it
+  // (no tile load is in flight after the last tile's barrier).
+  barrier();
+  {
     const float s = 0.125f;  // 1 / sqrt(64)
     // Map 2's score gradients were accumulated without their factor lambda (the same for
     // every score): dS2 = lambda P2 (D2 - dP).
     const float s2 = s * lamst->lambda_f;
+    const int sv = lds0 + wv * KV_STAGE, sk1 = sv + stage_bytes<DV>(), sk2 = sk1 + stage_bytes<D>();
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        const int col = 32 * b + 8 * jg + 4 * h;
         u32x2 pk = {pack_bf16x2(adv[b][4 * jg], adv[b][4 * jg + 1]),
                     pack_bf16x2(adv[b][4 * jg + 2], adv[b][4 * jg + 3])};
-        *reinterpret_cast<u32x2*>(dv + (ho + key) * DV + col) = pk;
+        stage_put<DV>(sv, m, h, b, jg, pk);
       }
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        const int col = 32 * b + 8 * jg + 4 * h;
         u32x2 pa = {pack_bf16x2(s * adk1[b][4 * jg], s * adk1[b][4 * jg + 1]),
                     pack_bf16x2(s * adk1[b][4 * jg + 2], s * adk1[b][4 * jg + 3])};
         u32x2 pb = {pack_bf16x2(s2 * adk2[b][4 * jg], s2 * adk2[b][4 * jg + 1]),
                     pack_bf16x2(s2 * adk2[b][4 * jg + 2], s2 * adk2[b][4 * jg + 3])};
-        *reinterpret_cast<u32x2*>(dk1 + (ho + key) * D + col) = pa;
-        *reinterpret_cast<u32x2*>(dk2 + (ho + key) * D + col) = pb;
+        stage_put<D>(sk1, m, h, b, jg, pa);
+        stage_put<D>(sk2, m, h, b, jg, pb);
       }
     }
+    const int r0 = k0 + 32 * wv, valid = N - r0;
+    stage_flush<DV>(sv, dv + (ho + r0) * DV, valid, lane);
+    stage_flush<D>(sk1, dk1 + (ho + r0) * D, valid, lane);
+    stage_flush<D>(sk2, dk2 + (ho + r0) * D, valid, lane);
   }
 }
 
@@ -1150,24 +1200,30 @@ __global__ void __launch_bounds__(NTQ, 1) bwd_dq_kernel(
     });
   }
 
-  if (qok) {
+  // Stores through LDS, in this wave's region of the ring once every wave is done with it
+  // (no tile load is in flight after the last tile's barrier).
+  barrier();
+  {
     const float s = 0.125f;  // 1 / sqrt(64)
     // Map 2's score gradients were accumulated without their factor lambda (the same for
     // every score): dS2 = lambda P2 (D2 - dP).
     const float s2 = s * lamst->lambda_f;
+    const int s1 = lds0 + wv * Q_STAGE, s2b = s1 + stage_bytes<D>();
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        const int col = 32 * b + 8 * jg + 4 * h;
         u32x2 pa = {pack_bf16x2(s * aq1[b][4 * jg], s * aq1[b][4 * jg + 1]),
                     pack_bf16x2(s * aq1[b][4 * jg + 2], s * aq1[b][4 * jg + 3])};
         u32x2 pb = {pack_bf16x2(s2 * aq2[b][4 * jg], s2 * aq2[b][4 * jg + 1]),
                     pack_bf16x2(s2 * aq2[b][4 * jg + 2], s2 * aq2[b][4 * jg + 3])};
-        *reinterpret_cast<u32x2*>(dq1 + (ho + q) * D + col) = pa;
-        *reinterpret_cast<u32x2*>(dq2 + (ho + q) * D + col) = pb;
+        stage_put<D>(s1, m, h, b, jg, pa);
+        stage_put<D>(s2b, m, h, b, jg, pb);
       }
     }
+    const int r0 = q0 + 32 * wv, valid = N - r0;
+    stage_flush<D>(s1, dq1 + (ho + r0) * D, valid, lane);
+    stage_flush<D>(s2b, dq2 + (ho + r0) * D, valid, lane);
   }
 }
 
