@@ -35,6 +35,12 @@
 //            VALU  softmax of S2(j) -> P2(j)
 //    A map's rescale (when its running max moved) happens between its half-steps, after
 //    the last product into that accumulator and before the next.
+//    With one group per wavefront the fast pass steps over whole 64-key tiles instead:
+//    the tile's two 32-key halves fill the places of the two groups in the same
+//    half-step schedule (two score tiles per map and half-step, twice the products
+//    between dependent instructions), sharing the wavefront's one set of rows, Q
+//    operands and accumulators. Products and row sums keep their key order, so the
+//    result is the same bit for bit as on 32-key sub-tiles.
 //  * Query rows are dealt to lanes with stride 4 NG (row 4 NG m + NG w + g of the
 //    workgroup's rows for lane column m, wavefront w, group g; NG groups per wavefront),
 //    so every wavefront and group sees the same key range: sub-tiles below the
@@ -782,6 +788,176 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
     }
   };
 
+  // One group per wave (128-row blocks), fast pass: 64-key steps. The two 32-key halves s
+  // of tile j take the part the two query groups take with NG = 2 (same slot order: 16
+  // accumulator products and 8 score products per half-step, 16 softmax pairs), but they
+  // share the wave's 32 rows: one Q operand set, one accumulator set, one row state. Each
+  // step carries twice the independent work of a 32-key sub-tile, which covers the
+  // latencies a 32-key step leaves exposed. Products, row-sum additions and the reference
+  // maximum (the first 32 keys) come in the same key order as on 32-key sub-tiles, so
+  // the results are the same bit for bit.
+  // Accumulator product pv of a half-step: key half pv / 8, k-step (pv / 4) % 2, region
+  // pv % 4 (key order within each accumulator).
+  auto half_kh = [&](auto masked, auto is_x, int j, f32x16 (&acc)[4],
+                     const bf16x8 (&Pin)[2][2], f32x16 (&S_next)[2], const bf16x8 (&qf)[4],
+                     int k_step, f32x16 (&S_cur)[2], RowState& st, bf16x8 (&Pout)[2][2],
+                     VtHalf (&vk)[2][2]) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    constexpr bool IS_X = decltype(is_x)::value;
+    constexpr int KN_OFF = IS_X ? K2_OFF : K1_OFF;   // map of S_next
+    KOps kop[2];
+    float y[32];
+    uint32_t pw[2][2][4];
+    float ssum[2] = {st.l, st.l2};
+    auto slot = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int q = qk_slot<2, IS_X>(k);
+      if constexpr (q < 0) {
+        constexpr int pv = pv_index<2, IS_X>(k);
+        constexpr int s = pv / 8, t = (pv / 4) % 2, b = pv % 4;
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_operand(vk[s][t], b), Pin[s][t],
+                                                         acc[b], 0, 0, 0);
+        // X refills the operand it just consumed with V^T(j), which Y(j) and X(j + 1) use.
+        if constexpr (IS_X) vt_issue_b<b, t>(vk[s][t], va + v_off(2 * j + s));
+      } else {
+        constexpr int kb = q / 2, s = q % 2;
+        qk_one(S_next[s], k_operand(kop[s], kb), qf[kb], kb == 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (k == 0) s_anchor(S_cur);
+      if constexpr (k == 2) {
+        k_issue<KN_OFF>(kop[0], ka, k_off(2 * k_step));
+        k_issue<KN_OFF>(kop[1], ka, k_off(2 * k_step + 1));
+      }
+      static_for<0, 16>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int pr = decltype(pc)::value;
+        constexpr int sa = pair_start<2>(pr);
+        constexpr int s = pr >> 3, e = 2 * (pr & 7);
+        if constexpr (k == sa) {          // scale and subtract the reference
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            float sv = S_cur[s][e + i];
+            if (MASKED && 64 * j + 32 * s + key_of(e + i, h) > row_of(0)) sv = -INFINITY;
+            y[16 * s + e + i] = fmaf(sv, c, -st.m);
+          }
+          asm volatile("" : "+v"(y[16 * s + e]), "+v"(y[16 * s + e + 1]));
+        }
+        if constexpr (k == sa + 1) {      // exp2 of the first
+          y[16 * s + e] = fast_exp2(y[16 * s + e]);
+          asm volatile("" : "+v"(y[16 * s + e]));
+        }
+        if constexpr (k == sa + 2) {      // exp2 of the second
+          y[16 * s + e + 1] = fast_exp2(y[16 * s + e + 1]);
+          asm volatile("" : "+v"(y[16 * s + e + 1]));
+        }
+        if constexpr (k == sa + 3) {      // pack to bf16
+          pw[s][e >> 3][(e & 7) >> 1] = pack_bf16x2(y[16 * s + e], y[16 * s + e + 1]);
+          asm volatile("" : "+v"(pw[s][e >> 3][(e & 7) >> 1]));
+        }
+        if constexpr (k == sa + 4) {      // row sum
+          ssum[e >> 3] += y[16 * s + e] + y[16 * s + e + 1];
+          asm volatile("" : "+v"(ssum[e >> 3]));
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    slot(Int<0>{});
+    slot(Int<1>{});
+    if (!IS_X && j + 1 < n_tiles) {
+      // tile j + 1 resident before its K1 rows are read (slot 2)
+      tile_barrier(j + 2 < n_tiles);
+      if (j + 3 < n_tiles) dma_tile(rs, lds, j + 3, wv, lane);
+    }
+    static_for<2, 24>(slot);
+    st.l = ssum[0];
+    st.l2 = ssum[1];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x4 w4 = {pw[s][hf][0], pw[s][hf][1], pw[s][hf][2], pw[s][hf][3]};
+        Pout[s][hf] = __builtin_bit_cast(bf16x8, w4);
+      }
+    }
+  };
+
+  auto run_kh = [&]() __attribute__((always_inline)) {
+    st1[0] = RowState{kMInit, 0.f, 0.f, 0.f};
+    st2[0] = RowState{kMInit, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc1[0][b][i] = acc2[0][b][i] = 0.f;
+    }
+    acc_pin(acc1);
+    acc_pin(acc2);
+    f32x16 SA[2], SB[2];           // scores of the two key halves, maps 1 and 2
+    bf16x8 PA[2][2], PB[2][2];     // packed weights [half][k-step]
+    VtHalf vk[2][2];               // V^T of the current tile [half][k-step]
+    dma_tile(rs, lds, 0, wv, lane);
+    if (n_tiles > 1) dma_tile(rs, lds, 1, wv, lane);
+    tile_barrier(n_tiles > 1);
+    if (n_tiles > 2) dma_tile(rs, lds, 2, wv, lane);
+    {
+      KOps k0, k1;
+      k_issue<K1_OFF>(k0, ka, k_off(0));
+      k_issue<K1_OFF>(k1, ka, k_off(1));
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        qk_one(SA[0], k_operand(k0, kb), qf1[0][kb], kb == 0);
+        qk_one(SA[1], k_operand(k1, kb), qf1[0][kb], kb == 0);
+      }
+    }
+    {
+      // Reference m of both maps: exact row maxima of the first 32 keys (masked where the
+      // block starts at key 0).
+      KOps kop;
+      k_issue<K2_OFF>(kop, ka, k_off(0));
+      f32x16 T2[1];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) qk_one(T2[0], k_operand(kop, kb), qf2[0][kb], kb == 0);
+      s_guard(SA);
+      s_guard(T2);
+      f32x16 a = SA[0], b = T2[0];
+      if (jd == 0) {
+        mask_scores(a, 0, row_of(0), h);
+        mask_scores(b, 0, row_of(0), h);
+      }
+      st1[0].m = max_halves(max16(a)) * c;
+      st2[0].m = max_halves(max16(b)) * c;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      PB[s][0] = PB[s][1] = bf16x8{};
+      // X(0) multiplies tile 0's V (finite) by P2 = 0.
+      vt_issue<0>(vk[s][0], va + v_off(s));
+      vt_issue<1>(vk[s][1], va + v_off(s));
+    }
+    auto step_kh = [&](int jj, auto msk) __attribute__((always_inline)) {
+      DIFFATTN_DEBUG_BARRIER();   // every wave runs the same steps
+      // X(j): acc2 += V^T(j-1) P2(j-1); S2(j); softmax of S1(j) -> P1.
+      half_kh(msk, Flag<true>{}, jj, acc2[0], PB, SB, qf2[0], jj, SA, st1[0], PA, vk);
+      // Y(j): acc1 += V^T(j) P1(j); S1(j+1); softmax of S2(j) -> P2.
+      half_kh(msk, Flag<false>{}, jj, acc1[0], PA, SA, qf1[0], jj + 1, SB, st2[0], PB, vk);
+    };
+    for (int jj = 0; jj < jd / 2; ++jj) step_kh(jj, Flag<false>{});
+    for (int jj = jd / 2; jj < n_tiles; ++jj) step_kh(jj, Flag<true>{});
+    st1[0].l += st1[0].l2;
+    st2[0].l += st2[0].l2;
+    bad[0] = static_cast<uint32_t>(st1[0].l > kBad || st2[0].l > kBad);
+    // Drain: acc2 += V^T(last) P2(last).
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc2[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_operand(vk[s][t], b),
+                                                               PB[s][t], acc2[0][b], 0, 0, 0);
+      }
+    }
+  };
+
   // Epilogue per group: combine the lane halves' normalisers, form O, RMSNorm, scale,
   // store. ONLY_BAD: only rows whose flag is set (after the safe re-run). The lane holds
   // 64 of its row's 128 channels: 32 b + 8 jg + 4 h + e for region b, chunk jg, e < 4.
@@ -914,7 +1090,11 @@ __global__ void __launch_bounds__(NT, 1) fwd_bf16_kernel(
   };
 
   if constexpr (!SAFE) {
-    run(Flag<false>{});
+    if constexpr (NG == 1) {
+      run_kh();
+    } else {
+      run(Flag<false>{});
+    }
     epilogue(Flag<false>{});
     // Row flags of this block: bit m of word NG wv + g for the row of lane column m and
     // group g.
