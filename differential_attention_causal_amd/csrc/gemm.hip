@@ -22,7 +22,10 @@
 // 16-deep step a wave reads 4 A and 4 B operands from LDS for 16 products: half an LDS
 // read per product, which keeps the LDS well below its bandwidth. A and B K-slabs
 // (32 KiB each) are copied global -> LDS by the buffer unit (buffer_load ... lds),
-// double-buffered, one barrier per K-step. The finished tile is rounded to bf16 and
+// double-buffered, one barrier per K-step. A slab's 16 loads per wave go out four at a
+// time: after the barrier that frees its stage, then at the start of each of the next
+// K-step's first three 16-deep steps, where the matrix core still has products queued
+// (sixteen at once stalled the wave's issue). The finished tile is rounded to bf16 and
 // staged through LDS, so that every lane stores 16 contiguous bytes. Tiles are ordered in
 // groups of four 256-row panels (so the 32 tiles one XCD runs at a time share A and B
 // slabs in its L2), and each XCD is given a contiguous range of that order.
@@ -77,6 +80,19 @@ __device__ __forceinline__ void load_slab(const u32x4& rs, uint32_t dst, int k0,
                                           int wv, int lane) {
 #pragma unroll
   for (int r = 0; r < 32 / NWAVE; ++r) {
+    const int t = wv + NWAVE * r;
+    const int row = 8 * t + (lane >> 3);
+    const int unit = (lane & 7) ^ swz(row);
+    dma16(rs, dst + 1024 * t, row * row_bytes + k0 * 2 + 16 * unit);
+  }
+}
+
+// Transfers R0 .. R0 + RN - 1 of this wave's eight (see load_slab).
+template <int R0, int RN>
+__device__ __forceinline__ void load_part(const u32x4& rs, uint32_t dst, int k0, int row_bytes,
+                                          int wv, int lane) {
+#pragma unroll
+  for (int r = R0; r < R0 + RN; ++r) {
     const int t = wv + NWAVE * r;
     const int row = 8 * t + (lane >> 3);
     const int unit = (lane & 7) ^ swz(row);
@@ -200,12 +216,20 @@ __global__ void __launch_bounds__(NT, 1)
   for (int kt = 0; kt < KT; ++kt) {
     DIFFATTN_DEBUG_BARRIER();   // every wave runs the same K-steps
     const uint32_t cur = lds0 + (kt & 1) * STAGE;
+    // The rest of slab kt + 1, a quarter per step (its first quarter went out after the
+    // previous K-step's barrier), into the stage this K-step does not read.
+    const bool rest = kt >= 1 && kt + 1 < KT;
+    const uint32_t nst = lds0 + ((kt + 1) & 1) * STAGE;
+    const int nk0 = (kt + 1) * BK;
+    if (rest) load_part<4, 4>(ra, nst, nk0, K * 2, wv, lane);
     read_ops(fa[1], fb[1], cur, 1);
     products(fa[0], fb[0], 0, 16);
     interleave();
+    if (rest) load_part<0, 4>(rb, nst + SLAB, nk0, K * 2, wv, lane);
     read_ops(fa[0], fb[0], cur, 2);
     products(fa[1], fb[1], 0, 16);
     interleave();
+    if (rest) load_part<4, 4>(rb, nst + SLAB, nk0, K * 2, wv, lane);
     read_ops(fa[1], fb[1], cur, 3);
     products(fa[0], fb[0], 0, 16);
     interleave();
@@ -220,10 +244,7 @@ __global__ void __launch_bounds__(NT, 1)
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
-      if (kt + 2 < KT) {
-        load_slab(ra, cur, (kt + 2) * BK, K * 2, wv, lane);
-        load_slab(rb, cur + SLAB, (kt + 2) * BK, K * 2, wv, lane);
-      }
+      if (kt + 2 < KT) load_part<0, 4>(ra, cur, (kt + 2) * BK, K * 2, wv, lane);
       read_ops(fa[0], fb[0], lds0 + ((kt + 1) & 1) * STAGE, 0);
     }
     products(fa[1], fb[1], 4, 12);
