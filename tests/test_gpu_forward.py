@@ -339,6 +339,29 @@ def test_training_saves():
     assert np.max(np.abs(np64(sv["rstd"]) / rs["rstd"] - 1.0)) <= 2e-2
 
 
+def test_one_group_and_two_group_kernels_agree_bitwise():
+    """A row's result depends on its own scores only, so the one-group kernel (128-row
+    blocks on 64-key steps, taken for a single head of N = 2000) and the two-group kernel
+    (256-row blocks on 32-key sub-tiles, taken when the same head is one of 400) give the
+    same bits: outputs and every training save. N is not a multiple of 64."""
+    N, H = 2000, 400
+    assert forward_groups(1, 1, N) == 1 and forward_groups(1, H, N) == 2
+    w = synth.custom("train", 1, 1, N, 64, 5, "bf16", number=560)
+    x = synth.make_inputs(w, DEV, with_dout=False)
+    st = da.lambda_(x["lq1"], x["lk1"], x["lq2"], x["lk2"], w.layer)
+    names = ("q1", "q2", "k1", "k2", "v")
+    rep = {k: x[k].expand(1, H, N, x[k].shape[-1]).contiguous() for k in names}
+    sv1 = da.alloc_saved(1, 1, N, 64, DEV)
+    svh = da.alloc_saved(1, H, N, 64, DEV)
+    y1 = da.forward(*(x[k] for k in names), st, saved=sv1)
+    yh = da.forward(*(rep[k] for k in names), st, saved=svh)
+    torch.cuda.synchronize()
+    for hh in (0, 177, H - 1):
+        assert torch.equal(yh[:, hh], y1[:, 0])
+        for k in ("lse1", "lse2", "o1", "o2", "rstd"):
+            assert torch.equal(svh[k][:, hh], sv1[k][:, 0]), k
+
+
 def test_empty_sequence():
     q = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
     v = torch.empty(1, 2, 0, 128, dtype=torch.bfloat16, device=DEV)
