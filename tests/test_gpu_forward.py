@@ -166,9 +166,13 @@ def test_fp32_shapes(d, n):
     assert np.all(normwise_rel(np64(y), ref, axes=(2, 3)) <= FP32_TOL)
 
 
-@pytest.mark.parametrize("b,hh,n", [(1, 1, 1), (1, 2, 31), (2, 1, 64), (1, 1, 127), (1, 3, 128),
-                                    (2, 2, 129), (1, 2, 200), (1, 1, 513), (1, 1, 1000)])
+@pytest.mark.parametrize("b,hh,n", [(1, 1, 1), (1, 2, 31), (1, 1, 63), (2, 1, 64), (1, 2, 65),
+                                    (1, 1, 127), (1, 3, 128), (2, 2, 129), (1, 1, 191),
+                                    (2, 1, 192), (1, 2, 200), (1, 1, 257), (1, 1, 513),
+                                    (1, 1, 1000)])
 def test_bf16_small_shapes(b, hh, n):
+    """Small shapes take the one-group kernel (128-row blocks, 64-key steps): lengths on
+    both sides of a 64-key step and of a second 128-row block."""
     w = synth.custom("fwd", b, hh, n, 64, 4, "bf16", number=400 + n)
     x, h, st, ls, y = _run_fwd(w)
     ref = orc.forward(h["q1"], h["q2"], h["k1"], h["k2"], h["v"], ls["lambda"],
